@@ -1,0 +1,231 @@
+"""Benchmark of the NVFP4 W4A4 linear hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: run-time
+NVFP4 quantization of the bf16 activations under the calibrated input scale, then the
+block-scaled W4A4 GEMM with bf16 output (the fused linear). Weights are quantized
+offline and the global scales calibrated before the timed region, as a deployed layer
+does. Inputs are resident in HBM when timing starts.
+
+Prints one JSON line (rank 0) with the step throughput in TFLOP/s (2*M*N*K per step),
+the dominant kernel's roofline (GEMM vs the f16 dense MFMA peak), the quantize kernel's
+HBM bandwidth on rotated buffers, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOP/s + % MFMA peak at FLUX shapes; quantize GB/s % HBM peak"
+PEAK_F16_TFLOPS = 2516.6  # MI355X dense f16/bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+QUANT_BYTES_PER_ELEM = 2.5625  # 2 B bf16 in + 0.5 B codes + 1/16 B scale out
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="attn_out")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--rotate-mb", type=int, default=1024,
+                    help="bytes of rotated activation buffers for the quantize bandwidth leg")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, d, ags, wgs, seconds):
+    """The oracle as it stands, on the first R activation rows (R grows until about
+    `seconds` of CPU work), full weights; scaled to TFLOP/s of the same 2*R*N*K count."""
+    import numpy as np
+
+    from oracle import nvfp4_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:  # threadpoolctl missing: report the affinity size
+        cores = len(os.sched_getaffinity(0))
+    wp, ws = O.quantize(d["w"], wgs)  # offline weight quantization, not timed
+    rows_done, t_total, chunk = 0, 0.0, 64
+    while t_total < seconds and rows_done < wl.M:
+        r1 = min(wl.M, rows_done + chunk)
+        t0 = time.perf_counter()
+        ap, as_ = O.quantize(d["x"][rows_done:r1], ags)
+        O.gemm_ref(ap, as_, ags, wp, ws, wgs, with_abs=False)
+        t_total += time.perf_counter() - t0
+        rows_done = r1
+        chunk = min(chunk * 2, 1024)
+    flops = 2.0 * rows_done * wl.N * wl.K
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"first {rows_done} of {wl.M} activation rows x full [{wl.N}x{wl.K}] weights: "
+                  f"NumPy quantize (1 thread) + float64 GEMM reference ({cores} BLAS threads), "
+                  f"{t_total:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_02_amd as nv
+    from workloads import make
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    lib = nv.load_library()
+    dev = torch.device("cuda:0")
+    wl = make(args.workload)
+    M, N, K = wl.M, wl.N, wl.K
+    d = wl.generate()
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = to_dev(d["x"])
+    w = to_dev(d["w"])
+    # offline: weight global scale + weight quantization; activation input scale
+    wgs = nv.calibrate(w)
+    wq, wsc = nv.quantize(w, wgs)
+    ags = nv.calibrate(to_dev(d["calib"])) if "calib" in d else nv.calibrate(x)
+    del w
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    work = torch.empty(nv.linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    qp, qs = nv.workspace_views(work, M, K)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    xa, qpa, qsa, wqa, wsa, oa = P(x), P(qp), P(qs), P(wq), P(wsc), P(out)
+    f_ags, f_wgs = ctypes.c_float(ags), ctypes.c_float(wgs)
+
+    def step():
+        s1 = lib.nvfp4_quantize(xa, M, K, f_ags, qpa, qsa, sp)
+        s2 = lib.nvfp4_gemm(qpa, qsa, f_ags, wqa, wsa, f_wgs, M, N, K, oa, sp)
+        if s1 or s2:
+            raise RuntimeError(f"status {s1} {s2}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; HIP events around each kernel on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        if lib.nvfp4_quantize(xa, M, K, f_ags, qpa, qsa, sp):
+            raise RuntimeError("quantize failed")
+        e[1].record(stream)
+        if lib.nvfp4_gemm(qpa, qsa, f_ags, wqa, wsa, f_wgs, M, N, K, oa, sp):
+            raise RuntimeError("gemm failed")
+        e[2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+
+    # quantize bandwidth on rotated buffers (beyond the 256 MB Infinity Cache)
+    n_rot = max(2, int(args.rotate_mb * 2**20 // (M * K * 2)))
+    xs = [x] + [x.clone() for _ in range(n_rot - 1)]
+    outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty((M, K // 16), dtype=torch.uint8, device=dev)) for _ in range(n_rot)]
+    ptrs = [(P(a), P(b), P(c)) for a, (b, c) in zip(xs, outs)]
+    for i in range(n_rot):
+        lib.nvfp4_quantize(ptrs[i][0], M, K, f_ags, ptrs[i][1], ptrs[i][2], sp)
+    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_q = max(args.steps, 4 * n_rot)
+    torch.cuda.synchronize()
+    qa.record(stream)
+    for i in range(n_q):
+        a, b, c = ptrs[i % n_rot]
+        lib.nvfp4_quantize(a, M, K, f_ags, b, c, sp)
+    qb.record(stream)
+    torch.cuda.synchronize()
+    q_rot_ms = qa.elapsed_time(qb) / n_q
+    q_gbs = QUANT_BYTES_PER_ELEM * M * K / (q_rot_ms * 1e-3) / 1e9
+    del xs, outs
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: NVFP4 W4A4 linear, x bf16 [M={M}, K={K}] "
+                        f"({wl.description}), W [N={N}, K={K}], bf16 out",
+            "global_batch": M,
+            "seq_len": None,
+            "parallelism": "none (1 GPU)",
+            "M": M, "N": N, "K": K,
+        },
+        "roofline": {
+            "kernel": "nvfp4 block-scaled GEMM (f16 MFMA after exact E2M1xE4M3 decode)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": None,
+            "avg_ms": round(g_ms, 5),
+        },
+        "quantize": {
+            "in_step_avg_ms": round(q_ms, 5),
+            "rotated_avg_ms": round(q_rot_ms, 5),
+            "achieved": round(q_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": int(QUANT_BYTES_PER_ELEM * M * K),
+            "rotated_buffers": n_rot,
+        },
+        "precision": "E2M1 x E4M3 operands decoded exactly to f16, f16 MFMA, fp32 accumulate, "
+                     "bf16 output",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, d, ags, wgs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

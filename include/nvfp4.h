@@ -1,0 +1,145 @@
+/*
+ * libnvfp4 -- NVFP4 W4A4 linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every entry point takes plain pointers and sizes; no C++ types cross it and no
+ * exception escapes it. Device buffers and streams belong to the caller; the library
+ * allocates nothing, keeps no per-call state and never synchronises the host, except
+ * where a function says otherwise (nvfp4_amax_host).
+ *
+ * The format (what a stored tensor is):
+ *   - "BFL (fp8r / nvfp4)" (Hugging Face diffusers docs), scheme list, item nvfp4: a
+ *     quantized linear layer stores a packed E2M1 `weight` (two values per byte), E4M3
+ *     block scales `weight_scale`, a global fp32 `weight_scale_2` and a calibrated fp32
+ *     activation scale `input_scale`.
+ *   - zubnet.ai, "NVIDIA FP4 format: diffusion model 1.68x speedup", paragraph 1:
+ *     microscaling, one shared scale per small block; NVFP4 = E2M1 with 16-element
+ *     blocks.
+ *   - "BFL (fp8r / nvfp4)", Kernels table, nvfp4 row: activations are quantized at run
+ *     time and fed, with the stored weights, to one fused FP4 GEMM.
+ *
+ * Conventions of this library (the pages do not fix them):
+ *   - A tensor is row-major [rows, K], K % 16 == 0. Blocks are 16 consecutive elements
+ *     along K. packed is uint8 [rows, K/2]: byte j of a row holds element 2j in its low
+ *     nibble and element 2j+1 in its high nibble. scales is uint8 [rows, K/16] of OCP
+ *     E4M3 ("FN") codes, never negative or NaN, at most 0x7E (448).
+ *   - An E2M1 code is sign<<3 | magnitude code; magnitudes 0..7 are
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}. Negative zero is code 0x8.
+ *   - Global scales are host fp32 in the dequantise direction:
+ *     value = e2m1(code) * e4m3(scale) * global.
+ *   - bf16 tensors are raw 16-bit storage. Weights are [N, K] (a linear layer's
+ *     layout); out = x * W^T is [M, N] bf16, row-major.
+ *   - Quantization rounding (every step IEEE binary32, round to nearest even): per block,
+ *     amax = max|x|; s = E4M3(RN(amax / RN(6 * global))) with ties to the even code and
+ *     saturation at 448; d = RN(s * global); code_i = E2M1(RN(|x_i| / d)) with ties to
+ *     the even code, saturation at 6 and the sign of x_i copied (d == 0 gives magnitude 0).
+ *   - GEMM: out = bf16_RNE(RN(a_global * w_global) * sum_k a_k w_k) with the decoded
+ *     (E2M1 x E4M3) operands; the products are exact and accumulate in fp32. Any result
+ *     within 2^-10 * sum_k |a_k w_k| (global scales included) + 1 bf16 ulp of the exact
+ *     value is correct; the library's result is deterministic for a given shape.
+ *
+ * Preconditions that are not checked (checking them would read the data):
+ *   inputs are finite; buffers do not overlap; pointers are device memory of the
+ *   current device (any HIP device pointer, including managed memory).
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ * Every compute call is asynchronous and stream-ordered. Calls are thread-safe.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+/* Status codes. All argument validation happens before any HIP call. */
+typedef enum nvfp4_status {
+  NVFP4_SUCCESS = 0,                  /* also returned for an empty problem (M == 0 or N == 0) */
+  NVFP4_ERROR_INVALID_VALUE = 1,      /* null pointer; global scale not finite, <= 0, or
+                                         outside [2^-100, 2^100] */
+  NVFP4_ERROR_INVALID_SHAPE = 2,      /* negative size, K < 16, K % 16 != 0, size overflow */
+  NVFP4_ERROR_MISALIGNED = 3,         /* x, packed, out or workspace not 16-byte aligned;
+                                         scales not 4-byte aligned */
+  NVFP4_ERROR_WORKSPACE = 4,          /* workspace smaller than nvfp4_linear_workspace_bytes */
+  NVFP4_ERROR_UNSUPPORTED_DEVICE = 5, /* no HIP device, or the current device is not gfx950 */
+  NVFP4_ERROR_HIP = 6                 /* a HIP call failed; see nvfp4_last_hip_error() */
+} nvfp4_status;
+
+/* Version of this ABI (NVFP4_ABI_VERSION). A binding must refuse a mismatch. */
+int nvfp4_abi_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* hipError_t of the last NVFP4_ERROR_HIP returned on the calling thread (0 if none). */
+int nvfp4_last_hip_error(void);
+
+/*
+ * Runtime activation (or offline weight) quantization, the counterpart of the pages'
+ * nvfp4_quantize ("BFL (fp8r / nvfp4)", Kernels table, nvfp4 row).
+ *   x_bf16       device, bf16 [M, K], 16-byte aligned, read only
+ *   M, K         rows and columns; M >= 0, K >= 16, K % 16 == 0
+ *   global_scale fp32 per-tensor scale (input_scale for activations, weight_scale_2 for
+ *                weights), finite, in [2^-100, 2^100]
+ *   packed       device, uint8 [M, K/2], 16-byte aligned, written
+ *   scales       device, uint8 [M, K/16], 4-byte aligned, written
+ * The output is bit-exact to the rounding rule in the header comment.
+ */
+int nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, float global_scale,
+                   void* packed, void* scales, void* stream);
+
+/*
+ * Block-scaled W4A4 GEMM, the counterpart of the pages' mm_fp4 ("BFL (fp8r / nvfp4)",
+ * Kernels table, nvfp4 row): out[M, N] = a_global * w_global * A_hat[M, K] W_hat[N, K]^T.
+ *   a_packed, a_scales  device, activations in NVFP4 layout [M, K/2], [M, K/16]
+ *   w_packed, w_scales  device, weights in NVFP4 layout [N, K/2], [N, K/16]
+ *   a_global_scale, w_global_scale  fp32, finite, > 0
+ *   out_bf16            device, bf16 [M, N], 16-byte aligned, written
+ * Packed operands must be 16-byte aligned, scales 4-byte aligned.
+ */
+int nvfp4_gemm(const void* a_packed, const void* a_scales, float a_global_scale,
+               const void* w_packed, const void* w_scales, float w_global_scale,
+               int64_t M, int64_t N, int64_t K, void* out_bf16, void* stream);
+
+/* Workspace bytes nvfp4_linear needs for an [M, K] activation (packed + scales, each
+ * rounded up to 256 bytes). Returns 0 for invalid shapes. */
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Fused linear: quantize x under a_global_scale into the workspace, then nvfp4_gemm,
+ * both on `stream` ("BFL (fp8r / nvfp4)", Kernels table, nvfp4 row, fused-kernel column:
+ * run-time activation quantization paired with the FP4 GEMM).
+ *   x_bf16     device bf16 [M, K]
+ *   workspace  device, >= nvfp4_linear_workspace_bytes(M, K) bytes, 256-byte aligned is
+ *              best (16 required); it holds the quantized activations on return:
+ *              packed [M, K/2] at offset 0, scales [M, K/16] at offset
+ *              round_up(M*K/2, 256).
+ * Other arguments as in nvfp4_quantize / nvfp4_gemm.
+ */
+int nvfp4_linear(const void* x_bf16, float a_global_scale, const void* w_packed,
+                 const void* w_scales, float w_global_scale, int64_t M, int64_t N, int64_t K,
+                 void* out_bf16, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Calibration of a global scale (the pages' calibrated fp32 input_scale and the stored
+ * weight_scale_2, "BFL (fp8r / nvfp4)", nvfp4 item).
+ *
+ * nvfp4_amax: amax_out[0] = max |x| over n bf16 values (0 for n == 0), computed on the
+ * device and written to device memory (fp32). x_bf16 must be 16-byte aligned; amax_out
+ * 4-byte aligned. Asynchronous.
+ */
+int nvfp4_amax(const void* x_bf16, int64_t n, float* amax_out, void* stream);
+
+/* Host function: RN32(amax / (6 * 448)), or 1.0 when amax == 0. Returns a NaN for a
+ * negative or non-finite amax. */
+float nvfp4_global_scale_from_amax(float amax);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

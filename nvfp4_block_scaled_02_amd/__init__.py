@@ -1,0 +1,20 @@
+"""libnvfp4: NVFP4 W4A4 linear layers with hand-written HIP kernels for MI355X (gfx950).
+
+Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
+
+* :func:`quantize`  -- bf16 [M, K] -> packed E2M1 [M, K/2] + E4M3 scales [M, K/16]
+* :func:`gemm`      -- block-scaled W4A4 GEMM, bf16 output
+* :func:`linear`    -- fused quantize + GEMM through a workspace
+* :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
+"""
+from ._lib import NVFP4Error, load_library  # noqa: F401
+from .ops import (  # noqa: F401
+    amax,
+    calibrate,
+    gemm,
+    global_scale_from_amax,
+    linear,
+    linear_workspace_bytes,
+    quantize,
+    workspace_views,
+)

@@ -1,0 +1,245 @@
+// C ABI of libnvfp4: argument validation, device check and kernel dispatch.
+// The entry points and their contracts are declared in include/nvfp4.h and
+// include/nvfp4_selftest.h.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/nvfp4.h"
+#include "../../include/nvfp4_selftest.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceEntry {
+  std::once_flag once;
+  int status = NVFP4_ERROR_UNSUPPORTED_DEVICE;
+  hipError_t err = hipSuccess;
+  nvfp4::LaunchInfo info{0};
+};
+DeviceEntry g_devices[kMaxDevices];
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return NVFP4_ERROR_HIP;
+}
+
+// Current device must be gfx950; the answer is cached per device (thread-safe).
+int current_device(nvfp4::LaunchInfo* info) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = (int)e;
+    return NVFP4_ERROR_UNSUPPORTED_DEVICE;
+  }
+  if (dev >= kMaxDevices) return NVFP4_ERROR_UNSUPPORTED_DEVICE;
+  DeviceEntry& d = g_devices[dev];
+  std::call_once(d.once, [&]() {
+    hipDeviceProp_t prop;
+    d.err = hipGetDeviceProperties(&prop, dev);
+    if (d.err != hipSuccess) {
+      d.status = NVFP4_ERROR_HIP;
+      return;
+    }
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      d.status = NVFP4_ERROR_UNSUPPORTED_DEVICE;
+      return;
+    }
+    d.info.num_cus = prop.multiProcessorCount;
+    d.status = NVFP4_SUCCESS;
+  });
+  if (d.status == NVFP4_ERROR_HIP) g_last_hip_error = (int)d.err;
+  *info = d.info;
+  return d.status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Global scales: finite, in [2^-100, 2^100] (keeps every per-block divisor normal).
+bool valid_scale(float g) { return isfinite(g) && g >= 0x1p-100f && g <= 0x1p100f; }
+
+// Shape: rows >= 0, K >= 16, K % 16 == 0, rows * K without overflow (bytes < 2^62).
+int check_shape(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 16 || K % 16 != 0) return NVFP4_ERROR_INVALID_SHAPE;
+  if (rows > 0 && K > ((int64_t)1 << 61) / rows) return NVFP4_ERROR_INVALID_SHAPE;
+  return NVFP4_SUCCESS;
+}
+
+constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int validate_gemm(const void* ap, const void* as, float ags, const void* wp, const void* ws,
+                  float wgs, int64_t M, int64_t N, int64_t K, const void* out) {
+  if (!ap || !as || !wp || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (!valid_scale(ags) || !valid_scale(wgs)) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  if (!aligned(ap, 16) || !aligned(wp, 16) || !aligned(out, 16) || !aligned(as, 4) ||
+      !aligned(ws, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  return NVFP4_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_SUCCESS: return "success";
+    case NVFP4_ERROR_INVALID_VALUE: return "invalid value (null pointer or bad global scale)";
+    case NVFP4_ERROR_INVALID_SHAPE: return "invalid shape (need K >= 16, K % 16 == 0, sizes >= 0)";
+    case NVFP4_ERROR_MISALIGNED: return "misaligned pointer";
+    case NVFP4_ERROR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERROR_UNSUPPORTED_DEVICE: return "no gfx950 device";
+    case NVFP4_ERROR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_last_hip_error(void) { return g_last_hip_error; }
+
+float nvfp4_global_scale_from_amax(float amax) {
+  if (!isfinite(amax) || amax < 0.0f) return NAN;
+  if (amax == 0.0f) return 1.0f;
+  volatile float den = 2688.0f;  // 6 * 448, exact
+  return amax / den;             // IEEE binary32 division
+}
+
+int nvfp4_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed, void* scales,
+                   void* stream) {
+  if (!x || !packed || !scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (!valid_scale(gs)) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return NVFP4_ERROR_MISALIGNED;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_quantize(x, M, K, gs, packed, scales, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_gemm(const void* ap, const void* as, float ags, const void* wp, const void* ws, float wgs,
+               int64_t M, int64_t N, int64_t K, void* out, void* stream) {
+  int s = validate_gemm(ap, as, ags, wp, ws, wgs, M, N, K, out);
+  if (s) return s;
+  if (M == 0 || N == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  nvfp4::GemmProblem p{(const uint8_t*)ap, (const uint8_t*)as, (const uint8_t*)wp,
+                       (const uint8_t*)ws, (uint16_t*)out, M, N, K, ags * wgs};
+  hipError_t e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (check_shape(M, K)) return 0;
+  return round_up((size_t)(M * K / 2), 256) + round_up((size_t)(M * K / 16), 256);
+}
+
+int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float wgs, int64_t M,
+                 int64_t N, int64_t K, void* out, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!x || !workspace) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  const size_t packed_bytes = round_up((size_t)(M * K / 2), 256);
+  uint8_t* ap = (uint8_t*)workspace;
+  uint8_t* as = ap + packed_bytes;
+  s = validate_gemm(ap, as, ags, wp, ws, wgs, M, N, K, out);
+  if (s) return s;
+  if (!aligned(x, 16)) return NVFP4_ERROR_MISALIGNED;
+  if (workspace_bytes < nvfp4_linear_workspace_bytes(M, K)) return NVFP4_ERROR_WORKSPACE;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_quantize(x, M, K, ags, ap, as, (hipStream_t)stream, info);
+  if (e != hipSuccess) return hip_fail(e);
+  if (N == 0) return NVFP4_SUCCESS;
+  nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
+                       M, N, K, ags * wgs};
+  e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_amax(const void* x, int64_t n, float* amax_out, void* stream) {
+  if (!x || !amax_out) return NVFP4_ERROR_INVALID_VALUE;
+  if (n < 0) return NVFP4_ERROR_INVALID_SHAPE;
+  if (!aligned(x, 16) || !aligned(amax_out, 4)) return NVFP4_ERROR_MISALIGNED;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_amax(x, n, amax_out, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+// ---- self-test entry points ----------------------------------------------------------
+
+int nvfp4_selftest_e2m1_encode(const float* y, uint8_t* hw_codes, uint8_t* sw_codes, int64_t n,
+                               void* stream) {
+  if (!y || !hw_codes || !sw_codes) return NVFP4_ERROR_INVALID_VALUE;
+  if (n < 0) return NVFP4_ERROR_INVALID_SHAPE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_encode(y, hw_codes, sw_codes, n, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_selftest_e2m1_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                   void* stream) {
+  if (!mismatches || !first16) return NVFP4_ERROR_INVALID_VALUE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_encode_exhaustive(mismatches, first16, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_selftest_division(unsigned long long* mismatches, uint32_t* first16, void* stream) {
+  if (!mismatches || !first16) return NVFP4_ERROR_INVALID_VALUE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_division(mismatches, first16, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_selftest_block_scale(const float* amax, float global_scale, uint8_t* codes, float* d,
+                               int64_t n, void* stream) {
+  if (!amax || !codes || !d) return NVFP4_ERROR_INVALID_VALUE;
+  if (!valid_scale(global_scale)) return NVFP4_ERROR_INVALID_VALUE;
+  if (n < 0) return NVFP4_ERROR_INVALID_SHAPE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_scale(amax, global_scale, codes, d, n, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw_f16,
+                          uint16_t* sw_f16, int64_t nbytes, void* stream) {
+  if (!packed || !scales || !hw_f16 || !sw_f16) return NVFP4_ERROR_INVALID_VALUE;
+  if (nbytes < 0) return NVFP4_ERROR_INVALID_SHAPE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_decode(packed, scales, hw_f16, sw_f16, nbytes,
+                                               (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Scalar NVFP4 codecs shared by the quantize kernel, the GEMM decode and the self-test
+// kernels. Everything here is plain IEEE binary32 / integer arithmetic; the functions
+// marked NVFP4_HD compile for the host as well, so their rounding can be checked on a
+// CPU. Hardware conversion builtins are device-only.
+//
+// Format: E2M1 elements, one E4M3 scale per 16-element block, fp32 global scale
+// ("BFL (fp8r / nvfp4)", nvfp4 item; zubnet.ai page, paragraph 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define NVFP4_HD __host__ __device__ __forceinline__
+
+namespace nvfp4 {
+
+// Native 16-byte vector (usable with the nontemporal load/store builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+NVFP4_HD float u2f(uint32_t u) {
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+NVFP4_HD uint32_t f2u(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  return u;
+}
+
+// Largest E4M3 value and its code; largest E2M1 magnitude.
+constexpr float kE4M3Max = 448.0f;
+constexpr uint32_t kE4M3MaxCode = 0x7E;
+
+// E4M3 code of the E4M3 value nearest to s (s >= 0, not NaN; +inf allowed), ties to
+// the even code, saturating at 448 (0x7E).
+//  * s >= 448: saturate.
+//  * s < 2^-6 (E4M3 subnormal range, spacing 2^-9): code = round-half-even(s * 2^9);
+//    the product is exact and code 8 is the smallest normal, so the rounding carries
+//    into the normal range seamlessly.
+//  * otherwise round the binary32 significand to 3 bits (half to even, at bit 20) and
+//    rebias the exponent from 127 to 7.
+NVFP4_HD uint32_t e4m3_encode_sat(float s) {
+  if (!(s < kE4M3Max)) return kE4M3MaxCode;
+  if (s < 0x1p-6f) return (uint32_t)__builtin_rintf(s * 512.0f);
+  uint32_t b = f2u(s);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  return (b >> 20) - (120u << 3);
+}
+
+// Exact value of a finite non-negative E4M3 code (0..0x7E), without relying on
+// denormal arithmetic: subnormal codes are m * 2^-9, normal codes shift into a
+// binary32 pattern with the exponent rebiased by +120.
+NVFP4_HD float e4m3_decode(uint32_t c) {
+  return c < 8u ? (float)c * 0x1p-9f : u2f((c << 20) + (120u << 23));
+}
+
+// E2M1 magnitude code of y >= 0 (or -0; +inf allowed): nearest of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating at 6. The midpoints
+// 0.25, 1.25, 2.5, 5 go down (to codes 0, 2, 4, 6) and 0.75, 1.75, 3.5 go up (to codes
+// 2, 4, 6).
+NVFP4_HD uint32_t e2m1_magnitude_encode(float y) {
+  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+         (uint32_t)(y > 5.0f);
+}
+
+// Correctly rounded x / d for a bf16-valued x (8 significant bits) and a normal
+// binary32 d, given r = RN(1/d): y0 = RN(x r), rho = RN(x - y0 d) (exact, fma),
+// y = RN(y0 + rho r) (Markstein's correction). An exhaustive check over every pair of
+// significands (bf16 x, binary32 d) shows y == RN(x/d). y0 is clamped to [-8, 8]
+// first; any |x/d| >= 6 saturates the E2M1 code, so the clamp only keeps a huge
+// quotient from turning into inf - inf = NaN. With r == 0 (for d == 0) the result is
+// a zero carrying the sign of x.
+NVFP4_HD float div_by_scale(float x, float d, float r) {
+  float y0 = x * r;
+  y0 = y0 < -8.0f ? -8.0f : (y0 > 8.0f ? 8.0f : y0);
+  float rho = __builtin_fmaf(-y0, d, x);
+  return __builtin_fmaf(rho, r, y0);
+}
+
+// Per-block quantization state: the scale code, d = RN(s * gs) and r = RN(1/d) (0 when
+// d == 0).
+struct BlockScale {
+  uint32_t code;
+  float d;
+  float r;
+};
+
+// Scale of one block from its amax under global scale gs, with den = RN(6 * gs):
+// s_raw = RN(amax / den), code = E4M3(s_raw), d = RN(decode(code) * gs).
+NVFP4_HD BlockScale block_scale(float amax, float den, float gs) {
+  BlockScale b;
+  float s_raw = amax / den;
+  b.code = e4m3_encode_sat(s_raw);
+  b.d = e4m3_decode(b.code) * gs;
+  b.r = b.d == 0.0f ? 0.0f : 1.0f / b.d;
+  return b;
+}
+
+// 4-bit code of one element (software path): sign bit of x, magnitude of |y|.
+NVFP4_HD uint32_t e2m1_encode_sw(float x, float y) {
+  uint32_t sign = (f2u(x) >> 31) << 3;
+  return sign | e2m1_magnitude_encode(__builtin_fabsf(y));
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct LaunchInfo {
+  int num_cus;  // compute units of the current device
+};
+
+hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,
+                           void* scales, hipStream_t stream, const LaunchInfo& dev);
+
+struct GemmProblem {
+  const uint8_t* a_packed;
+  const uint8_t* a_scales;
+  const uint8_t* w_packed;
+  const uint8_t* w_scales;
+  uint16_t* out;
+  int64_t M, N, K;
+  float alpha;  // RN(a_global * w_global)
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
+
+hipError_t launch_amax(const void* x, int64_t n, float* out, hipStream_t stream,
+                       const LaunchInfo& dev);
+
+// self-test support
+hipError_t launch_selftest_encode(const float* y, uint8_t* hw, uint8_t* sw, int64_t n,
+                                  hipStream_t stream);
+hipError_t launch_selftest_encode_exhaustive(unsigned long long* count, uint32_t* first,
+                                             hipStream_t stream);
+hipError_t launch_selftest_division(unsigned long long* count, uint32_t* first,
+                                    hipStream_t stream);
+hipError_t launch_selftest_scale(const float* amax, float gs, uint8_t* code, float* d, int64_t n,
+                                 hipStream_t stream);
+hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,
+                                  uint16_t* sw, int64_t nbytes, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,217 @@
+// NVFP4 quantization kernel for gfx950: bf16 [M, K] -> packed E2M1 [M, K/2] + E4M3
+// scales [M, K/16] under an fp32 global scale.
+//
+// The run-time activation quantizer that the pages pair with the FP4 GEMM
+// ("BFL (fp8r / nvfp4)", Kernels table, nvfp4 row); microscaling with 16-element E2M1
+// blocks (zubnet.ai page, paragraph 1).
+//
+// Design (memory-bound: 2 B read + 0.5625 B written per element):
+//  * K % 16 == 0, so 16-element blocks never straddle rows and the tensor is a flat
+//    array of M*K/16 independent blocks; block b reads bytes [32b, 32b+32) of x, writes
+//    bytes [8b, 8b+8) of packed and byte b of scales.
+//  * One lane owns one block: two 16-byte loads, the amax in registers (no cross-lane
+//    traffic), one 8-byte and one 1-byte store. Consecutive lanes own consecutive
+//    blocks, so a wave reads 2 KiB and writes 512 + 64 contiguous bytes.
+//  * Each lane handles UNROLL blocks per step with all loads issued first (UNROLL x 32 B
+//    in flight per lane) to keep enough bytes in flight for HBM.
+//  * Rounding: the per-block scale uses IEEE division; the per-element quotient
+//    |x| / d uses the reciprocal of d plus Markstein's fma correction, which equals the
+//    IEEE quotient for every bf16 x (see codec.hpp); the E2M1 encode is the gfx950
+//    conversion instruction, whose rounding (to nearest even, saturating) is checked
+//    exhaustively against the software encoder by the self-test entry points.
+#include "codec.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = u2f(w[i] << 16);
+    f[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Encode 16 values (in f) of one block into 8 packed bytes, given the block's scale.
+template <bool kHwEncode>
+__device__ __forceinline__ uint2 encode_block(const float* f, const BlockScale& bs) {
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float y0 = div_by_scale(f[2 * j], bs.d, bs.r);
+    const float y1 = div_by_scale(f[2 * j + 1], bs.d, bs.r);
+    if constexpr (kHwEncode) {
+      // byte j % 4 of word j / 4 <- {code(y1) << 4 | code(y0)}
+      switch (j & 3) {
+        case 0: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 0); break;
+        case 1: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 1); break;
+        case 2: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 2); break;
+        default: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 3); break;
+      }
+    } else {
+      const uint32_t c = e2m1_encode_sw(f[2 * j], y0) | (e2m1_encode_sw(f[2 * j + 1], y1) << 4);
+      out[j >> 2] |= c << (8 * (j & 3));
+    }
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+template <int UNROLL, bool kHwEncode>
+__global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__ x,
+                                                       uint2* __restrict__ packed,
+                                                       uint8_t* __restrict__ scales,
+                                                       int64_t nblocks, float gs, float den) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * UNROLL;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nblocks;
+       base += stride) {
+    u32x4 v[UNROLL][2];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t b = base + (int64_t)u * blockDim.x;
+      if (b < nblocks) {
+        v[u][0] = __builtin_nontemporal_load(&x[2 * b]);
+        v[u][1] = __builtin_nontemporal_load(&x[2 * b + 1]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t b = base + (int64_t)u * blockDim.x;
+      if (b < nblocks) {
+        float f[16];
+        unpack_bf16x8(v[u][0], f);
+        unpack_bf16x8(v[u][1], f + 8);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+        const BlockScale bs = block_scale(amax, den, gs);
+        const uint2 p = encode_block<kHwEncode>(f, bs);
+        __builtin_nontemporal_store(p.x, &packed[b].x);
+        __builtin_nontemporal_store(p.y, &packed[b].y);
+        scales[b] = (uint8_t)bs.code;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,
+                           void* scales, hipStream_t stream, const LaunchInfo& dev) {
+  const int64_t nblocks = M * (K / 16);
+  if (nblocks == 0) return hipSuccess;
+  constexpr int kThreads = 256;
+  constexpr int kUnroll = 4;
+  const float den = 6.0f * gs;
+  int64_t want = (nblocks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  // Enough workgroups to fill every CU several times over; the grid-stride loop covers
+  // the rest.
+  const int64_t cap = (int64_t)dev.num_cus * 8;
+  const int grid = (int)(want < cap ? want : cap);
+  hipLaunchKernelGGL((quantize_kernel<kUnroll, true>), dim3(grid), dim3(kThreads), 0, stream,
+                     (const u32x4*)x, (uint2*)packed, (uint8_t*)scales, nblocks, gs, den);
+  return hipGetLastError();
+}
+
+// ---- self-test support: the exact device functions the quantizer uses ---------------
+
+namespace {
+
+__global__ void selftest_encode_kernel(const float* __restrict__ y, uint8_t* __restrict__ hw,
+                                       uint8_t* __restrict__ sw, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = y[i];
+  hw[i] = (uint8_t)(__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu);
+  sw[i] = (uint8_t)e2m1_encode_sw(v, v);
+}
+
+// All 2^32 binary32 patterns except NaNs: count where the conversion instruction and
+// the software encoder disagree; record up to 16 offending patterns.
+__global__ void selftest_encode_exhaustive_kernel(unsigned long long* __restrict__ count,
+                                                  uint32_t* __restrict__ first) {
+  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t nthreads = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long local = 0;
+  for (uint64_t u = tid; u < (1ull << 32); u += nthreads) {
+    const uint32_t bits = (uint32_t)u;
+    const float v = u2f(bits);
+    if (v != v) continue;
+    const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
+    const uint32_t sw = e2m1_encode_sw(v, v);
+    if (hw != sw) {
+      const unsigned long long k = atomicAdd(count, 1ull);
+      if (k < 16) first[k] = bits;
+      ++local;
+    }
+  }
+  (void)local;
+}
+
+// Markstein division vs IEEE division on every pair (bf16 significand of x, binary32
+// significand of d), with x in [1, 4) and d in [1, 2).
+__global__ void selftest_division_kernel(unsigned long long* __restrict__ count,
+                                         uint32_t* __restrict__ first) {
+  const uint32_t dm = blockIdx.x * blockDim.x + threadIdx.x;  // 2^23 threads
+  if (dm >= (1u << 23)) return;
+  const float d = u2f(0x3F800000u | dm);
+  const float r = 1.0f / d;
+  for (uint32_t xm = 0; xm < 256; ++xm) {
+    const float x = u2f(((127u + (xm >> 7)) << 23) | ((xm & 127u) << 16));
+    const float y = div_by_scale(x, d, r);
+    const float q = x / d;
+    if (f2u(y) != f2u(q)) {
+      const unsigned long long k = atomicAdd(count, 1ull);
+      if (k < 8) {
+        first[2 * k] = f2u(x);
+        first[2 * k + 1] = f2u(d);
+      }
+    }
+  }
+}
+
+__global__ void selftest_scale_kernel(const float* __restrict__ amax, float gs, float den,
+                                      uint8_t* __restrict__ code, float* __restrict__ d_out,
+                                      int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const BlockScale b = block_scale(amax[i], den, gs);
+  code[i] = (uint8_t)b.code;
+  d_out[i] = b.d;
+}
+
+}  // namespace
+
+hipError_t launch_selftest_encode(const float* y, uint8_t* hw, uint8_t* sw, int64_t n,
+                                  hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(selftest_encode_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, y, hw, sw, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_encode_exhaustive(unsigned long long* count, uint32_t* first,
+                                             hipStream_t stream) {
+  hipLaunchKernelGGL(selftest_encode_exhaustive_kernel, dim3(8192), dim3(256), 0, stream, count,
+                     first);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_division(unsigned long long* count, uint32_t* first,
+                                    hipStream_t stream) {
+  hipLaunchKernelGGL(selftest_division_kernel, dim3((1u << 23) / 256), dim3(256), 0, stream,
+                     count, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_scale(const float* amax, float gs, uint8_t* code, float* d, int64_t n,
+                                 hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(selftest_scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, amax, gs, 6.0f * gs, code, d, n);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

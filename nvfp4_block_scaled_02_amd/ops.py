@@ -1,0 +1,146 @@
+"""Thin PyTorch-facing binding over libnvfp4's C ABI.
+
+Argument marshalling only: each function checks tensor dtypes, shapes and devices, takes
+the current HIP stream from PyTorch, passes raw pointers to the library and raises on a
+non-zero status. Every step of the computation runs in the library's HIP kernels.
+Function names follow the C entry points (include/nvfp4.h).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import check, load_library
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize(x: torch.Tensor, global_scale: float, packed: torch.Tensor | None = None,
+             scales: torch.Tensor | None = None, stream=None):
+    """NVFP4-quantize bf16 ``x`` [M, K] -> (packed uint8 [M, K/2], scales uint8 [M, K/16])."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    if packed is None:
+        packed = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    _need(packed, "packed", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    if tuple(packed.shape) != (M, K // 2) or tuple(scales.shape) != (M, K // 16):
+        raise ValueError("output shapes do not match x")
+    lib = load_library()
+    check(lib.nvfp4_quantize(_ptr(x), M, K, float(global_scale), _ptr(packed), _ptr(scales),
+                             _stream(stream)), "nvfp4_quantize")
+    return packed, scales
+
+
+def gemm(a_packed: torch.Tensor, a_scales: torch.Tensor, a_global_scale: float,
+         w_packed: torch.Tensor, w_scales: torch.Tensor, w_global_scale: float,
+         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Block-scaled W4A4 GEMM: bf16 [M, N] = a_gs * w_gs * A_hat @ W_hat^T."""
+    for t, n in ((a_packed, "a_packed"), (a_scales, "a_scales"), (w_packed, "w_packed"),
+                 (w_scales, "w_scales")):
+        _need(t, n, torch.uint8, 2)
+    M, Kh = a_packed.shape
+    N = w_packed.shape[0]
+    K = 2 * Kh
+    if tuple(w_packed.shape) != (N, Kh) or tuple(a_scales.shape) != (M, K // 16) or \
+            tuple(w_scales.shape) != (N, K // 16):
+        raise ValueError("operand shapes are inconsistent")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_packed.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape must be [M, N]")
+    lib = load_library()
+    check(lib.nvfp4_gemm(_ptr(a_packed), _ptr(a_scales), float(a_global_scale), _ptr(w_packed),
+                         _ptr(w_scales), float(w_global_scale), M, N, K, _ptr(out),
+                         _stream(stream)), "nvfp4_gemm")
+    return out
+
+
+def linear_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().nvfp4_linear_workspace_bytes(M, K))
+
+
+def linear(x: torch.Tensor, a_global_scale: float, w_packed: torch.Tensor,
+           w_scales: torch.Tensor, w_global_scale: float, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fused NVFP4 linear: quantize x under a_global_scale, then the W4A4 GEMM."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_packed, "w_packed", torch.uint8, 2)
+    _need(w_scales, "w_scales", torch.uint8, 2)
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if tuple(w_packed.shape) != (N, K // 2) or tuple(w_scales.shape) != (N, K // 16):
+        raise ValueError("weight shapes do not match x")
+    need = linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape must be [M, N]")
+    lib = load_library()
+    check(lib.nvfp4_linear(_ptr(x), float(a_global_scale), _ptr(w_packed), _ptr(w_scales),
+                           float(w_global_scale), M, N, K, _ptr(out), _ptr(workspace),
+                           workspace.numel(), _stream(stream)), "nvfp4_linear")
+    return out
+
+
+def workspace_views(workspace: torch.Tensor, M: int, K: int):
+    """(packed [M, K/2], scales [M, K/16]) views of a linear() workspace (layout of
+    nvfp4_linear: packed at 0, scales at round_up(M*K/2, 256))."""
+    off = (M * K // 2 + 255) // 256 * 256
+    packed = workspace[: M * K // 2].view(M, K // 2)
+    scales = workspace[off: off + M * K // 16].view(M, K // 16)
+    return packed, scales
+
+
+def amax(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Device fp32 [1] tensor holding max |x| over a bf16 tensor (any shape, contiguous)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 HIP tensor")
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=x.device)
+    lib = load_library()
+    check(lib.nvfp4_amax(_ptr(x), x.numel(), _ptr(out), _stream(stream)), "nvfp4_amax")
+    return out
+
+
+def global_scale_from_amax(a: float) -> float:
+    """RN32(amax / 2688) computed by the library (1.0 for amax == 0)."""
+    return float(load_library().nvfp4_global_scale_from_amax(float(a)))
+
+
+def calibrate(x: torch.Tensor, stream=None) -> float:
+    """Global scale of a bf16 tensor: device amax, read back (synchronises), then
+    RN32(amax / 2688). Used once per tensor, offline (weights) or at calibration time
+    (static activation scale)."""
+    a = amax(x, stream=stream)
+    return global_scale_from_amax(float(a.item()))

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the headers
+declare, and rejects bad arguments with the documented status before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from nvfp4_block_scaled_02_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from nvfp4_block_scaled_02_amd import build
+
+        build.build()
+    return L.load_library()
+
+
+def _declared_functions():
+    names = set()
+    for h in ("nvfp4.h", "nvfp4_selftest.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert declared == set(L.SIGNATURES), declared ^ set(L.SIGNATURES)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == L.ABI_VERSION
+    for s in range(7):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_status_string(99) == b"unknown status"
+
+
+# Fake but aligned device addresses: validation never dereferences them.
+P16 = ctypes.c_void_p(0x10000)
+P16b = ctypes.c_void_p(0x20000)
+NULL = ctypes.c_void_p(0)
+ODD = ctypes.c_void_p(0x10008)
+
+
+def test_quantize_validation(lib):
+    q = lib.nvfp4_quantize
+    assert q(NULL, 4, 32, 1.0, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, 1.0, NULL, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, 0.0, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, -1.0, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, float("nan"), P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, float("inf"), P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, 2.0**-101, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 32, 2.0**101, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 24, 1.0, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(P16, 4, 0, 1.0, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(P16, -1, 32, 1.0, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(P16, 2**40, 2**40, 1.0, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(ODD, 4, 32, 1.0, P16, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 4, 32, 1.0, ODD, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 4, 32, 1.0, P16, ctypes.c_void_p(0x20002), NULL) == L.MISALIGNED
+    # empty problem: success without touching a device
+    assert q(P16, 0, 32, 1.0, P16, P16b, NULL) == L.SUCCESS
+
+
+def test_gemm_validation(lib):
+    g = lib.nvfp4_gemm
+    args = [P16, P16b, 1.0, P16, P16b, 1.0, 8, 8, 64, P16, NULL]
+
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return g(*a)
+
+    assert call({0: NULL}) == L.INVALID_VALUE
+    assert call({4: NULL}) == L.INVALID_VALUE
+    assert call({9: NULL}) == L.INVALID_VALUE
+    assert call({2: 0.0}) == L.INVALID_VALUE
+    assert call({5: float("inf")}) == L.INVALID_VALUE
+    assert call({8: 40}) == L.INVALID_SHAPE
+    assert call({8: 0}) == L.INVALID_SHAPE
+    assert call({6: -3}) == L.INVALID_SHAPE
+    assert call({7: -3}) == L.INVALID_SHAPE
+    assert call({0: ODD}) == L.MISALIGNED
+    assert call({9: ODD}) == L.MISALIGNED
+    assert call({1: ctypes.c_void_p(0x20001)}) == L.MISALIGNED
+    assert call({6: 0}) == L.SUCCESS
+    assert call({7: 0}) == L.SUCCESS
+
+
+def test_linear_validation_and_workspace(lib):
+    ws = lib.nvfp4_linear_workspace_bytes
+    assert ws(4608, 3072) == (4608 * 3072 // 2) + ((4608 * 3072 // 16 + 255) // 256 * 256)
+    assert ws(3, 16) == 256 + 256
+    assert ws(3, 24) == 0 and ws(-1, 16) == 0
+    lin = lib.nvfp4_linear
+    need = ws(8, 64)
+    base = [P16, 1.0, P16b, P16b, 1.0, 8, 8, 64, P16, ctypes.c_void_p(0x40000), need, NULL]
+    assert lin(*base[:10], need - 1, NULL) == L.WORKSPACE
+    b = list(base)
+    b[9] = NULL
+    assert lin(*b) == L.INVALID_VALUE
+    b = list(base)
+    b[0] = ODD
+    assert lin(*b) == L.MISALIGNED
+    b = list(base)
+    b[7] = 72
+    assert lin(*b) == L.INVALID_SHAPE
+    b = list(base)
+    b[5] = 0
+    assert lin(*b) == L.SUCCESS
+
+
+def test_amax_validation(lib):
+    out = ctypes.c_void_p(0x30000)
+    assert lib.nvfp4_amax(NULL, 16, out, NULL) == L.INVALID_VALUE
+    assert lib.nvfp4_amax(P16, -1, out, NULL) == L.INVALID_SHAPE
+    assert lib.nvfp4_amax(ODD, 16, out, NULL) == L.MISALIGNED
+
+
+def test_no_device_is_reported(lib, gpu_available):
+    if gpu_available:
+        pytest.skip("a GPU is present")
+    assert lib.nvfp4_quantize(P16, 4, 32, 1.0, P16, P16b, NULL) == L.UNSUPPORTED_DEVICE
+    assert lib.nvfp4_gemm(P16, P16b, 1.0, P16, P16b, 1.0, 8, 8, 64, P16, NULL) == \
+        L.UNSUPPORTED_DEVICE
+
+
+def test_global_scale_from_amax_matches_oracle(lib):
+    from oracle import nvfp4_oracle as O
+
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        np.float32([0.0, 1.0, 2688.0, 448.0 * 6, 1e-30, 3.3e38]),
+        np.exp2(rng.uniform(-120, 120, 5000)).astype(np.float32),
+    ])
+    for v in vals:
+        got = np.float32(lib.nvfp4_global_scale_from_amax(float(v)))
+        assert got.view(np.uint32) == O.global_scale_from_amax(v).view(np.uint32), v
+    assert np.isnan(lib.nvfp4_global_scale_from_amax(-1.0))
+    assert np.isnan(lib.nvfp4_global_scale_from_amax(float("inf")))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        L.load_library(str(tmp_path / "missing.so"))

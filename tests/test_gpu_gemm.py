@@ -1,0 +1,130 @@
+"""nvfp4_gemm and nvfp4_linear on the GPU against the CPU oracle.
+
+The GEMM's exact result has many correct bf16 roundings (summation order is free), so
+each output element must lie within 2^-10 * sum_k |a_k w_k| + 1 bf16 ulp of the exact
+float64 reference. Small shapes are compared in full; the FLUX-sized workloads run at
+full size in the bench's launch configuration and are compared on sampled rows (every
+column of each sampled row)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_02_amd as nv
+from gpu_helpers import bf16_to_dev, guarded, say, to_host, u8_to_dev
+from oracle import nvfp4_oracle as O
+from workloads import make, names, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(x, w, ags=None):
+    ags = O.global_scale(x) if ags is None else ags
+    wgs = O.global_scale(w)
+    ap, as_ = O.quantize(x, ags)
+    wp, ws = O.quantize(w, wgs)
+    return ags, wgs, ap, as_, wp, ws
+
+
+def _gemm_dev(ap, as_, ags, wp, ws, wgs, guard=True):
+    M, N = ap.shape[0], wp.shape[0]
+    if guard:
+        out, ok = guarded((M, N), torch.bfloat16)
+    else:
+        out, ok = torch.empty((M, N), dtype=torch.bfloat16, device="cuda"), (lambda: True)
+    nv.gemm(u8_to_dev(ap), u8_to_dev(as_), float(ags), u8_to_dev(wp), u8_to_dev(ws),
+            float(wgs), out=out)
+    return out, ok
+
+
+def _assert_close(got_bits, ap, as_, ags, wp, ws, wgs, label):
+    ref, absref = O.gemm_ref(ap, as_, ags, wp, ws, wgs)
+    ok, worst, nbad = O.check_gemm(got_bits, ref, absref)
+    assert ok, f"{label}: {nbad} elements out of tolerance (worst err/tol {worst:.3g})"
+    return worst
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 128, 256),      # tiny config shape
+    (1, 64, 64), (17, 72, 128), (256, 256, 256), (300, 520, 320), (513, 260, 1024),
+    (33, 40, 16), (40, 36, 48), (64, 64, 80), (130, 132, 144),   # K % 64 != 0, K % 32 == 16
+    (255, 257, 192), (7, 3, 32),
+])
+def test_gemm_small_shapes_in_full(M, N, K):
+    rng = np.random.default_rng(M * 131 + N * 7 + K)
+    x = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ags, wgs, ap, as_, wp, ws = _operands(x, w)
+    say("gemm", M, N, K)
+    out, ok = _gemm_dev(ap, as_, ags, wp, ws, wgs)
+    got = to_host(out)
+    assert ok(), "write outside out"
+    _assert_close(got, ap, as_, ags, wp, ws, wgs, f"{M}x{N}x{K}")
+
+
+def test_gemm_exact_cases():
+    """Closed forms: zero operands give exact zeros; W = 3 * I reproduces the dequantised
+    activations (the epilogue rounds them to bf16)."""
+    rng = np.random.default_rng(3)
+    K = 128
+    x = to_bf16_bits(rng.standard_normal((96, K)).astype(np.float32))
+    ags = O.global_scale(x)
+    ap, as_ = O.quantize(x, ags)
+    eye = to_bf16_bits((np.eye(K) * 3.0).astype(np.float32))
+    wgs = np.float32(2.0**-6)
+    wp, ws = O.quantize(eye, wgs)
+    say("gemm identity")
+    out, _ = _gemm_dev(ap, as_, ags, wp, ws, wgs)
+    want = to_bf16_bits(O.dequantize(ap, as_, ags).astype(np.float32) * np.float32(3.0))
+    # alpha = RN(ags * 2^-6) is exact, acc = 3 * 2^6 * q * s is exact, so out is exact
+    assert np.array_equal(to_host(out), want)
+    zp, zs = O.quantize(np.zeros((50, K), np.uint16), 1.0)
+    out, _ = _gemm_dev(zp, zs, 1.0, wp, ws, wgs)
+    assert np.all((to_host(out) & 0x7FFF) == 0)
+
+
+def _sample_rows(M, rng, n=48):
+    rows = {0, M - 1, M // 2}
+    rows |= set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", names())
+def test_gemm_workloads_full_size_sampled_rows(name):
+    wl = make(name)
+    d = wl.generate()
+    ags_src = d.get("calib", d["x"])
+    ags = O.global_scale(ags_src)
+    wgs = O.global_scale(d["w"])
+    ap, as_ = O.quantize(d["x"], ags)
+    wp, ws = O.quantize(d["w"], wgs)
+    say("gemm workload", name, wl.M, wl.N, wl.K)
+    out, ok = _gemm_dev(ap, as_, ags, wp, ws, wgs, guard=wl.M * wl.N < 64 * 2**20)
+    got = to_host(out)
+    assert ok()
+    rows = _sample_rows(wl.M, np.random.default_rng(11))
+    _assert_close(got[rows], ap[rows], as_[rows], ags, wp, ws, wgs, name)
+    # determinism: a second launch gives the same bits
+    out2, _ = _gemm_dev(ap, as_, ags, wp, ws, wgs, guard=False)
+    assert np.array_equal(to_host(out2), got)
+
+
+@pytest.mark.parametrize("name", ["tiny", "attn_out", "mlp_up_static", "odd_m17", "odd_m1000"])
+def test_linear_matches_quantize_then_gemm(name):
+    wl = make(name)
+    d = wl.generate()
+    ags = O.global_scale(d.get("calib", d["x"]))
+    wgs = O.global_scale(d["w"])
+    wp, ws = O.quantize(d["w"], wgs)
+    xd = bf16_to_dev(d["x"])
+    ws_bytes = nv.linear_workspace_bytes(wl.M, wl.K)
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    say("linear", name)
+    out = nv.linear(xd, float(ags), u8_to_dev(wp), u8_to_dev(ws), float(wgs), workspace=work)
+    got = to_host(out)
+    qp, qs = nv.workspace_views(work, wl.M, wl.K)
+    ap, as_ = O.quantize(d["x"], ags)
+    assert np.array_equal(to_host(qp), ap) and np.array_equal(to_host(qs), as_)
+    g2, _ = _gemm_dev(ap, as_, ags, wp, ws, wgs, guard=False)
+    assert np.array_equal(to_host(g2), got)
+    rows = _sample_rows(wl.M, np.random.default_rng(12), n=32)
+    _assert_close(got[rows], ap[rows], as_[rows], ags, wp, ws, wgs, name)
