@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rotate-mb", type=int, default=1024,
                     help="bytes of rotated activation buffers for the quantize bandwidth leg")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run 3 plain device copies of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -177,6 +180,15 @@ def main():
     q_rot_ms = qa.elapsed_time(qb) / n_q
     q_gbs = QUANT_BYTES_PER_ELEM * M * K / (q_rot_ms * 1e-3) / 1e9
     del xs, outs
+
+    if args.copy_calibration_mb:
+        nbytes = args.copy_calibration_mb * 2**20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     result = {
         "metric": METRIC,

@@ -66,17 +66,19 @@ NVFP4_HD uint32_t e2m1_magnitude_encode(float y) {
 }
 
 // Correctly rounded x / d for a bf16-valued x (8 significant bits) and a normal
-// binary32 d, given r = RN(1/d): y0 = RN(x r), rho = RN(x - y0 d) (exact, fma),
-// y = RN(y0 + rho r) (Markstein's correction). An exhaustive check over every pair of
-// significands (bf16 x, binary32 d) shows y == RN(x/d). y0 is clamped to [-8, 8]
-// first; any |x/d| >= 6 saturates the E2M1 code, so the clamp only keeps a huge
-// quotient from turning into inf - inf = NaN. With r == 0 (for d == 0) the result is
-// a zero carrying the sign of x.
+// binary32 d, given r = RN(1/d) (Markstein's correction):
+//   y0 = RN(x r),  e = RN(y0 d - x) (exact, fma),  y = RN(y0 - e r).
+// An exhaustive check over every pair of significands (bf16 x, binary32 d) shows
+// y == RN(x/d). Writing the residual as y0 d - x (not x - y0 d) keeps the sign of a
+// zero x: for x = -0, e = +0 and y = -0 - (+0)r = -0. y0 is clamped to [-8, 8] first;
+// any |x/d| >= 6 saturates the E2M1 code, so the clamp only keeps a huge quotient
+// from turning into inf - inf = NaN. With r == 0 (for d == 0) the result is a zero
+// carrying the sign of x.
 NVFP4_HD float div_by_scale(float x, float d, float r) {
   float y0 = x * r;
   y0 = y0 < -8.0f ? -8.0f : (y0 > 8.0f ? 8.0f : y0);
-  float rho = __builtin_fmaf(-y0, d, x);
-  return __builtin_fmaf(rho, r, y0);
+  const float e = __builtin_fmaf(y0, d, -x);
+  return __builtin_fmaf(-e, r, y0);
 }
 
 // Per-block quantization state: the scale code, d = RN(s * gs) and r = RN(1/d) (0 when

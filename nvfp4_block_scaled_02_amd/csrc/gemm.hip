@@ -26,8 +26,9 @@
 //    operands use the same mapping, so each product pairs equal k; each lane's 8
 //    elements sit inside one 16-element block and share one scale.
 //  * Decode: the gfx950 conversion v_cvt_scalef32_pk_f16_fp4 turns two codes into two
-//    f16 values times 2^8; one packed f16 multiply by the block scale times 2^-8
-//    (which is the E4M3 byte shifted into f16 position) gives q * s exactly.
+//    f16 values, v_cvt_scalef32_pk_f16_fp8 turns a lane's two E4M3 scale bytes into f16,
+//    and one packed f16 multiply per pair gives q * s exactly (all values are normal
+//    f16, so no step depends on the denormal mode).
 //  * The weights are the MFMA's A operand and the activations its B operand, so each
 //    lane ends up holding 4 consecutive output columns of one row: 8-byte bf16 stores.
 //  * Epilogue: fp32 accumulator * alpha (fp32), round to nearest even bf16.
@@ -43,25 +44,36 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// f16 pair holding s * 2^-8 in both halves for E4M3 code c (exact; subnormal E4M3 codes
-// become f16 subnormals).
-__device__ __forceinline__ half2_t scale_pair(uint32_t c) {
-  return __builtin_bit_cast(half2_t, c * 0x00800080u);
+// f16 values {s(c0), s(c1)} of the two E4M3 scale codes in the low 16 bits of v (c0 in
+// bits 0..7). Every E4M3 value, subnormals included, is a normal f16, so the
+// conversion is exact.
+template <bool kHw>
+__device__ __forceinline__ half2_t scales_to_f16(uint32_t v) {
+  if constexpr (kHw) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+  } else {
+    half2_t r;
+    r.x = (_Float16)e4m3_decode(v & 0xFFu);
+    r.y = (_Float16)e4m3_decode((v >> 8) & 0xFFu);
+    return r;
+  }
 }
 
-// f16 high bytes of q * 256 for E2M1 magnitude codes 0..7 (the low byte is always 0).
-constexpr uint32_t kLutLo = 0x5E5C5800u;  // 0, 128, 256, 384
-constexpr uint32_t kLutHi = 0x66646260u;  // 512, 768, 1024, 1536
+// f16 high bytes of the E2M1 magnitudes 0, .5, 1, 1.5 | 2, 3, 4, 6 (low bytes are 0).
+constexpr uint32_t kLutLo = 0x3E3C3800u;
+constexpr uint32_t kLutHi = 0x46444240u;
 
-// Eight E2M1 codes (element i in bits 4i..4i+3 of p) times the block scale, as f16.
+// Eight E2M1 codes (element i in bits 4i..4i+3 of p) times the block scale s (both
+// halves of s2), as f16. q and s are normal f16 values and q * s (at most 6
+// significant bits, in [2^-10, 2688]) is a normal f16, so the product is exact.
 template <bool kHw>
 __device__ __forceinline__ half8_t decode8(uint32_t p, half2_t s2) {
   half2_t h[4];
   if constexpr (kHw) {
-    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 256.0f, 0);
-    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 256.0f, 1);
-    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 256.0f, 2);
-    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 256.0f, 3);
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 1.0f, 0);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 1.0f, 1);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 1.0f, 2);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(p, 1.0f, 3);
   } else {
     // Byte-table lookup: even elements from the low nibbles, odd from the high ones,
     // signs moved to bit 7 of each byte; then interleave into f16 high bytes.
@@ -245,13 +257,13 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmProblem p) {
         half8_t wf[FN], xf[FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-          const uint32_t word = wraw[i][j];
-          wf[i] = decode8<kHw>(word, scale_pair((wsc[i] >> (8 * (j >> 1))) & 0xFFu));
+          const half2_t s01 = scales_to_f16<kHw>(wsc[i]);
+          wf[i] = decode8<kHw>(wraw[i][j], j < 2 ? s01.xx : s01.yy);
         }
 #pragma unroll
         for (int g = 0; g < FM; ++g) {
-          const uint32_t word = xraw[g][j];
-          xf[g] = decode8<kHw>(word, scale_pair((xsc[g] >> (8 * (j >> 1))) & 0xFFu));
+          const half2_t s01 = scales_to_f16<kHw>(xsc[g]);
+          xf[g] = decode8<kHw>(xraw[g][j], j < 2 ? s01.xx : s01.yy);
         }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -321,7 +333,8 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     if (i * 4 + e < nbytes) word |= (uint32_t)packed[i * 4 + e] << (8 * e);
-  const half8_t v = decode8<kHw>(word, scale_pair(scales[i]));
+  const half2_t s2 = scales_to_f16<kHw>(scales[i]);
+  const half8_t v = decode8<kHw>(word, s2.xx);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     if (i * 8 + e < nbytes * 2) out[i * 8 + e] = __builtin_bit_cast(uint16_t, v[e]);

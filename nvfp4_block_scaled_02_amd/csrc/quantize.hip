@@ -158,10 +158,12 @@ __global__ void selftest_division_kernel(unsigned long long* __restrict__ count,
   if (dm >= (1u << 23)) return;
   const float d = u2f(0x3F800000u | dm);
   const float r = 1.0f / d;
-  for (uint32_t xm = 0; xm < 256; ++xm) {
-    const float x = u2f(((127u + (xm >> 7)) << 23) | ((xm & 127u) << 16));
-    const float y = div_by_scale(x, d, r);
-    const float q = x / d;
+  for (uint32_t xm = 0; xm < 260; ++xm) {
+    // bf16 significands of x in [1, 4), then +0, -0 (whose quotient keeps the sign)
+    const float x = xm < 256 ? u2f(((127u + (xm >> 7)) << 23) | ((xm & 127u) << 16))
+                             : (xm & 1u ? -0.0f : 0.0f);
+    const float y = xm < 258 ? div_by_scale(x, d, r) : div_by_scale(x, 0.0f, 0.0f);
+    const float q = xm < 258 ? x / d : x;
     if (f2u(y) != f2u(q)) {
       const unsigned long long k = atomicAdd(count, 1ull);
       if (k < 8) {

@@ -56,6 +56,18 @@ int main(int argc, char** argv) {
         if (f2u(yn) != (f2u(q) | 0x80000000u)) ++bad;
       }
     }
+    // zeros keep their sign, for every divisor and for the d == 0 (r = 0) case
+    for (uint32_t dm = 0; dm < (1u << 23); dm += 97) {
+      const float d = u2f(0x3F800000u | dm);
+      const float r = 1.0f / d;
+      if (f2u(div_by_scale(0.0f, d, r)) != 0u) ++bad;
+      if (f2u(div_by_scale(-0.0f, d, r)) != 0x80000000u) ++bad;
+    }
+    for (uint32_t xm = 0; xm < 65536; ++xm) {  // every finite bf16 pattern with d == 0
+      if ((xm & 0x7F80u) == 0x7F80u) continue;  // inputs are finite by contract
+      const float x = u2f(xm << 16);
+      if (f2u(div_by_scale(x, 0.0f, 0.0f)) != (f2u(x) & 0x80000000u)) ++bad;
+    }
     printf("mismatches %llu\n", bad);
     return 0;
   }

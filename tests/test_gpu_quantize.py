@@ -25,7 +25,9 @@ def _check_quantize(x_bits, gs, label):
     wp, ws = O.quantize(x_bits, gs)
     bad = np.argwhere(gp != wp)
     assert np.array_equal(gsc, ws), (label, np.argwhere(gsc != ws)[:5])
-    assert bad.size == 0, (label, bad[:5])
+    detail = [(int(r), int(c), hex(int(gp[r, c])), hex(int(wp[r, c])),
+               [hex(int(v)) for v in x_bits[r, 2 * c: 2 * c + 2]]) for r, c in bad[:5]]
+    assert bad.size == 0, (label, len(bad), detail)
     return p, s
 
 
