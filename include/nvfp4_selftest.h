@@ -42,9 +42,10 @@ int nvfp4_selftest_block_scale(const float* amax, float global_scale, uint8_t* c
                                int64_t n, void* stream);
 
 /* The GEMM's operand decode: packed[nbytes] holds 2*nbytes E2M1 codes (low nibble
- * first); scales[(nbytes + 3) / 4] holds one E4M3 code per 4 packed bytes. Writes
- * 2*nbytes f16 bit patterns of code value * scale to hw_f16 (conversion-instruction
- * decode) and sw_f16 (byte-table decode). */
+ * first); scales[nbytes / 4] holds one E4M3 code per 4 packed bytes. Writes 2*nbytes
+ * f16 bit patterns of code value * scale to hw_f16 (conversion-instruction decode) and
+ * sw_f16 (byte-table decode). nbytes must be a multiple of 4 and both outputs 16-byte
+ * aligned, else NVFP4_ERROR_HIP (hipErrorInvalidValue). */
 int nvfp4_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw_f16,
                           uint16_t* sw_f16, int64_t nbytes, void* stream);
 

@@ -335,9 +335,10 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
     if (i * 4 + e < nbytes) word |= (uint32_t)packed[i * 4 + e] << (8 * e);
   const half2_t s2 = scales_to_f16<kHw>(scales[i]);
   const half8_t v = decode8<kHw>(word, s2.xx);
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (i * 8 + e < nbytes * 2) out[i * 8 + e] = __builtin_bit_cast(uint16_t, v[e]);
+  // Store the whole vector (the GEMM also consumes whole vectors): this compiler
+  // version folds per-element reads of the fp4->f16 conversion result to its low
+  // element, so no element is extracted here. nbytes is a multiple of 4.
+  *(u32x4*)&out[i * 8] = __builtin_bit_cast(u32x4, v);
 }
 
 }  // namespace
@@ -354,6 +355,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
 hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,
                                   uint16_t* sw, int64_t nbytes, hipStream_t stream) {
   if (nbytes == 0) return hipSuccess;
+  if (nbytes % 4 != 0 || (uintptr_t)hw % 16 != 0 || (uintptr_t)sw % 16 != 0)
+    return hipErrorInvalidValue;
   const int64_t nthreads = (nbytes + 3) / 4;
   const unsigned grid = (unsigned)((nthreads + 255) / 256);
   hipLaunchKernelGGL(selftest_decode_kernel<true>, dim3(grid), dim3(256), 0, stream, packed, scales,

@@ -99,9 +99,7 @@ def test_block_scale_matches_oracle(lib, gs):
     assert np.array_equal(to_host(d).view(np.uint32), want_d.view(np.uint32))
 
 
-def test_gemm_operand_decode_is_exact(lib):
-    """Every packed byte under every finite E4M3 scale decodes to q * s exactly (f16)."""
-    say("decode all bytes x scales")
+def _decode_all(lib):
     nb = 256 * 127 * 4  # each (byte, scale) pair: the byte repeated in a 4-byte group
     byte = np.repeat(np.tile(np.arange(256, dtype=np.uint8), 127), 4)
     scale = np.repeat(np.arange(127, dtype=np.uint8), 256)
@@ -112,11 +110,27 @@ def test_gemm_operand_decode_is_exact(lib):
     assert lib.nvfp4_selftest_decode(_p(bd), _p(sd), _p(hw), _p(sw), nb, _s()) == 0
     codes = O.unpack_codes(byte.reshape(1, -1))[0]
     s_el = np.repeat(O.e4m3_decode(scale), 8)
-    want = (O.e2m1_decode(codes) * s_el).astype(np.float16)
-    assert np.array_equal(want.astype(np.float64), O.e2m1_decode(codes) * s_el)  # exact in f16
-    want_bits = want.view(np.uint16)
-    for label, got in (("table", to_host(sw).view(np.uint16)), ("instruction", to_host(hw).view(np.uint16))):
-        bad = np.nonzero(got != want_bits)[0]
-        detail = [(int(i), int(codes[i]), int(scale[i // 8]), hex(int(got[i])), hex(int(want_bits[i])))
-                  for i in bad[:8]]
-        assert bad.size == 0, (label, bad.size, detail)
+    exact = O.e2m1_decode(codes) * s_el
+    want = exact.astype(np.float16)
+    assert np.array_equal(want.astype(np.float64), exact)  # q * s is exact in f16
+    return codes, np.repeat(scale, 8), want.view(np.uint16), {
+        "table": to_host(sw).view(np.uint16), "instruction": to_host(hw).view(np.uint16)}
+
+
+@pytest.mark.parametrize("path", ["instruction", "table"])
+def test_gemm_operand_decode_is_exact(lib, path):
+    """Every packed byte under every finite E4M3 scale decodes to q * s exactly (f16)."""
+    say("decode all bytes x scales", path)
+    codes, scales, want, got_all = _decode_all(lib)
+    got = got_all[path]
+    bad = np.nonzero(got != want)[0]
+    if bad.size:
+        value_equal = np.float16(got[bad].view(np.float16)) == np.float16(want[bad].view(np.float16))
+        by_scale = np.bincount(scales[bad], minlength=127)
+        by_code = np.bincount(codes[bad], minlength=16)
+        detail = [(int(i), int(codes[i]), int(scales[i]), hex(int(got[i])), hex(int(want[i])))
+                  for i in bad[:12]]
+        raise AssertionError(
+            f"{path}: {bad.size} mismatches; {int(value_equal.sum())} differ only in the sign "
+            f"of zero; by scale code (nonzero) {[(k, int(v)) for k, v in enumerate(by_scale) if v][:40]}; "
+            f"by element code {by_code.tolist()}; first {detail}")
