@@ -35,6 +35,11 @@
 #include "codec.hpp"
 #include "kernels.hpp"
 
+// VALU instructions the scheduler is asked to place after each MFMA of a k-step.
+#ifndef NVFP4_GEMM_VALU_PER_MFMA
+#define NVFP4_GEMM_VALU_PER_MFMA 5
+#endif
+
 namespace nvfp4 {
 
 namespace {
@@ -99,7 +104,41 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-constexpr int kThreads = 256;
+// Epilogue shared by the GEMM kernels: lane holds, for weight group i and activation
+// group g, output row m = m_base + 32g + (lane % 32) and columns
+// n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is scaled by
+// alpha in fp32, rounded to nearest even bf16 and stored (8 bytes per lane when the row
+// pitch allows).
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
+                                           int64_t m_base, int64_t n_base, int lane) {
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const bool n_vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < FM; ++g) {
+    const int64_t m = m_base + g * 32 + r32;
+    if (m >= p.M) continue;
+    uint16_t* orow = p.out + m * p.N;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+        if (n_vec && n + 3 < p.N) {
+          *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+        }
+      }
+    }
+  }
+}
 
 template <int BM, int BN, int KC>
 struct alignas(16) GemmSmem {
@@ -110,31 +149,36 @@ struct alignas(16) GemmSmem {
 };
 
 // Registers that carry one stage from global memory to LDS.
-template <int ROWS, int KC>
+template <int ROWS, int KC, int NT>
 struct StageRegs {
-  static constexpr int kPieces = ROWS * KC * 2 / kThreads;  // 16-byte pieces per thread
-  static constexpr int kScales = (ROWS * KC + kThreads - 1) / kThreads;
-  static constexpr bool kScalesExact = (ROWS * KC) % kThreads == 0;
+  static_assert((ROWS * KC * 2) % NT == 0, "pieces must divide evenly among threads");
+  static constexpr int kPieces = ROWS * KC * 2 / NT;  // 16-byte pieces per thread
+  static constexpr int kScales = (ROWS * KC + NT - 1) / NT;
+  static constexpr bool kScalesExact = (ROWS * KC) % NT == 0;
   u32x4 piece[kPieces];
   uint32_t scale[kScales];
 };
 
-// Load one operand's stage (ROWS rows starting at row0, K chunks [k64, k64 + KC)).
-// kFast: K is a multiple of 64*KC and rows are 16-byte aligned (K % 32 == 0).
-template <int ROWS, int KC, bool kFast>
-__device__ __forceinline__ void load_stage(StageRegs<ROWS, KC>& r, const uint8_t* __restrict__ packed,
+// Load one operand's stage: ROWS rows from row0, K chunks [k64, k64 + KC) of 64 elements.
+// Consecutive threads take consecutive 16-byte pieces of the same row (a row holds
+// 2*KC pieces per stage), so a wave reads whole cache lines. Rows past nrows repeat the
+// last row (their results are never stored). kFast: K is a multiple of 64*KC and the
+// operands are 16-byte (packed) / 4-byte (scales) aligned; otherwise pieces and scale
+// bytes past K read as zero (a zero scale makes the decoded value zero).
+template <int ROWS, int KC, int NT, bool kFast>
+__device__ __forceinline__ void load_stage(StageRegs<ROWS, KC, NT>& r, const uint8_t* __restrict__ packed,
                                            const uint8_t* __restrict__ scales, int64_t row0,
                                            int64_t nrows, int64_t K, int64_t k64, int tid) {
   const int64_t pitch = K >> 1;
   const int64_t spitch = K >> 4;
 #pragma unroll
-  for (int p = 0; p < StageRegs<ROWS, KC>::kPieces; ++p) {
-    const int i = tid + p * kThreads;
-    const int row = i % ROWS;
-    const int kh = i / ROWS;  // chunk * 2 + half
+  for (int p = 0; p < StageRegs<ROWS, KC, NT>::kPieces; ++p) {
+    const int i = tid + p * NT;
+    const int row = i / (2 * KC);
+    const int q = i % (2 * KC);  // chunk * 2 + half
     int64_t grow = row0 + row;
     grow = grow < nrows ? grow : nrows - 1;
-    const int64_t kel = (k64 + (kh >> 1)) * 64 + (kh & 1) * 32;  // first element of the piece
+    const int64_t kel = (k64 + (q >> 1)) * 64 + (q & 1) * 32;  // first element of the piece
     const uint8_t* src = packed + grow * pitch + (kel >> 1);
     if constexpr (kFast) {
       r.piece[p] = *(const u32x4*)src;
@@ -152,11 +196,11 @@ __device__ __forceinline__ void load_stage(StageRegs<ROWS, KC>& r, const uint8_t
     }
   }
 #pragma unroll
-  for (int q = 0; q < StageRegs<ROWS, KC>::kScales; ++q) {
-    const int i = tid + q * kThreads;
-    if (StageRegs<ROWS, KC>::kScalesExact || i < ROWS * KC) {
-      const int row = i % ROWS;
-      const int kc = i / ROWS;
+  for (int q = 0; q < StageRegs<ROWS, KC, NT>::kScales; ++q) {
+    const int i = tid + q * NT;
+    if (StageRegs<ROWS, KC, NT>::kScalesExact || i < ROWS * KC) {
+      const int row = i / KC;
+      const int kc = i % KC;
       int64_t grow = row0 + row;
       grow = grow < nrows ? grow : nrows - 1;
       const int64_t blk = (k64 + kc) * 4;  // first scale of the chunk
@@ -174,37 +218,42 @@ __device__ __forceinline__ void load_stage(StageRegs<ROWS, KC>& r, const uint8_t
   }
 }
 
-template <int ROWS, int KC>
-__device__ __forceinline__ void store_stage(const StageRegs<ROWS, KC>& r, uint8_t (*dst)[ROWS * 32],
+// Store a stage into LDS in MFMA fragment order (see the file comment).
+template <int ROWS, int KC, int NT>
+__device__ __forceinline__ void store_stage(const StageRegs<ROWS, KC, NT>& r, uint8_t (*dst)[ROWS * 32],
                                             uint32_t (*dscale)[ROWS], int tid) {
 #pragma unroll
-  for (int p = 0; p < StageRegs<ROWS, KC>::kPieces; ++p) {
-    const int i = tid + p * kThreads;
-    const int row = i % ROWS;
-    const int kh = i / ROWS;
-    const int slot = (row >> 5) * 64 + (kh & 1) * 32 + (row & 31);
-    *(u32x4*)&dst[kh >> 1][slot * 16] = r.piece[p];
+  for (int p = 0; p < StageRegs<ROWS, KC, NT>::kPieces; ++p) {
+    const int i = tid + p * NT;
+    const int row = i / (2 * KC);
+    const int q = i % (2 * KC);
+    const int slot = (row >> 5) * 64 + (q & 1) * 32 + (row & 31);
+    *(u32x4*)&dst[q >> 1][slot * 16] = r.piece[p];
   }
 #pragma unroll
-  for (int q = 0; q < StageRegs<ROWS, KC>::kScales; ++q) {
-    const int i = tid + q * kThreads;
-    if (StageRegs<ROWS, KC>::kScalesExact || i < ROWS * KC) dscale[i / ROWS][i % ROWS] = r.scale[q];
+  for (int q = 0; q < StageRegs<ROWS, KC, NT>::kScales; ++q) {
+    const int i = tid + q * NT;
+    if (StageRegs<ROWS, KC, NT>::kScalesExact || i < ROWS * KC) dscale[i % KC][i / KC] = r.scale[q];
   }
 }
 
-template <int BM, int BN, int KC, bool kHw, bool kFast>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmProblem p) {
+// WM x WN waves; wave (wave_m, wave_n) owns activation rows [wave_m*WTM, +WTM) and
+// weight rows (output columns) [wave_n*WTN, +WTN) of the BM x BN tile.
+template <int BM, int BN, int KC, int WM, int WN, bool kHw, bool kFast>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
+  constexpr int NT = 64 * WM * WN;
   __shared__ GemmSmem<BM, BN, KC> sm;
-  constexpr int WTM = BM / 2;  // activation rows per wave
-  constexpr int WTN = BN / 2;  // weight rows (output columns) per wave
+  constexpr int WTM = BM / WM;  // activation rows per wave
+  constexpr int WTN = BN / WN;  // weight rows (output columns) per wave
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
+  static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tiles are multiples of 32");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wave_n = wave & 1;
-  const int wave_m = wave >> 1;
+  const int wave_n = wave % WN;
+  const int wave_m = wave / WN;
 
   const int64_t tiles_n = (p.N + BN - 1) / BN;
   const int64_t tile_m = blockIdx.x / tiles_n;
@@ -221,102 +270,303 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmProblem p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
 
-  StageRegs<BM, KC> xr;
-  StageRegs<BN, KC> wr;
-  load_stage<BM, KC, kFast>(xr, p.a_packed, p.a_scales, m0, p.M, p.K, 0, tid);
-  load_stage<BN, KC, kFast>(wr, p.w_packed, p.w_scales, n0, p.N, p.K, 0, tid);
-  store_stage<BM, KC>(xr, sm.x[0], sm.xs[0], tid);
-  store_stage<BN, KC>(wr, sm.w[0], sm.ws[0], tid);
+  StageRegs<BM, KC, NT> xr;
+  StageRegs<BN, KC, NT> wr;
+  load_stage<BM, KC, NT, kFast>(xr, p.a_packed, p.a_scales, m0, p.M, p.K, 0, tid);
+  load_stage<BN, KC, NT, kFast>(wr, p.w_packed, p.w_scales, n0, p.N, p.K, 0, tid);
+  store_stage<BM, KC, NT>(xr, sm.x[0], sm.xs[0], tid);
+  store_stage<BN, KC, NT>(wr, sm.w[0], sm.ws[0], tid);
   __syncthreads();
 
   const int h = lane >> 5;
   const int r32 = lane & 31;
 
+  // Main loop over K stages of KC chunks (64 elements each). The body is branch-free
+  // (the prefetch issued on the last stage re-reads that stage) so the scheduler sees
+  // one region per stage. Within a stage the k-steps (4 per chunk) are flattened: the
+  // fragments of chunk c+1 are read from LDS while chunk c computes, and the decode of
+  // k-step s+1 is issued before the MFMAs of k-step s, so VALU decode can overlap the
+  // matrix core.
+  constexpr int kSteps = 4 * KC;
   for (int64_t t = 0; t < nk; ++t) {
     const int buf = (int)(t & 1);
-    if (t + 1 < nk) {
-      load_stage<BM, KC, kFast>(xr, p.a_packed, p.a_scales, m0, p.M, p.K, (t + 1) * KC, tid);
-      load_stage<BN, KC, kFast>(wr, p.w_packed, p.w_scales, n0, p.N, p.K, (t + 1) * KC, tid);
-    }
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 wraw[FN], xraw[FM];
-      uint32_t wsc[FN], xsc[FM];
+    const int64_t tn = t + 1 < nk ? t + 1 : t;
+    load_stage<BM, KC, NT, kFast>(xr, p.a_packed, p.a_scales, m0, p.M, p.K, tn * KC, tid);
+    load_stage<BN, KC, NT, kFast>(wr, p.w_packed, p.w_scales, n0, p.N, p.K, tn * KC, tid);
+    // Keep the prefetch at the top of the stage: left to itself the scheduler sinks
+    // these loads next to their LDS stores at the end of the body, exposing the whole
+    // memory latency once per stage.
+    __builtin_amdgcn_sched_barrier(0);
+
+    u32x4 wraw[KC][FN], xraw[KC][FM];
+    uint32_t wsr[KC][FN], xsr[KC][FM];  // the two scale bytes (blocks 2h, 2h+1) per fragment
+    auto read_chunk = [&](int kc) {
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
-        wraw[i] = *(const u32x4*)&sm.w[buf][kc][((wave_n * FN + i) * 64 + lane) * 16];
-        wsc[i] = *(const uint16_t*)((const uint8_t*)&sm.ws[buf][kc][wave_n * WTN + i * 32 + r32] + 2 * h);
+        wraw[kc][i] = *(const u32x4*)&sm.w[buf][kc][((wave_n * FN + i) * 64 + lane) * 16];
+        wsr[kc][i] = *(const uint16_t*)((const uint8_t*)&sm.ws[buf][kc][wave_n * WTN + i * 32 + r32] + 2 * h);
       }
 #pragma unroll
       for (int g = 0; g < FM; ++g) {
-        xraw[g] = *(const u32x4*)&sm.x[buf][kc][((wave_m * FM + g) * 64 + lane) * 16];
-        xsc[g] = *(const uint16_t*)((const uint8_t*)&sm.xs[buf][kc][wave_m * WTM + g * 32 + r32] + 2 * h);
+        xraw[kc][g] = *(const u32x4*)&sm.x[buf][kc][((wave_m * FM + g) * 64 + lane) * 16];
+        xsr[kc][g] = *(const uint16_t*)((const uint8_t*)&sm.xs[buf][kc][wave_m * WTM + g * 32 + r32] + 2 * h);
+      }
+    };
+    half2_t wsc[FN], xsc[FM];  // f16 scales of the chunk being decoded
+    half8_t wf[2][FN], xf[2][FM];
+    auto decode_step = [&](int st, half8_t* wo, half8_t* xo) {
+      const int kc = st >> 2, j = st & 3;
+      if (j == 0) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) wsc[i] = scales_to_f16<kHw>(wsr[kc][i]);
+#pragma unroll
+        for (int g = 0; g < FM; ++g) xsc[g] = scales_to_f16<kHw>(xsr[kc][g]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half8_t wf[FN], xf[FM];
+      for (int i = 0; i < FN; ++i) wo[i] = decode8<kHw>(wraw[kc][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const half2_t s01 = scales_to_f16<kHw>(wsc[i]);
-          wf[i] = decode8<kHw>(wraw[i][j], j < 2 ? s01.xx : s01.yy);
-        }
+      for (int g = 0; g < FM; ++g) xo[g] = decode8<kHw>(xraw[kc][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
+    };
+    read_chunk(0);
+    decode_step(0, wf[0], xf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // One scheduling region per k-step: the MFMAs of step st, the decode of step st+1,
+    // the LDS reads of the next chunk (on the first step of a chunk) and, on the last
+    // step, the LDS stores of the prefetched stage. The group barriers ask for each MFMA
+    // to be followed by a few VALU (and memory) instructions, so the decode runs in the
+    // matrix core's shadow.
+    constexpr int kMfmaPerStep = FN * FM;
+    constexpr int kReadsPerChunk = 2 * (FN + FM);
 #pragma unroll
-        for (int g = 0; g < FM; ++g) {
-          const half2_t s01 = scales_to_f16<kHw>(xsc[g]);
-          xf[g] = decode8<kHw>(xraw[g][j], j < 2 ? s01.xx : s01.yy);
-        }
+    for (int st = 0; st < kSteps; ++st) {
+      const int cur = st & 1;
+      const bool reads = (st & 3) == 0 && (st >> 2) + 1 < KC;
+      if (reads) read_chunk((st >> 2) + 1);
+      if (st + 1 < kSteps) decode_step(st + 1, wf[cur ^ 1], xf[cur ^ 1]);
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+      for (int i = 0; i < FN; ++i)
 #pragma unroll
-          for (int g = 0; g < FM; ++g)
-            acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], xf[g], acc[i][g], 0, 0, 0);
+        for (int g = 0; g < FM; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
+      if (st + 1 == kSteps) {
+        store_stage<BM, KC, NT>(xr, sm.x[buf ^ 1], sm.xs[buf ^ 1], tid);
+        store_stage<BN, KC, NT>(wr, sm.w[buf ^ 1], sm.ws[buf ^ 1], tid);
       }
-    }
-    if (t + 1 < nk) {
-      store_stage<BM, KC>(xr, sm.x[buf ^ 1], sm.xs[buf ^ 1], tid);
-      store_stage<BN, KC>(wr, sm.w[buf ^ 1], sm.ws[buf ^ 1], tid);
+#pragma unroll
+      for (int q = 0; q < kMfmaPerStep; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (reads && q < kReadsPerChunk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (st + 1 == kSteps) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
 
-  // Epilogue: lane holds, for weight group i and activation group g, output row
-  // m = m_base + r32 and columns n_base + 8q + 4h + {0..3} in acc[i][g][4q..4q+3].
-  const bool n_vec = (p.N & 3) == 0;
-#pragma unroll
-  for (int g = 0; g < FM; ++g) {
-    const int64_t m = m0 + wave_m * WTM + g * 32 + r32;
-    if (m >= p.M) continue;
-    uint16_t* orow = p.out + m * p.N;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wave_n * WTN + i * 32 + 8 * q + 4 * h;
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
-        if (n_vec && n + 3 < p.N) {
-          *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
-        }
-      }
-    }
-  }
+  store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
+// ---- fast path: direct-to-LDS loads, three LDS stages, one pipeline across stages ----
+
 template <int BM, int BN, int KC>
+struct alignas(16) GemmSmem3 {
+  uint8_t x[3][KC][BM * 32];
+  uint8_t w[3][KC][BN * 32];
+  uint32_t xs[3][KC][BM];
+  uint32_t ws[3][KC][BN];
+};
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// One direct-to-LDS load per lane: 16 (or 4) bytes from src to lds_base + lane * 16 (4).
+__device__ __forceinline__ void dma_load16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma_load4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
+}
+
+// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0; other counters free).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Requires K % (64 * KC) == 0, 16-byte aligned packed operands and 4-byte aligned scales.
+//
+// Stage t (64*KC elements of K) lives in LDS buffer t % 3. Its direct-to-LDS loads are
+// issued during stage t-2, spread over the k-steps; at the end of every stage each wave
+// waits for its own loads and the workgroup synchronises, so stage t+1 is complete in
+// LDS while stage t computes. That lets the k-step pipeline run across stage
+// boundaries: the first chunk of stage t+1 is read and its first k-step decoded while
+// the last MFMAs of stage t run. Each lane of a load instruction fills one 16-byte slot
+// of the fragment layout (32 rows x 32 bytes per instruction), so the LDS image is
+// identical to the register-staged kernel's.
+template <int BM, int BN, int KC, int WM, int WN, bool kHw>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
+  constexpr int NW = WM * WN;
+  __shared__ GemmSmem3<BM, BN, KC> sm;
+  constexpr int WTM = BM / WM;
+  constexpr int WTN = BN / WN;
+  constexpr int FM = WTM / 32;
+  constexpr int FN = WTN / 32;
+  constexpr int kSteps = 4 * KC;
+  static_assert(KC % 2 == 0, "chunk parity must repeat every stage");
+  // Per stage: KC*BM/32 + KC*BN/32 packed loads and KC*BM/64 + KC*BN/64 scale loads.
+  constexpr int kPa = KC * BM / 32, kPw = KC * BN / 32, kSa = KC * BM / 64, kSw = KC * BN / 64;
+  static_assert(kPa % NW == 0 && kPw % NW == 0 && kSa % NW == 0 && kSw % NW == 0,
+                "loads must divide evenly among waves");
+  constexpr int kLoadsPerWave = (kPa + kPw + kSa + kSw) / NW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_n = wave % WN;
+  const int wave_m = wave / WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tile_m = blockIdx.x / tiles_n;
+  const int64_t tile_n = blockIdx.x % tiles_n;
+  const int64_t m0 = tile_m * BM;
+  const int64_t n0 = tile_n * BN;
+  const int64_t nk = p.K / (64 * KC);
+  const int64_t pitch = p.K >> 1;
+  const int64_t spitch = p.K >> 4;
+
+  // The j-th load of this wave for stage `stage` into LDS buffer `buf`. The load list is
+  // [packed x | packed w | scales x | scales w]; load number j*NW + wave.
+  auto issue = [&](int j, int64_t stage, int buf) {
+    int i = j * NW + wave;
+    if (j * NW < kPa) {  // packed activations: (chunk, 32-row group)
+      const int kc = i / (BM / 32), g = i % (BM / 32);
+      int64_t row = m0 + g * 32 + r32;
+      row = row < p.M ? row : p.M - 1;
+      dma_load16(p.a_packed + row * pitch + (stage * KC + kc) * 32 + h * 16, &sm.x[buf][kc][g * 1024]);
+    } else if (j * NW < kPa + kPw) {
+      i -= kPa;
+      const int kc = i / (BN / 32), g = i % (BN / 32);
+      int64_t row = n0 + g * 32 + r32;
+      row = row < p.N ? row : p.N - 1;
+      dma_load16(p.w_packed + row * pitch + (stage * KC + kc) * 32 + h * 16, &sm.w[buf][kc][g * 1024]);
+    } else if (j * NW < kPa + kPw + kSa) {  // scales: (chunk, 64-row group), 4 bytes per row
+      i -= kPa + kPw;
+      const int kc = i / (BM / 64), g = i % (BM / 64);
+      int64_t row = m0 + g * 64 + lane;
+      row = row < p.M ? row : p.M - 1;
+      dma_load4(p.a_scales + row * spitch + (stage * KC + kc) * 4, &sm.xs[buf][kc][g * 64]);
+    } else {
+      i -= kPa + kPw + kSa;
+      const int kc = i / (BN / 64), g = i % (BN / 64);
+      int64_t row = n0 + g * 64 + lane;
+      row = row < p.N ? row : p.N - 1;
+      dma_load4(p.w_scales + row * spitch + (stage * KC + kc) * 4, &sm.ws[buf][kc][g * 64]);
+    }
+  };
+
+  floatx16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  // fragments of two chunks (by chunk parity) and decoded operands of two k-steps
+  u32x4 wraw[2][FN], xraw[2][FM];
+  uint32_t wsr[2][FN], xsr[2][FM];
+  half2_t wsc[FN], xsc[FM];
+  half8_t wf[2][FN], xf[2][FM];
+  auto read_chunk = [&](int par, int buf, int kc) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      wraw[par][i] = *(const u32x4*)&sm.w[buf][kc][((wave_n * FN + i) * 64 + lane) * 16];
+      wsr[par][i] = *(const uint16_t*)((const uint8_t*)&sm.ws[buf][kc][wave_n * WTN + i * 32 + r32] + 2 * h);
+    }
+#pragma unroll
+    for (int g = 0; g < FM; ++g) {
+      xraw[par][g] = *(const u32x4*)&sm.x[buf][kc][((wave_m * FM + g) * 64 + lane) * 16];
+      xsr[par][g] = *(const uint16_t*)((const uint8_t*)&sm.xs[buf][kc][wave_m * WTM + g * 32 + r32] + 2 * h);
+    }
+  };
+  auto decode_step = [&](int par, int j, half8_t* wo, half8_t* xo) {
+    if (j == 0) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wsc[i] = scales_to_f16<kHw>(wsr[par][i]);
+#pragma unroll
+      for (int g = 0; g < FM; ++g) xsc[g] = scales_to_f16<kHw>(xsr[par][g]);
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wo[i] = decode8<kHw>(wraw[par][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
+#pragma unroll
+    for (int g = 0; g < FM; ++g) xo[g] = decode8<kHw>(xraw[par][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
+  };
+
+  // prologue: stages 0 and 1 into buffers 0 and 1
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : 0, 1);
+  wait_dma();
+  __syncthreads();
+  read_chunk(0, 0, 0);
+  decode_step(0, 0, wf[0], xf[0]);
+
+  constexpr int kMfmaPerStep = FN * FM;
+  constexpr int kReadsPerChunk = 2 * (FN + FM);
+  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
+  int buf = 0;
+  for (int64_t t = 0; t < nk; ++t) {
+    const int nbuf = buf == 2 ? 0 : buf + 1;     // stage t + 1
+    const int lbuf = nbuf == 2 ? 0 : nbuf + 1;   // stage t + 2
+    const int64_t lstage = t + 2 < nk ? t + 2 : nk - 1;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int cur = st & 1;
+      const int chunk = st >> 2, j = st & 3;
+#pragma unroll
+      for (int l = 0; l < kLoadsPerStep; ++l)
+        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf);
+      const bool reads = j == 0;
+      if (reads) {  // next chunk: the rest of this stage, then the first chunk of the next
+        if (chunk + 1 < KC) read_chunk((chunk + 1) & 1, buf, chunk + 1);
+        else read_chunk(0, nbuf, 0);
+      }
+      // decode of the next k-step (the first k-step of the next stage after the last)
+      if (st + 1 < kSteps) decode_step((st + 1) >> 2 & 1, (st + 1) & 3, wf[cur ^ 1], xf[cur ^ 1]);
+      else decode_step(0, 0, wf[cur ^ 1], xf[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < kMfmaPerStep; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (reads && q < kReadsPerChunk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (q < kLoadsPerStep) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_dma();
+    __syncthreads();
+    buf = nbuf;
+  }
+
+  store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
+}
+
+template <int BM, int BN, int KC, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool fast) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (fast)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, true, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, KC, WM, WN, true>), dim3((unsigned)tiles),
+                       dim3(64 * WM * WN), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, true, false>), dim3((unsigned)tiles), dim3(kThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, WM, WN, true, false>), dim3((unsigned)tiles),
+                       dim3(64 * WM * WN), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -347,9 +597,18 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
   (void)dev;
   const bool aligned = ((uintptr_t)p.a_packed % 16 == 0) && ((uintptr_t)p.w_packed % 16 == 0) &&
                        ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.w_scales % 4 == 0);
-  constexpr int BM = 256, BN = 256, KC = 2;
+#ifndef NVFP4_GEMM_KC
+#define NVFP4_GEMM_KC 2
+#endif
+#ifndef NVFP4_GEMM_WM
+#define NVFP4_GEMM_WM 2
+#endif
+#ifndef NVFP4_GEMM_WN
+#define NVFP4_GEMM_WN 2
+#endif
+  constexpr int BM = 256, BN = 256, KC = NVFP4_GEMM_KC;
   const bool fast = aligned && (p.K % (64 * KC) == 0);
-  return launch_tile<BM, BN, KC>(p, stream, fast);
+  return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
 }
 
 hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,
