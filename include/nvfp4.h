@@ -3,8 +3,7 @@
  *
  * C ABI. Every entry point takes plain pointers and sizes; no C++ types cross it and no
  * exception escapes it. Device buffers and streams belong to the caller; the library
- * allocates nothing, keeps no per-call state and never synchronises the host, except
- * where a function says otherwise (nvfp4_amax_host).
+ * allocates nothing, keeps no per-call state and never synchronises the host.
  *
  * The format (what a stored tensor is):
  *   - "BFL (fp8r / nvfp4)" (Hugging Face diffusers docs), scheme list, item nvfp4: a
@@ -60,7 +59,7 @@ extern "C" {
 typedef enum nvfp4_status {
   NVFP4_SUCCESS = 0,                  /* also returned for an empty problem (M == 0 or N == 0) */
   NVFP4_ERROR_INVALID_VALUE = 1,      /* null pointer; global scale not finite, <= 0, or
-                                         outside [2^-100, 2^100] */
+                                         outside [2^-90, 2^90] */
   NVFP4_ERROR_INVALID_SHAPE = 2,      /* negative size, K < 16, K % 16 != 0, size overflow */
   NVFP4_ERROR_MISALIGNED = 3,         /* x, packed, out or workspace not 16-byte aligned;
                                          scales not 4-byte aligned */
@@ -84,7 +83,8 @@ int nvfp4_last_hip_error(void);
  *   x_bf16       device, bf16 [M, K], 16-byte aligned, read only
  *   M, K         rows and columns; M >= 0, K >= 16, K % 16 == 0
  *   global_scale fp32 per-tensor scale (input_scale for activations, weight_scale_2 for
- *                weights), finite, in [2^-100, 2^100]
+ *                weights), finite, in [2^-90, 2^90] (any bf16 tensor with amax in
+ *                [2^-78, 2^101] calibrates into this range)
  *   packed       device, uint8 [M, K/2], 16-byte aligned, written
  *   scales       device, uint8 [M, K/16], 4-byte aligned, written
  * The output is bit-exact to the rounding rule in the header comment.

@@ -60,8 +60,11 @@ int current_device(nvfp4::LaunchInfo* info) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Global scales: finite, in [2^-100, 2^100] (keeps every per-block divisor normal).
-bool valid_scale(float g) { return isfinite(g) && g >= 0x1p-100f && g <= 0x1p100f; }
+// Global scales: finite, in [2^-90, 2^90]. In this range every per-block divisor
+// d = s * gs (s >= 2^-9) and 6 * gs stay far enough from the fp32 subnormal range that
+// the quantizer's reciprocal-plus-correction divisions are exact (their residuals never
+// underflow).
+bool valid_scale(float g) { return isfinite(g) && g >= 0x1p-90f && g <= 0x1p90f; }
 
 // Shape: rows >= 0, K >= 16, K % 16 == 0, rows * K without overflow (bytes < 2^62).
 int check_shape(int64_t rows, int64_t K) {

@@ -14,8 +14,9 @@
 
 namespace nvfp4 {
 
-// Native 16-byte vector (usable with the nontemporal load/store builtins).
+// Native 16- and 8-byte vectors (usable with the nontemporal load/store builtins).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 NVFP4_HD float u2f(uint32_t u) {
   float f;
@@ -69,14 +70,33 @@ NVFP4_HD uint32_t e2m1_magnitude_encode(float y) {
 // binary32 d, given r = RN(1/d) (Markstein's correction):
 //   y0 = RN(x r),  e = RN(y0 d - x) (exact, fma),  y = RN(y0 - e r).
 // An exhaustive check over every pair of significands (bf16 x, binary32 d) shows
-// y == RN(x/d). Writing the residual as y0 d - x (not x - y0 d) keeps the sign of a
-// zero x: for x = -0, e = +0 and y = -0 - (+0)r = -0. y0 is clamped to [-8, 8] first;
-// any |x/d| >= 6 saturates the E2M1 code, so the clamp only keeps a huge quotient
-// from turning into inf - inf = NaN. With r == 0 (for d == 0) the result is a zero
-// carrying the sign of x.
+// y == RN(x/d), and it stays exact while the residual e cannot underflow, which holds
+// for every d = s * gs with s >= 2^-9 and gs >= 2^-90 in the quotient range that decides
+// a code. Writing the residual as y0 d - x (not x - y0 d) keeps the sign of a zero x:
+// for x = -0, e = +0 and y = -0 - (+0)r = -0. With r == 0 (for d == 0) the result is a
+// zero carrying the sign of x.
+//
+// This form needs |x r| finite; it is used for every block whose scale did not saturate
+// (there |x| / d <= amax / d < 9).
+NVFP4_HD float div_by_scale_unclamped(float x, float d, float r) {
+  const float y0 = x * r;
+  const float e = __builtin_fmaf(y0, d, -x);
+  return __builtin_fmaf(-e, r, y0);
+}
+
+NVFP4_HD float clamp8(float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_fmed3f(v, -8.0f, 8.0f);
+#else
+  return v < -8.0f ? -8.0f : (v > 8.0f ? 8.0f : v);
+#endif
+}
+
+// Same quotient for any finite x: y0 is clamped to [-8, 8] first. Any |x/d| >= 6
+// saturates the E2M1 code, so the clamp only keeps a huge quotient from turning into
+// inf - inf = NaN; below 8 it changes nothing.
 NVFP4_HD float div_by_scale(float x, float d, float r) {
-  float y0 = x * r;
-  y0 = y0 < -8.0f ? -8.0f : (y0 > 8.0f ? 8.0f : y0);
+  const float y0 = clamp8(x * r);
   const float e = __builtin_fmaf(y0, d, -x);
   return __builtin_fmaf(-e, r, y0);
 }
@@ -89,11 +109,16 @@ struct BlockScale {
   float r;
 };
 
-// Scale of one block from its amax under global scale gs, with den = RN(6 * gs):
-// s_raw = RN(amax / den), code = E4M3(s_raw), d = RN(decode(code) * gs).
-NVFP4_HD BlockScale block_scale(float amax, float den, float gs) {
+// Scale of one block from its amax under global scale gs, with den = RN(6 * gs) and
+// rden = RN(1 / den): s_raw = RN(amax / den) (the same reciprocal-plus-correction
+// quotient, amax being a bf16 value; the first product is clamped to [0, 1024] so an
+// overflow ends in saturation, never NaN), code = E4M3(s_raw), d = RN(decode(code) * gs).
+NVFP4_HD BlockScale block_scale(float amax, float den, float rden, float gs) {
   BlockScale b;
-  float s_raw = amax / den;
+  float q0 = amax * rden;
+  q0 = q0 < 1024.0f ? q0 : 1024.0f;
+  const float e = __builtin_fmaf(q0, den, -amax);
+  const float s_raw = __builtin_fmaf(-e, rden, q0);
   b.code = e4m3_encode_sat(s_raw);
   b.d = e4m3_decode(b.code) * gs;
   b.r = b.d == 0.0f ? 0.0f : 1.0f / b.d;

@@ -47,7 +47,6 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // f16 values {s(c0), s(c1)} of the two E4M3 scale codes in the low 16 bits of v (c0 in
 // bits 0..7). Every E4M3 value, subnormals included, is a normal f16, so the

@@ -36,34 +36,34 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
 }
 
 // Encode 16 values (in f) of one block into 8 packed bytes, given the block's scale.
-template <bool kHwEncode>
-__device__ __forceinline__ uint2 encode_block(const float* f, const BlockScale& bs) {
+// kClamp selects the quotient form that tolerates an overflowing |x| * r (only needed
+// for blocks whose scale saturated).
+template <bool kClamp>
+__device__ __forceinline__ u32x2 encode_block(const float* f, const BlockScale& bs) {
   uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float y0 = div_by_scale(f[2 * j], bs.d, bs.r);
-    const float y1 = div_by_scale(f[2 * j + 1], bs.d, bs.r);
-    if constexpr (kHwEncode) {
-      // byte j % 4 of word j / 4 <- {code(y1) << 4 | code(y0)}
-      switch (j & 3) {
-        case 0: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 0); break;
-        case 1: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 1); break;
-        case 2: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 2); break;
-        default: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 3); break;
-      }
-    } else {
-      const uint32_t c = e2m1_encode_sw(f[2 * j], y0) | (e2m1_encode_sw(f[2 * j + 1], y1) << 4);
-      out[j >> 2] |= c << (8 * (j & 3));
+    const float y0 = kClamp ? div_by_scale(f[2 * j], bs.d, bs.r)
+                            : div_by_scale_unclamped(f[2 * j], bs.d, bs.r);
+    const float y1 = kClamp ? div_by_scale(f[2 * j + 1], bs.d, bs.r)
+                            : div_by_scale_unclamped(f[2 * j + 1], bs.d, bs.r);
+    // byte j % 4 of word j / 4 <- {code(y1) << 4 | code(y0)}
+    switch (j & 3) {
+      case 0: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 0); break;
+      case 1: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 1); break;
+      case 2: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 2); break;
+      default: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 3); break;
     }
   }
-  return make_uint2(out[0], out[1]);
+  return u32x2{out[0], out[1]};
 }
 
-template <int UNROLL, bool kHwEncode>
+template <int UNROLL>
 __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__ x,
-                                                       uint2* __restrict__ packed,
+                                                       u32x2* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
-                                                       int64_t nblocks, float gs, float den) {
+                                                       int64_t nblocks, float gs, float den,
+                                                       float rden) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * UNROLL;
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nblocks;
        base += stride) {
@@ -86,10 +86,16 @@ __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-        const BlockScale bs = block_scale(amax, den, gs);
-        const uint2 p = encode_block<kHwEncode>(f, bs);
-        __builtin_nontemporal_store(p.x, &packed[b].x);
-        __builtin_nontemporal_store(p.y, &packed[b].y);
+        const BlockScale bs = block_scale(amax, den, rden, gs);
+        // Saturated scales are rare (the tensor's largest block under a self-calibrated
+        // scale, or a static scale that is too small); the whole wave takes the clamped
+        // quotient if any of its lanes has one.
+        u32x2 p;
+        if (__any(bs.code == kE4M3MaxCode))
+          p = encode_block<true>(f, bs);
+        else
+          p = encode_block<false>(f, bs);
+        __builtin_nontemporal_store(p, &packed[b]);
         scales[b] = (uint8_t)bs.code;
       }
     }
@@ -102,16 +108,23 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
                            void* scales, hipStream_t stream, const LaunchInfo& dev) {
   const int64_t nblocks = M * (K / 16);
   if (nblocks == 0) return hipSuccess;
+#ifndef NVFP4_QUANT_UNROLL
+#define NVFP4_QUANT_UNROLL 1
+#endif
+#ifndef NVFP4_QUANT_WG_PER_CU
+#define NVFP4_QUANT_WG_PER_CU 32
+#endif
   constexpr int kThreads = 256;
-  constexpr int kUnroll = 4;
-  const float den = 6.0f * gs;
+  constexpr int kUnroll = NVFP4_QUANT_UNROLL;
+  const float den = 6.0f * gs;   // IEEE binary32 on the host
+  const float rden = 1.0f / den;
   int64_t want = (nblocks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   // Enough workgroups to fill every CU several times over; the grid-stride loop covers
   // the rest.
-  const int64_t cap = (int64_t)dev.num_cus * 8;
+  const int64_t cap = (int64_t)dev.num_cus * NVFP4_QUANT_WG_PER_CU;
   const int grid = (int)(want < cap ? want : cap);
-  hipLaunchKernelGGL((quantize_kernel<kUnroll, true>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const u32x4*)x, (uint2*)packed, (uint8_t*)scales, nblocks, gs, den);
+  hipLaunchKernelGGL((quantize_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                     (const u32x4*)x, (u32x2*)packed, (uint8_t*)scales, nblocks, gs, den, rden);
   return hipGetLastError();
 }
 
@@ -163,8 +176,9 @@ __global__ void selftest_division_kernel(unsigned long long* __restrict__ count,
     const float x = xm < 256 ? u2f(((127u + (xm >> 7)) << 23) | ((xm & 127u) << 16))
                              : (xm & 1u ? -0.0f : 0.0f);
     const float y = xm < 258 ? div_by_scale(x, d, r) : div_by_scale(x, 0.0f, 0.0f);
+    const float yu = xm < 258 ? div_by_scale_unclamped(x, d, r) : div_by_scale_unclamped(x, 0.0f, 0.0f);
     const float q = xm < 258 ? x / d : x;
-    if (f2u(y) != f2u(q)) {
+    if (f2u(y) != f2u(q) || f2u(yu) != f2u(q)) {
       const unsigned long long k = atomicAdd(count, 1ull);
       if (k < 8) {
         first[2 * k] = f2u(x);
@@ -175,11 +189,11 @@ __global__ void selftest_division_kernel(unsigned long long* __restrict__ count,
 }
 
 __global__ void selftest_scale_kernel(const float* __restrict__ amax, float gs, float den,
-                                      uint8_t* __restrict__ code, float* __restrict__ d_out,
-                                      int64_t n) {
+                                      float rden, uint8_t* __restrict__ code,
+                                      float* __restrict__ d_out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const BlockScale b = block_scale(amax[i], den, gs);
+  const BlockScale b = block_scale(amax[i], den, rden, gs);
   code[i] = (uint8_t)b.code;
   d_out[i] = b.d;
 }
@@ -211,8 +225,9 @@ hipError_t launch_selftest_division(unsigned long long* count, uint32_t* first,
 hipError_t launch_selftest_scale(const float* amax, float gs, uint8_t* code, float* d, int64_t n,
                                  hipStream_t stream) {
   if (n == 0) return hipSuccess;
+  const float den = 6.0f * gs;
   hipLaunchKernelGGL(selftest_scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     stream, amax, gs, 6.0f * gs, code, d, n);
+                     stream, amax, gs, den, 1.0f / den, code, d, n);
   return hipGetLastError();
 }
 

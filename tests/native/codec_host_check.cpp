@@ -46,8 +46,9 @@ int main(int argc, char** argv) {
       for (uint32_t xm = 0; xm < 256; ++xm) {
         const float x = u2f(((127u + (xm >> 7)) << 23) | ((xm & 127u) << 16));
         const float y = div_by_scale(x, d, r);
+        const float yu = div_by_scale_unclamped(x, d, r);
         const float q = x / d;
-        if (f2u(y) != f2u(q)) {
+        if (f2u(y) != f2u(q) || f2u(yu) != f2u(q)) {
           if (bad < 5) printf("x=%a d=%a y=%a q=%a\n", x, d, y, q);
           ++bad;
         }
@@ -71,13 +72,59 @@ int main(int argc, char** argv) {
     printf("mismatches %llu\n", bad);
     return 0;
   }
+  if (!strcmp(argv[1], "extremes")) {
+    // Random significand pairs at the extreme exponents the validated global-scale range
+    // allows: d = s * gs in [2^-99, 2^99] (s in [2^-9, 448], gs in [2^-90, 2^90]) with
+    // quotients x / d in [2^-3, 2^4) (the range that decides a code), for both quotient
+    // forms; and the block-scale quotient amax / den with den = 6 * gs at the range ends.
+    unsigned long long bad = 0, n = 0;
+    uint64_t st = 0x9E3779B97F4A7C15ull;
+    auto rnd = [&]() { st ^= st << 13; st ^= st >> 7; st ^= st << 17; return (uint32_t)(st >> 11); };
+    const int dexp[] = {-99, -98, -97, -90, 88, 95, 98};
+    for (int de : dexp) {
+      for (int it = 0; it < 4000000; ++it) {
+        const float d = u2f(((uint32_t)(de + 127) << 23) | (rnd() & 0x7FFFFFu));
+        const int qe = (int)(rnd() % 7) - 3;
+        const float x = u2f(((uint32_t)(de + qe + 127) << 23) | ((rnd() & 0x7Fu) << 16));
+        const float r = 1.0f / d;
+        const float q = x / d;
+        ++n;
+        // unclamped: exact everywhere; clamped: exact below 8, saturating (>= 6) above
+        const float yc = div_by_scale(x, d, r);
+        const bool ok_c = q < 8.0f ? f2u(yc) == f2u(q) : yc >= 6.0f;
+        if (!ok_c || f2u(div_by_scale_unclamped(x, d, r)) != f2u(q)) {
+          if (bad < 5) printf("x=%a d=%a\n", x, d);
+          ++bad;
+        }
+      }
+    }
+    const float gss[] = {0x1p-90f, 0x1.8p-90f, 0x1p90f, 0x1.fffffep89f};
+    for (float gs : gss) {
+      const float den = 6.0f * gs, rden = 1.0f / den;
+      for (int it = 0; it < 4000000; ++it) {
+        const int qe = (int)(rnd() % 21) - 11;  // s_raw in [2^-11, 2^10)
+        const int ae = (int)((f2u(den) >> 23) & 0xFF) - 127 + qe;
+        const float amax = u2f(((uint32_t)(ae + 127) << 23) | ((rnd() & 0x7Fu) << 16));
+        const BlockScale b = block_scale(amax, den, rden, gs);
+        const uint32_t want = e4m3_encode_sat(amax / den);
+        ++n;
+        if (b.code != want) {
+          if (bad < 5) printf("amax=%a den=%a\n", amax, den);
+          ++bad;
+        }
+      }
+    }
+    printf("checked %llu mismatches %llu\n", n, bad);
+    return 0;
+  }
   if (!strcmp(argv[1], "scale") && argc == 5) {
     const std::vector<float> a = read_f32(argv[2]);
     const float gs = u2f((uint32_t)strtoul(argv[3], nullptr, 16));
     const float den = 6.0f * gs;
+    const float rden = 1.0f / den;
     std::vector<uint8_t> out(a.size() * 5);
     for (size_t i = 0; i < a.size(); ++i) {
-      const BlockScale b = block_scale(a[i], den, gs);
+      const BlockScale b = block_scale(a[i], den, rden, gs);
       out[5 * i] = (uint8_t)b.code;
       memcpy(&out[5 * i + 1], &b.d, 4);
     }

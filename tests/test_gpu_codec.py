@@ -68,7 +68,7 @@ def test_division_exhaustive(lib):
     assert int(to_host(cnt)[0]) == 0, [hex(v & 0xFFFFFFFF) for v in to_host(first)]
 
 
-@pytest.mark.parametrize("gs", [1.0, 2.0**-6, 1.0 / 3.0, 3.7e-4, 2.0**-100, 2.0**100])
+@pytest.mark.parametrize("gs", [1.0, 2.0**-6, 1.0 / 3.0, 3.7e-4, 2.0**-90, 2.0**90])
 def test_block_scale_matches_oracle(lib, gs):
     say("block scale", gs)
     gs = np.float32(gs)

@@ -84,7 +84,7 @@ def test_adversarial_and_ragged(M, K):
         # static scales that are too small (E4M3 and E2M1 saturation) and too large
         # (E4M3 subnormal scales, scale underflow to 0)
         for f in (2.0**-12, 0.37, 2.0**9, 2.0**40):
-            g2 = np.float32(np.clip(np.float32(gs) * np.float32(f), 2.0**-100, 2.0**100))
+            g2 = np.float32(np.clip(np.float32(gs) * np.float32(f), 2.0**-90, 2.0**90))
             _check_quantize(x, g2, f"{label} {M}x{K} x{f}")
 
 
