@@ -107,10 +107,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 // group g, output row m = m_base + 32g + (lane % 32) and columns
 // n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is scaled by
 // alpha in fp32, rounded to nearest even bf16 and stored (8 bytes per lane when the row
-// pitch allows).
+// pitch allows). Only column quads q in [q0, q1) are stored.
 template <int FM, int FN>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
-                                           int64_t m_base, int64_t n_base, int lane) {
+                                           int64_t m_base, int64_t n_base, int lane, int q0 = 0,
+                                           int q1 = 4) {
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 3) == 0;
@@ -123,6 +124,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (q < q0 || q >= q1) continue;
         const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
         uint32_t b[4];
 #pragma unroll
@@ -556,6 +558,273 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
   store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
+// ---- fit-tile path: 288 x 192 tiles ------------------------------------------------------
+//
+// The 256x256 tile leaves part of the chip idle at the token count of a 1024x1024 FLUX
+// image: 4608 = 18 x 256 rows against 256 compute units gives 216 tiles for a 3072-wide
+// output. 4608 = 16 x 288 and every FLUX width (3072, 9216, 12288) is a multiple of 192,
+// so a 288 x 192 tile splits these products into whole multiples of 256 tiles.
+//
+// The tile is 9 x 6 blocks of 32 x 32 outputs (the 32x32x16 MFMA), which 4 waves cannot
+// share evenly. Wave (m, n) owns weight groups 3n..3n+2 and activation groups 0..3 (m = 0)
+// or 5..8 (m = 1) over the whole K range, plus the middle activation group 4 over one of
+// the two 64-element chunks of every 128-element stage. Each wave runs "its" chunk first
+// (wave m = 0 physical chunk 0, m = 1 chunk 1) and takes group 4 there, so all waves run
+// one program: 13.5 blocks of work per wave and k-step on average. At the end the two
+// partial sums of group 4 meet in LDS.
+//
+// LDS image of a stage (same fragment order as the 256x256 kernel): per chunk and 32-row
+// group, 64 slots of 16 bytes in MFMA lane order; scale bytes as 32-bit words [row][chunk].
+template <int BM, int BN>
+struct alignas(16) GemmSmemFit {
+  uint8_t x[3][2][BM * 32];  // activations: [stage buffer][chunk][fragment order]
+  uint8_t w[3][2][BN * 32];  // weights
+  uint32_t xs[3][BM * 2];    // scale words: [row][chunk], 4 scale bytes per word
+  uint32_t ws[3][BN * 2];
+};
+
+// Wait until at most n of this wave's vector memory operations are outstanding (n < 16;
+// expcnt and lgkmcnt left free). Loads complete in issue order.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+}
+
+// Raw buffer resource over n bytes at p (gfx9-family descriptor word 3: 32-bit data
+// format, no swizzle); loads at offsets >= n return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// Direct-to-LDS buffer loads: each lane reads 16 (4) bytes at voff + soff and writes
+// them to lds_base + lane * 16 (4).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                 uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
+// (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
+//
+// Stage t lives in LDS buffer t % 3; its loads are issued during stage t-2, spread over
+// the first k-steps. At the end of stage t each wave waits until its loads for stage t+1
+// have landed (those for t+2 stay in flight) and the workgroup meets at a barrier; by then
+// every wave has consumed its LDS reads of stage t, whose buffer the loads issued during
+// stage t+1 overwrite. The first chunk of stage t+1 is read and its first k-step decoded
+// during the second chunk of stage t.
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
+  constexpr int NW = 4;
+  constexpr int GX = BM / 32, GW = BN / 32;
+  static_assert(GX * 32 == BM && GW * 32 == BN, "tiles are whole 32-row groups");
+  static_assert(GX % 2 == 1 && GW % 2 == 0, "odd activation groups, even weight groups");
+  constexpr int FM = GX / 2;  // whole activation groups per wave
+  constexpr int FN = GW / 2;  // weight groups per wave
+  constexpr int GS = FM;      // the shared middle activation group
+  constexpr int kSteps = 8;   // 16-element k-steps per stage (two chunks of 4)
+  __shared__ GemmSmemFit<BM, BN> sm;
+
+  // Loads per stage: one 16-byte load per lane fills a (chunk, 32-row group) piece of 1 KB;
+  // one 4-byte load per lane fills the scale words of 32 rows. Four lists (packed x, packed
+  // w, scales x, scales w); wave w takes entries j * NW + w of each. Every wave issues the
+  // same number of loads, so the vmcnt wait counts the same; entries past a list repeat
+  // its last one, which writes the same bytes to the same place.
+  constexpr int kPa = 2 * GX, kPw = 2 * GW, kSa = GX, kSw = GW;
+  constexpr int kPaW = (kPa + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW;
+  constexpr int kSaW = (kSa + NW - 1) / NW, kSwW = (kSw + NW - 1) / NW;
+  constexpr int kLoadsPerWave = kPaW + kPwW + kSaW + kSwW;
+  static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
+  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_n = wave & 1;
+  const int wave_m = wave >> 1;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tile_m = (int)blockIdx.x / tiles_n;
+  const int tile_n = (int)blockIdx.x % tiles_n;
+  const int m0 = tile_m * BM;
+  const int n0 = tile_n * BN;
+  const int nk = (int)(p.K / 128);
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
+
+  // Buffer resources: the range check returns zeros for rows past M (or N), so a ragged
+  // last tile needs no clamping.
+  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
+  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const uint32_t voff_p = r32 * pitch + h * 16;                   // 32 rows x 32 bytes
+  const uint32_t voff_s = (lane >> 1) * spitch + (lane & 1) * 4;  // 32 rows x 8 bytes
+
+  auto issue = [&](int j, int stage, int buf) {
+    if (j < kPaW) {
+      const int i = min(j * NW + wave, kPa - 1);
+      const int c = i / GX, g = i % GX;
+      buffer_load_lds16(rxp, &sm.x[buf][c][g * 1024], voff_p,
+                        (uint32_t)(m0 + g * 32) * pitch + (uint32_t)stage * 64 + c * 32);
+    } else if (j < kPaW + kPwW) {
+      const int i = min((j - kPaW) * NW + wave, kPw - 1);
+      const int c = i / GW, g = i % GW;
+      buffer_load_lds16(rwp, &sm.w[buf][c][g * 1024], voff_p,
+                        (uint32_t)(n0 + g * 32) * pitch + (uint32_t)stage * 64 + c * 32);
+    } else if (j < kPaW + kPwW + kSaW) {
+      const int g = min((j - kPaW - kPwW) * NW + wave, kSa - 1);
+      buffer_load_lds4(rxs, &sm.xs[buf][g * 64], voff_s,
+                       (uint32_t)(m0 + g * 32) * spitch + (uint32_t)stage * 8);
+    } else {
+      const int g = min((j - kPaW - kPwW - kSaW) * NW + wave, kSw - 1);
+      buffer_load_lds4(rws, &sm.ws[buf][g * 64], voff_s,
+                       (uint32_t)(n0 + g * 32) * spitch + (uint32_t)stage * 8);
+    }
+  };
+
+  floatx16 acc[FN][FM], accs[FN];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accs[i][v] = 0.0f;
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
+  }
+
+  // Fragments of two chunks (by the wave's own chunk order: 0 = first, 1 = second) and
+  // decoded operands of two k-steps.
+  const int xg0 = wave_m ? GS + 1 : 0;  // first whole activation group of this wave
+  const int wfrag = (wave_n * FN * 64 + lane) * 16;
+  const int xfrag = (xg0 * 64 + lane) * 16;
+  const int sfrag = (GS * 64 + lane) * 16;
+  const int wsw = (wave_n * FN * 32 + r32) * 8 + 2 * h;  // scale byte offsets (chunk 0)
+  const int xsw = (xg0 * 32 + r32) * 8 + 2 * h;
+  const int ssw = (GS * 32 + r32) * 8 + 2 * h;
+  u32x4 wraw[2][FN], xraw[2][FM], sraw;
+  uint32_t wsr[2][FN], xsr[2][FM], ssr;
+  half2_t wsc[FN], xsc[FM], ssc;
+  half8_t wf[2][FN], xf[2][FM], sf[2];
+  // read the fragments of chunk `c` (physical) of stage buffer `buf` as the wave's chunk
+  // `par`; the shared group only in its first chunk
+  auto read_chunk = [&](int par, int buf, int c) {
+    const uint8_t* wb = &sm.w[buf][c][wfrag];
+    const uint8_t* xb = &sm.x[buf][c][xfrag];
+    const uint8_t* wsb = (const uint8_t*)sm.ws[buf] + wsw + c * 4;
+    const uint8_t* xsb = (const uint8_t*)sm.xs[buf] + xsw + c * 4;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      wraw[par][i] = *(const u32x4*)(wb + i * 1024);
+      wsr[par][i] = *(const uint16_t*)(wsb + i * 256);
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      xraw[par][f] = *(const u32x4*)(xb + f * 1024);
+      xsr[par][f] = *(const uint16_t*)(xsb + f * 256);
+    }
+    if (par == 0) {
+      sraw = *(const u32x4*)&sm.x[buf][c][sfrag];
+      ssr = *(const uint16_t*)((const uint8_t*)sm.xs[buf] + ssw + c * 4);
+    }
+  };
+  auto decode_step = [&](int par, int j, int slot) {
+    if (j == 0) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wsc[i] = scales_to_f16<true>(wsr[par][i]);
+#pragma unroll
+      for (int f = 0; f < FM; ++f) xsc[f] = scales_to_f16<true>(xsr[par][f]);
+      if (par == 0) ssc = scales_to_f16<true>(ssr);
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wf[slot][i] = decode8<true>(wraw[par][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
+#pragma unroll
+    for (int f = 0; f < FM; ++f) xf[slot][f] = decode8<true>(xraw[par][f][j], j < 2 ? xsc[f].xx : xsc[f].yy);
+    if (par == 0) sf[slot] = decode8<true>(sraw[j], j < 2 ? ssc.xx : ssc.yy);
+  };
+
+  // prologue: stages 0 and 1 into buffers 0 and 1
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : 0, 1);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  read_chunk(0, 0, wave_m);
+  decode_step(0, 0, 0);
+
+  int buf = 0;
+  for (int t = 0; t < nk; ++t) {
+    const int nbuf = buf == 2 ? 0 : buf + 1;    // stage t + 1
+    const int lbuf = nbuf == 2 ? 0 : nbuf + 1;  // stage t + 2
+    const int lstage = t + 2 < nk ? t + 2 : nk - 1;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int cur = st & 1;
+      const int par = st >> 2, j = st & 3;
+#pragma unroll
+      for (int l = 0; l < kLoadsPerStep; ++l)
+        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf);
+      if (j == 0) {  // the wave's second chunk of this stage, or its first of the next
+        if (par == 0) read_chunk(1, buf, wave_m ^ 1);
+        else read_chunk(0, nbuf, wave_m);
+      }
+      decode_step(((st + 1) >> 2) & 1, (st + 1) & 3, cur ^ 1);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][i], xf[cur][f], acc[i][f], 0, 0, 0);
+        if (par == 0) accs[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][i], sf[cur], accs[i], 0, 0, 0);
+      }
+      constexpr int kReads = 2 * (FN + FM) + 2;
+      const int nmfma = FN * FM + (par == 0 ? FN : 0);
+#pragma unroll
+      for (int q = 0; q < FN * (FM + 1); ++q) {
+        if (q < nmfma) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (j == 0 && q < kReads / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+          if (q < kLoadsPerStep && st * kLoadsPerStep + q < kLoadsPerWave)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
+          __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<kLoadsPerWave>();
+    __builtin_amdgcn_s_barrier();
+    buf = nbuf;
+  }
+
+  // The two partial sums of the shared group: drain the last (unused) loads, then swap
+  // them through LDS (the stage buffers are free now).
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  float* xch = (float*)&sm.x[0][0][0];
+  static_assert(NW * FN * 16 * 64 * sizeof(float) <= sizeof(sm.x), "exchange fits");
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) xch[((wave * FN + i) * 16 + v) * 64 + lane] = accs[i][v];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accs[i][v] += xch[(((wave ^ 2) * FN + i) * 16 + v) * 64 + lane];
+
+  const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
+  store_tile<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane);
+  // group GS: wave m = 0 stores column quads 0-1 of every block, m = 1 quads 2-3
+  store_tile<1, FN>(*(const floatx16(*)[FN][1])&accs, p, (int64_t)m0 + GS * 32, n_base, lane,
+                    wave_m * 2, wave_m * 2 + 2);
+}
+
 template <int BM, int BN, int KC, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool fast) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -593,7 +862,6 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  (void)dev;
   const bool aligned = ((uintptr_t)p.a_packed % 16 == 0) && ((uintptr_t)p.w_packed % 16 == 0) &&
                        ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.w_scales % 4 == 0);
 #ifndef NVFP4_GEMM_KC
@@ -606,7 +874,35 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
 #define NVFP4_GEMM_WN 2
 #endif
   constexpr int BM = 256, BN = 256, KC = NVFP4_GEMM_KC;
+#ifndef NVFP4_FIT_BM
+#define NVFP4_FIT_BM 288
+#define NVFP4_FIT_BN 192
+#endif
+  constexpr int FBM = NVFP4_FIT_BM, FBN = NVFP4_FIT_BN;
   const bool fast = aligned && (p.K % (64 * KC) == 0);
+  if (aligned && p.K % 128 == 0) {
+    // Tiles run one per compute unit at a time: compare whole passes over the chip,
+    // each costing a tile's area, and take the fit tile unless it loses.
+    const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
+    const int64_t t256 = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int64_t tfit = ((p.M + FBM - 1) / FBM) * ((p.N + FBN - 1) / FBN);
+    const int64_t c256 = (t256 + cus - 1) / cus * (int64_t)(BM * BN);
+    const int64_t cfit = (tfit + cus - 1) / cus * (int64_t)(FBM * FBN);
+    // the fit kernel addresses operands with 32-bit buffer offsets
+    const bool fits32 = (p.M + FBM) * (p.K / 2) < ((int64_t)1 << 31) &&
+                        (p.N + FBN) * (p.K / 2) < ((int64_t)1 << 31);
+#ifdef NVFP4_GEMM_FORCE_TILE
+    const bool use_fit = NVFP4_GEMM_FORCE_TILE == 1 && fits32;
+#else
+    const bool use_fit = cfit <= c256 && fits32;
+#endif
+    if (use_fit) {
+      if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream,
+                         p);
+      return hipGetLastError();
+    }
+  }
   return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
 }
 
