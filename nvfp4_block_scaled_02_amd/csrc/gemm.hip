@@ -141,6 +141,53 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
   }
 }
 
+// The same stores through LDS: one 32-row group of the wave's blocks at a time is
+// written, rounded, into the wave's own LDS area `blk` (32 x FN*32 bf16, row-major) and
+// read back as 16-byte row pieces, so each store instruction writes whole row segments
+// (FN*64 bytes per row) instead of 16-byte pieces of 32 rows. `blk` must not be used by
+// other waves; LDS order within the wave makes the round trip safe without a barrier.
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
+                                               int64_t m_base, int64_t n_base, int lane,
+                                               uint16_t* blk) {
+  constexpr int W = FN * 32;          // columns of the wave's blocks
+  constexpr int kPieces = 32 * W / 8;  // 16-byte pieces per 32-row group
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
+#pragma unroll
+  for (int g = 0; g < FM; ++g) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+        *(u32x2*)&blk[r32 * W + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+      }
+    const int64_t m_row = m_base + g * 32;
+#pragma unroll
+    for (int it = 0; it < (kPieces + 63) / 64; ++it) {
+      const int c = it * 64 + lane;
+      if (c < kPieces) {
+        const int r = c / (W / 8), col = (c % (W / 8)) * 8;
+        const int64_t m = m_row + r, n = n_base + col;
+        if (m < p.M) {
+          const u32x4 v = *(const u32x4*)&blk[r * W + col];
+          if (n_vec && n + 7 < p.N) {
+            *(u32x4*)&p.out[m * p.N + n] = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < p.N) p.out[m * p.N + n + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int KC>
 struct alignas(16) GemmSmem {
   uint8_t x[2][KC][BM * 32];   // activations, fragment order
@@ -555,7 +602,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
     buf = nbuf;
   }
 
-  store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
+  // every load has landed and every wave is past its last LDS read (the loop ends with
+  // a full wait and a barrier), so the stage buffers can stage the stores
+  static_assert(NW * 32 * FN * 32 * 2 <= sizeof(sm.x), "store staging fits");
+  store_tile_lds<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
+                         (uint16_t*)&sm.x[0][0][0] + wave * 32 * FN * 32);
 }
 
 // ---- fit-tile path: 288 x 192 tiles ------------------------------------------------------
@@ -608,6 +659,30 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 4, (int)voff, (int)soff, 0, 0);
 }
 
+#ifndef NVFP4_GEMM_XCD_GROUP
+#define NVFP4_GEMM_XCD_GROUP 4
+#endif
+// Workgroup -> tile. Consecutive workgroups go to the 8 XCDs in turn and each XCD has its
+// own L2, so workgroup b takes tile (b % 8) * (T / 8) + b / 8 of an order in which each
+// XCD's share is contiguous; that order walks groups of G tile rows column by column, so
+// an XCD's tiles share few activation and weight rows. (T % 8 != 0: plain order.)
+__device__ __forceinline__ void tile_order(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, G = NVFP4_GEMM_XCD_GROUP;
+  const int T = tiles_m * tiles_n;
+  if (G <= 0 || T % kXcd != 0) {
+    tm = b / tiles_n;
+    tn = b % tiles_n;
+    return;
+  }
+  const int q = (b % kXcd) * (T / kXcd) + b / kXcd;
+  const int per_group = G * tiles_n;
+  const int gm0 = (q / per_group) * G;
+  const int rows = min(tiles_m - gm0, G);
+  const int r = q % per_group;
+  tm = gm0 + r % rows;
+  tn = r / rows;
+}
+
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
 // (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
 //
@@ -649,8 +724,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   const int r32 = lane & 31;
 
   const int tiles_n = (int)((p.N + BN - 1) / BN);
-  const int tile_m = (int)blockIdx.x / tiles_n;
-  const int tile_n = (int)blockIdx.x % tiles_n;
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  int tile_m, tile_n;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
   const int nk = (int)(p.K / 128);
@@ -819,7 +895,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     for (int v = 0; v < 16; ++v) accs[i][v] += xch[(((wave ^ 2) * FN + i) * 16 + v) * 64 + lane];
 
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
-  store_tile<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane);
+  static_assert(NW * 32 * FN * 32 * 2 <= sizeof(sm.w), "store staging fits");
+  store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane,
+                         (uint16_t*)&sm.w[0][0][0] + wave * 32 * FN * 32);
   // group GS: wave m = 0 stores column quads 0-1 of every block, m = 1 quads 2-3
   store_tile<1, FN>(*(const floatx16(*)[FN][1])&accs, p, (int64_t)m0 + GS * 32, n_base, lane,
                     wave_m * 2, wave_m * 2 + 2);
