@@ -903,6 +903,157 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
                     wave_m * 2, wave_m * 2 + 2);
 }
 
+// ---- small-M path: split K inside the workgroup -----------------------------------------
+//
+// For short activations (a few to a few hundred tokens) the tiled kernels leave most of
+// the chip idle: M = 1 gives one tile row, so only N / 192 compute units work while the
+// weights (the bulk of the bytes) stream through them. Here a workgroup owns A x B output
+// blocks of 32 x 32 (32A weight rows, 32B activation rows) and its 4 waves split K:
+// wave w takes the 64-element chunks w, w+4, w+8, ..., so together they read whole
+// 128-byte lines of every row. Each lane loads its fragments straight into registers
+// (16 bytes = 32 codes of one row, the same K mapping as the LDS layouts of the tiled
+// kernels, plus its two scale bytes), D chunks ahead of their use; the four partial sums
+// of each block meet in LDS at the end and are added in a fixed order.
+//
+// Requires K % 32 == 0, 16-byte aligned packed operands and 4-byte aligned scales, and
+// both operands below 2^31 bytes (32-bit buffer offsets). In a last chunk that holds only
+// 32 elements, the upper lane half reads past its row; its scale is forced to zero, so
+// those products vanish (E2M1 codes are always finite).
+template <int A, int B, int D>
+__global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
+  constexpr int NW = 4;
+  __shared__ float red[2][NW][16 * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int tiles_m = (int)((p.M + 32 * B - 1) / (32 * B));
+  const int tm = (int)blockIdx.x % tiles_m;  // consecutive workgroups share weight rows
+  const int tn = (int)blockIdx.x / tiles_m;
+  const int m0 = tm * 32 * B;
+  const int n0 = tn * 32 * A;
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
+  const int nchunks = (int)((p.K + 63) / 64);
+  const int nq = (nchunks - wave + NW - 1) / NW;  // this wave's chunks
+
+  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
+  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const uint32_t voff_p = r32 * pitch + h * 16;
+  const uint32_t voff_s = r32 * spitch + h * 2;
+
+  floatx16 acc[A][B];
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int g = 0; g < B; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  u32x4 wraw[D][A], xraw[D][B];
+  uint32_t wsr[D][A], xsr[D][B];
+  // chunk number q of this wave (chunk index wave + 4q) into ring slot d
+  auto load = [&](int d, int q) {
+    const int c = wave + NW * q;
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      wraw[d][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rwp, (int)voff_p, (int)((uint32_t)(n0 + 32 * i) * pitch + (uint32_t)c * 32), 0);
+      wsr[d][i] = __builtin_amdgcn_raw_buffer_load_b16(
+          rws, (int)voff_s, (int)((uint32_t)(n0 + 32 * i) * spitch + (uint32_t)c * 4), 0);
+    }
+#pragma unroll
+    for (int g = 0; g < B; ++g) {
+      xraw[d][g] = __builtin_amdgcn_raw_buffer_load_b128(
+          rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
+      xsr[d][g] = __builtin_amdgcn_raw_buffer_load_b16(
+          rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+    }
+  };
+  auto compute = [&](int d, int q) {
+    // upper lane half of a 32-element last chunk: no elements, zero scale
+    const bool dead = h == 1 && (int64_t)(wave + NW * q) * 64 + 32 >= p.K;
+    half2_t wsc[A], xsc[B];
+#pragma unroll
+    for (int i = 0; i < A; ++i) wsc[i] = scales_to_f16<true>(dead ? 0u : wsr[d][i]);
+#pragma unroll
+    for (int g = 0; g < B; ++g) xsc[g] = scales_to_f16<true>(dead ? 0u : xsr[d][g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half8_t wf[A], xf[B];
+#pragma unroll
+      for (int i = 0; i < A; ++i) wf[i] = decode8<true>(wraw[d][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
+#pragma unroll
+      for (int g = 0; g < B; ++g) xf[g] = decode8<true>(xraw[d][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
+#pragma unroll
+      for (int i = 0; i < A; ++i)
+#pragma unroll
+        for (int g = 0; g < B; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], xf[g], acc[i][g], 0, 0, 0);
+      // keep each k-step's decode next to its MFMAs (bounded register use)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nq) load(d, d);
+  for (int q = 0; q < nq; q += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (q + d < nq) {
+        compute(d, q + d);
+        if (q + d + D < nq) load(d, q + d + D);
+      }
+    }
+  }
+
+  // Partial sums: block by block, every wave writes its part, the owner wave (block
+  // number % 4) adds the four in wave order and stores.
+  const bool n_vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int g = 0; g < B; ++g) {
+      const int blk = i * B + g;
+      float* rb = red[blk & 1][0];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) rb[(wave * 16 + v) * 64 + lane] = acc[i][g][v];
+      __syncthreads();
+      if (wave == blk % NW) {
+        const int64_t m = (int64_t)m0 + g * 32 + r32;
+        if (m < p.M) {
+          uint16_t* orow = p.out + m * p.N;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = (int64_t)n0 + i * 32 + 8 * q + 4 * h;
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * q + e;
+              float s = rb[(0 * 16 + v) * 64 + lane];
+              s += rb[(1 * 16 + v) * 64 + lane];
+              s += rb[(2 * 16 + v) * 64 + lane];
+              s += rb[(3 * 16 + v) * 64 + lane];
+              b[e] = bf16_rne(s * p.alpha);
+            }
+            if (n_vec && n + 3 < p.N) {
+              *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+            }
+          }
+        }
+      }
+    }
+}
+
 template <int BM, int BN, int KC, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool fast) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -937,6 +1088,36 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
   *(u32x4*)&out[i * 8] = __builtin_bit_cast(u32x4, v);
 }
 
+// Rough cost model (core cycles of one launch) used to choose between the tiled
+// kernels; calibrated on the 32x32x16 f16 MFMA, which issues every ~34 cycles back to
+// back and slows down once a wave has more than about 3 VALU instructions per MFMA (the
+// decode costs 8 VALU per fragment of 8 elements per lane).
+double mfma_cycles(double frags_per_mfma) {
+  const double v = 8.0 * frags_per_mfma;
+  return 34.0 + (v > 3.0 ? 3.5 * (v - 3.0) : 0.0);
+}
+int64_t passes(int64_t wgs, int64_t cus) { return (wgs + cus - 1) / cus; }
+
+struct SplitShape { int a, b; };
+
+// Split-K workgroup shape for M activation rows: 32 x 32B outputs with B the smallest
+// of 1, 2, 4 that covers min(M, 128) rows (measured: wider shapes do not pay at these M).
+SplitShape splitk_shape(int64_t M) {
+  if (M <= 32) return {1, 1};
+  if (M <= 64) return {1, 2};
+  return {1, 4};
+}
+
+hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s) {
+  const int64_t wgs = ((p.N + 32 * s.a - 1) / (32 * s.a)) * ((p.M + 32 * s.b - 1) / (32 * s.b));
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs), block(256);
+  if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8>), grid, block, 0, stream, p);
+  else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 6>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 4>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
@@ -958,28 +1139,35 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
 #endif
   constexpr int FBM = NVFP4_FIT_BM, FBN = NVFP4_FIT_BN;
   const bool fast = aligned && (p.K % (64 * KC) == 0);
-  if (aligned && p.K % 128 == 0) {
-    // Tiles run one per compute unit at a time: compare whole passes over the chip,
-    // each costing a tile's area, and take the fit tile unless it loses.
-    const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
-    const int64_t t256 = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    const int64_t tfit = ((p.M + FBM - 1) / FBM) * ((p.N + FBN - 1) / FBN);
-    const int64_t c256 = (t256 + cus - 1) / cus * (int64_t)(BM * BN);
-    const int64_t cfit = (tfit + cus - 1) / cus * (int64_t)(FBM * FBN);
-    // the fit kernel addresses operands with 32-bit buffer offsets
-    const bool fits32 = (p.M + FBM) * (p.K / 2) < ((int64_t)1 << 31) &&
-                        (p.N + FBN) * (p.K / 2) < ((int64_t)1 << 31);
+  const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
+  // 32-bit buffer offsets (with one tile of rows past the end) for the fit and split-K kernels
+  const bool fits32 = (p.M + FBM) * (p.K / 2) < ((int64_t)1 << 31) &&
+                      (p.N + FBN) * (p.K / 2) < ((int64_t)1 << 31);
+  const int64_t nk = p.K / 128;
+  // tiled kernels: one tile per compute unit at a time, plus epilogue and prologue
+  const int64_t t256 = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const int64_t tfit = ((p.M + FBM - 1) / FBM) * ((p.N + FBN - 1) / FBN);
+  const double c256 = fast ? (double)passes(t256, cus) * (nk * 128 * mfma_cycles(0.5) + 20000.0) : 1e300;
+  const bool fit_ok = aligned && p.K % 128 == 0 && fits32;
+  const double cfit = fit_ok ? (double)passes(tfit, cus) * (nk * 108 * mfma_cycles(7.5 / 13.5) + 20000.0) : 1e300;
+  // Few tiles (short activations): the tiled kernels would leave most compute units
+  // idle for a whole K loop; split K inside the workgroup instead.
+  const bool split_ok = aligned && p.K % 32 == 0 && fits32;
+  const bool use_split = split_ok && tfit * 4 <= cus;
 #ifdef NVFP4_GEMM_FORCE_TILE
-    const bool use_fit = NVFP4_GEMM_FORCE_TILE == 1 && fits32;
-#else
-    const bool use_fit = cfit <= c256 && fits32;
+  // development switch: 0 = 256x256, 1 = fit tile, 2 = split-K
+  if (NVFP4_GEMM_FORCE_TILE == 2 && split_ok) return launch_splitk(p, stream, splitk_shape(p.M));
+  if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) {
+    hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (NVFP4_GEMM_FORCE_TILE == 0) return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
 #endif
-    if (use_fit) {
-      if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream,
-                         p);
-      return hipGetLastError();
-    }
+  if (use_split) return launch_splitk(p, stream, splitk_shape(p.M));
+  if (cfit <= c256 && fit_ok) {
+    if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+    return hipGetLastError();
   }
   return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
 }

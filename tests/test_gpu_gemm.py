@@ -48,6 +48,10 @@ def _assert_close(got_bits, ap, as_, ags, wp, ws, wgs, label):
     (1, 64, 64), (17, 72, 128), (256, 256, 256), (300, 520, 320), (513, 260, 1024),
     (33, 40, 16), (40, 36, 48), (64, 64, 80), (130, 132, 144),   # K % 64 != 0, K % 32 == 16
     (255, 257, 192), (7, 3, 32),
+    # split-K path with a half-filled last 64-element chunk (K % 64 == 32), covering the
+    # three workgroup shapes the launcher picks: 32x32, 32x64 and 32x128 outputs
+    (5, 200, 96), (100, 70, 224), (3, 5000, 1056), (33, 6144, 96), (256, 12288, 96),
+    (640, 3072, 96),
 ])
 def test_gemm_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 131 + N * 7 + K)
