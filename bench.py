@@ -8,7 +8,8 @@ does. Inputs are resident in HBM when timing starts.
 
 Prints one JSON line (rank 0) with the step throughput in TFLOP/s (2*M*N*K per step),
 the dominant kernel's roofline (GEMM vs the f16 dense MFMA peak), the quantize kernel's
-HBM bandwidth on rotated buffers, and the CPU oracle timed on a bounded sample.
+HBM bandwidth on rotated buffers (for the workload's activation and for a large
+4608 x 12288 activation), and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
 """
@@ -210,6 +211,30 @@ def main():
     q_gbs = QUANT_BYTES_PER_ELEM * M * K / (q_rot_ms * 1e-3) / 1e9
     del xs, outs
 
+    # quantize bandwidth on a large activation (the 4608 x 12288 input of a FLUX MLP down
+    # projection), rotated the same way
+    LM, LK = 4608, 12288
+    n_rot_l = max(2, int(args.rotate_mb * 2**20 // (LM * LK * 2)))
+    gen = torch.Generator(device=dev).manual_seed(5)
+    xl = [torch.randn((LM, LK), device=dev, generator=gen).to(torch.bfloat16) for _ in range(n_rot_l)]
+    ol = [(torch.empty((LM, LK // 2), dtype=torch.uint8, device=dev),
+           torch.empty((LM, LK // 16), dtype=torch.uint8, device=dev)) for _ in range(n_rot_l)]
+    f_lgs = ctypes.c_float(nv.calibrate(xl[0]))
+    pl = [(P(a), P(b), P(c)) for a, (b, c) in zip(xl, ol)]
+    for i in range(n_rot_l):
+        lib.nvfp4_quantize(pl[i][0], LM, LK, f_lgs, pl[i][1], pl[i][2], sp)
+    n_ql = max(args.steps, 4 * n_rot_l)
+    torch.cuda.synchronize()
+    qa.record(stream)
+    for i in range(n_ql):
+        a, b, c = pl[i % n_rot_l]
+        lib.nvfp4_quantize(a, LM, LK, f_lgs, b, c, sp)
+    qb.record(stream)
+    torch.cuda.synchronize()
+    ql_ms = qa.elapsed_time(qb) / n_ql
+    ql_gbs = QUANT_BYTES_PER_ELEM * LM * LK / (ql_ms * 1e-3) / 1e9
+    del xl, ol
+
     if args.copy_calibration_mb:
         # Known-size reference for the hardware byte counters: a plain device copy of
         # N MiB whose source was evicted from the caches by a larger fill in between.
@@ -263,6 +288,13 @@ def main():
             "frac": round(q_gbs / PEAK_HBM_GBS, 4),
             "bytes_per_launch": int(QUANT_BYTES_PER_ELEM * M * K),
             "rotated_buffers": n_rot,
+            "large": {
+                "shape": [LM, LK],
+                "rotated_avg_ms": round(ql_ms, 5),
+                "achieved": round(ql_gbs, 1),
+                "frac": round(ql_gbs / PEAK_HBM_GBS, 4),
+                "rotated_buffers": n_rot_l,
+            },
         },
         "precision": "E2M1 x E4M3 operands decoded exactly to f16, f16 MFMA, fp32 accumulate, "
                      "bf16 output",

@@ -9,11 +9,13 @@
 //  * K % 16 == 0, so 16-element blocks never straddle rows and the tensor is a flat
 //    array of M*K/16 independent blocks; block b reads bytes [32b, 32b+32) of x, writes
 //    bytes [8b, 8b+8) of packed and byte b of scales.
-//  * One lane owns one block: two 16-byte loads, the amax in registers (no cross-lane
-//    traffic), one 8-byte and one 1-byte store. Consecutive lanes own consecutive
-//    blocks, so a wave reads 2 KiB and writes 512 + 64 contiguous bytes.
-//  * Each lane handles UNROLL blocks per step with all loads issued first (UNROLL x 32 B
-//    in flight per lane) to keep enough bytes in flight for HBM.
+//  * Two lanes share a block: lane 2i+h loads the h-th 16 bytes (8 elements) of block
+//    i, so the lanes of a wave read 1 KiB of consecutive bytes per load instruction.
+//    The block amax is the larger of the pair's partial maxima (one DPP lane swap);
+//    both lanes derive the same scale, each encodes its 8 elements into one 32-bit word
+//    (consecutive lanes write consecutive words) and the even lane writes the scale.
+//  * Each lane handles UNROLL halves per step with all loads issued first, to keep
+//    enough bytes in flight for HBM.
 //  * Rounding: the per-block scale uses IEEE division; the per-element quotient
 //    |x| / d uses the reciprocal of d plus Markstein's fma correction, which equals the
 //    IEEE quotient for every bf16 x (see codec.hpp); the E2M1 encode is the gfx950
@@ -35,68 +37,69 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
   }
 }
 
-// Encode 16 values (in f) of one block into 8 packed bytes, given the block's scale.
-// kClamp selects the quotient form that tolerates an overflowing |x| * r (only needed
-// for blocks whose scale saturated).
+// Encode 8 values (in f) of one half block into 4 packed bytes (element 2j in the low
+// nibble of byte j), given the block's scale. kClamp selects the quotient form that
+// tolerates an overflowing |x| * r (only needed for blocks whose scale saturated).
 template <bool kClamp>
-__device__ __forceinline__ u32x2 encode_block(const float* f, const BlockScale& bs) {
-  uint32_t out[2] = {0u, 0u};
+__device__ __forceinline__ uint32_t encode_half(const float* f, const BlockScale& bs) {
+  uint32_t out = 0u;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const float y0 = kClamp ? div_by_scale(f[2 * j], bs.d, bs.r)
                             : div_by_scale_unclamped(f[2 * j], bs.d, bs.r);
     const float y1 = kClamp ? div_by_scale(f[2 * j + 1], bs.d, bs.r)
                             : div_by_scale_unclamped(f[2 * j + 1], bs.d, bs.r);
-    // byte j % 4 of word j / 4 <- {code(y1) << 4 | code(y0)}
-    switch (j & 3) {
-      case 0: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 0); break;
-      case 1: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 1); break;
-      case 2: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 2); break;
-      default: out[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], y0, y1, 1.0f, 3); break;
+    switch (j) {
+      case 0: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 0); break;
+      case 1: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 1); break;
+      case 2: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 2); break;
+      default: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 3); break;
     }
   }
-  return u32x2{out[0], out[1]};
+  return out;
 }
 
+// nhalves = 2 * (number of blocks); half index hi covers x[hi] (16 bytes) and packed
+// word hi. The pair (hi, hi ^ 1) is one block; since nhalves is even and workgroups are
+// a multiple of 2 lanes, both lanes of a pair are always in the same loop state.
 template <int UNROLL>
 __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__ x,
-                                                       u32x2* __restrict__ packed,
+                                                       uint32_t* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
-                                                       int64_t nblocks, float gs, float den,
+                                                       int64_t nhalves, float gs, float den,
                                                        float rden) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * UNROLL;
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nblocks;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nhalves;
        base += stride) {
-    u32x4 v[UNROLL][2];
+    u32x4 v[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int64_t b = base + (int64_t)u * blockDim.x;
-      if (b < nblocks) {
-        v[u][0] = __builtin_nontemporal_load(&x[2 * b]);
-        v[u][1] = __builtin_nontemporal_load(&x[2 * b + 1]);
-      }
+      const int64_t hi = base + (int64_t)u * blockDim.x;
+      v[u] = hi < nhalves ? __builtin_nontemporal_load(&x[hi]) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int64_t b = base + (int64_t)u * blockDim.x;
-      if (b < nblocks) {
-        float f[16];
-        unpack_bf16x8(v[u][0], f);
-        unpack_bf16x8(v[u][1], f + 8);
-        float amax = 0.0f;
+      const int64_t hi = base + (int64_t)u * blockDim.x;
+      float f[8];
+      unpack_bf16x8(v[u], f);
+      float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-        const BlockScale bs = block_scale(amax, den, rden, gs);
-        // Saturated scales are rare (the tensor's largest block under a self-calibrated
-        // scale, or a static scale that is too small); the whole wave takes the clamped
-        // quotient if any of its lanes has one.
-        u32x2 p;
-        if (__any(bs.code == kE4M3MaxCode))
-          p = encode_block<true>(f, bs);
-        else
-          p = encode_block<false>(f, bs);
-        __builtin_nontemporal_store(p, &packed[b]);
-        scales[b] = (uint8_t)bs.code;
+      for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(f[i]));
+      // partner lane's partial maximum (DPP quad_perm [1, 0, 3, 2]: lane ^ 1)
+      const float o = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), den, rden, gs);
+      // Saturated scales are rare (the tensor's largest block under a self-calibrated
+      // scale, or a static scale that is too small); the whole wave takes the clamped
+      // quotient if any of its lanes has one.
+      uint32_t word;
+      if (__any(bs.code == kE4M3MaxCode))
+        word = encode_half<true>(f, bs);
+      else
+        word = encode_half<false>(f, bs);
+      if (hi < nhalves) {
+        __builtin_nontemporal_store(word, &packed[hi]);
+        if ((hi & 1) == 0) scales[hi >> 1] = (uint8_t)bs.code;
       }
     }
   }
@@ -106,10 +109,10 @@ __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__
 
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,
                            void* scales, hipStream_t stream, const LaunchInfo& dev) {
-  const int64_t nblocks = M * (K / 16);
-  if (nblocks == 0) return hipSuccess;
+  const int64_t nhalves = M * (K / 16) * 2;
+  if (nhalves == 0) return hipSuccess;
 #ifndef NVFP4_QUANT_UNROLL
-#define NVFP4_QUANT_UNROLL 1
+#define NVFP4_QUANT_UNROLL 2
 #endif
 #ifndef NVFP4_QUANT_WG_PER_CU
 #define NVFP4_QUANT_WG_PER_CU 32
@@ -118,13 +121,13 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
   constexpr int kUnroll = NVFP4_QUANT_UNROLL;
   const float den = 6.0f * gs;   // IEEE binary32 on the host
   const float rden = 1.0f / den;
-  int64_t want = (nblocks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  const int64_t want = (nhalves + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   // Enough workgroups to fill every CU several times over; the grid-stride loop covers
   // the rest.
   const int64_t cap = (int64_t)dev.num_cus * NVFP4_QUANT_WG_PER_CU;
   const int grid = (int)(want < cap ? want : cap);
   hipLaunchKernelGGL((quantize_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const u32x4*)x, (u32x2*)packed, (uint8_t*)scales, nblocks, gs, den, rden);
+                     (const u32x4*)x, (uint32_t*)packed, (uint8_t*)scales, nhalves, gs, den, rden);
   return hipGetLastError();
 }
 
