@@ -105,6 +105,26 @@ int nvfp4_gemm(const void* a_packed, const void* a_scales, float a_global_scale,
                const void* w_packed, const void* w_scales, float w_global_scale,
                int64_t M, int64_t N, int64_t K, void* out_bf16, void* stream);
 
+/*
+ * W4A16 GEMM: NVFP4 weights, bf16 activations left unquantized, the pages' path for
+ * hardware without the fused FP4 kernel ("BFL (fp8r / nvfp4)", text under the Kernels
+ * table: the weights are dequantized to the compute dtype and the layer runs as an
+ * ordinary linear, so results differ slightly from the W4A4 path).
+ *   out = bf16_RNE(w_global * sum_k x_k w_k) with w_k = E2M1 x E4M3 decoded exactly; the
+ *   products are exact and accumulate in fp32; any result within
+ *   2^-10 * sum_k |x_k w_k| (global scale included) + 1 bf16 ulp of the exact value is
+ *   correct, and the library's result is deterministic for a given shape.
+ *   x_bf16              device, bf16 [M, K], 16-byte aligned, read only
+ *   w_packed, w_scales  device, weights in NVFP4 layout [N, K/2] (16-byte aligned),
+ *                       [N, K/16] (4-byte aligned)
+ *   w_global_scale      fp32, finite, in [2^-90, 2^90]
+ *   K                   K % 32 == 0 and K <= 2^22 (else NVFP4_ERROR_INVALID_SHAPE)
+ *   out_bf16            device, bf16 [M, N], 16-byte aligned, written
+ */
+int nvfp4_gemm_w4a16(const void* x_bf16, const void* w_packed, const void* w_scales,
+                     float w_global_scale, int64_t M, int64_t N, int64_t K, void* out_bf16,
+                     void* stream);
+
 /* Workspace bytes nvfp4_linear needs for an [M, K] activation (packed + scales, each
  * rounded up to 256 bytes). Returns 0 for invalid shapes. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);

@@ -5,6 +5,7 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`quantize`  -- bf16 [M, K] -> packed E2M1 [M, K/2] + E4M3 scales [M, K/16]
 * :func:`gemm`      -- block-scaled W4A4 GEMM, bf16 output
 * :func:`linear`    -- fused quantize + GEMM through a workspace
+* :func:`gemm_w4a16` -- NVFP4 weights x bf16 activations (not quantized), bf16 output
 * :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
 """
 from ._lib import NVFP4Error, load_library  # noqa: F401
@@ -12,6 +13,7 @@ from .ops import (  # noqa: F401
     amax,
     calibrate,
     gemm,
+    gemm_w4a16,
     global_scale_from_amax,
     linear,
     linear_workspace_bytes,

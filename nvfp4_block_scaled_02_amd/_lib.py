@@ -36,6 +36,7 @@ SIGNATURES = {
     "nvfp4_last_hip_error": (_int, []),
     "nvfp4_quantize": (_int, [_vp, _i64, _i64, _f32, _vp, _vp, _vp]),
     "nvfp4_gemm": (_int, [_vp, _vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_linear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_linear": (_int, [_vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp,
                             ctypes.c_size_t, _vp]),

@@ -147,6 +147,28 @@ int nvfp4_gemm(const void* ap, const void* as, float ags, const void* wp, const 
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
+int nvfp4_gemm_w4a16(const void* x, const void* wp, const void* ws, float wgs, int64_t M,
+                     int64_t N, int64_t K, void* out, void* stream) {
+  if (!x || !wp || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if (!valid_scale(wgs)) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (K % 32 != 0 || K > ((int64_t)1 << 22)) return NVFP4_ERROR_INVALID_SHAPE;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  if (!aligned(x, 16) || !aligned(wp, 16) || !aligned(out, 16) || !aligned(ws, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  if (M == 0 || N == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  nvfp4::W4A16Problem p{(const uint16_t*)x, (const uint8_t*)wp, (const uint8_t*)ws,
+                        (uint16_t*)out, M, N, K, wgs};
+  hipError_t e = nvfp4::launch_gemm_w4a16(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
   if (check_shape(M, K)) return 0;
   return round_up((size_t)(M * K / 2), 256) + round_up((size_t)(M * K / 16), 256);

@@ -1,0 +1,186 @@
+// W4A16 GEMM for gfx950: out[M, N] (bf16) = w_global * X[M, K] W_hat[N, K]^T with X
+// bf16 (unquantized activations) and W_hat decoded from NVFP4 (E2M1 codes x per-16 E4M3
+// scales).
+//
+// This is the pages' path for hardware without the fused FP4 kernel: the weights stay
+// NVFP4 in memory and the activations are not quantized ("BFL (fp8r / nvfp4)", text
+// under the Kernels table), so its results differ slightly from the W4A4 kernel. It also
+// suits short activations, where the weights dominate the bytes.
+//
+// Arithmetic: a decoded weight q * s has at most 6 significant bits and is exact in bf16;
+// a bf16 x times it is exact in fp32, so the bf16 MFMA forms exact products and
+// accumulates in fp32. The weight decode goes through fp32 (gfx950 has no packed bf16
+// multiply): the fp4 -> fp32 conversion gives q, one fp32 multiply by s, and a packed
+// conversion to bf16 (exact). 16 VALU per 8 elements per lane; the activations need none.
+//
+// Structure (split K inside the workgroup, as the W4A4 short-activation kernel): a
+// workgroup owns 32 weight rows x 32B activation rows; its 4 waves take interleaved
+// 64-element chunks of K (wave w: chunks w, w+4, ...), load their fragments straight into
+// registers D chunks ahead, and the four partial sums of each 32x32 block meet in LDS in
+// a fixed order. K mapping as in the W4A4 kernels: lane half h feeds MFMA K-slots
+// [8h, 8h+8) with chunk elements 32h + 8j .. 32h + 8j + 7 on k-step j, which for X is one
+// 16-byte load of 8 consecutive bf16.
+//
+// Buffer resources start at the workgroup's first row, so offsets are tile-local (any M
+// and N) and rows past M or N read as zero.
+#include "gemm_common.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Eight E2M1 codes (element i in bits 4i..4i+3 of p) times the fp32 block scale s, as
+// bf16 (exact). Every conversion result is consumed as a whole vector.
+__device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t p, float s) {
+  const float2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+  const float2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
+  const float2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
+  const float2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
+  const bf16x2_t b0 = __builtin_convertvector(q0 * s, bf16x2_t);
+  const bf16x2_t b1 = __builtin_convertvector(q1 * s, bf16x2_t);
+  const bf16x2_t b2 = __builtin_convertvector(q2 * s, bf16x2_t);
+  const bf16x2_t b3 = __builtin_convertvector(q3 * s, bf16x2_t);
+  return __builtin_bit_cast(bf16x8_t, u32x4{__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                                            __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3)});
+}
+
+template <int B, int D>
+__global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
+  constexpr int NW = 4;
+  __shared__ float red[2][NW][16 * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int64_t tiles_m = (p.M + 32 * B - 1) / (32 * B);
+  const int64_t tm = (int64_t)blockIdx.x % tiles_m;  // consecutive workgroups share weight rows
+  const int64_t tn = (int64_t)blockIdx.x / tiles_m;
+  const int64_t m0 = tm * 32 * B;
+  const int64_t n0 = tn * 32;
+  const uint32_t xpitch = (uint32_t)(p.K * 2);  // bytes per activation row
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
+  const int nchunks = (int)((p.K + 63) / 64);
+  const int nq = (nchunks - wave + NW - 1) / NW;  // this wave's chunks
+
+  auto clamp31 = [](int64_t n) { return (uint32_t)(n < 0x7FFFFFFF ? n : 0x7FFFFFFF); };
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x + m0 * p.K, clamp31((p.M - m0) * (int64_t)xpitch));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed + n0 * pitch, clamp31((p.N - n0) * (int64_t)pitch));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales + n0 * spitch, clamp31((p.N - n0) * (int64_t)spitch));
+  const uint32_t voff_x = r32 * xpitch + h * 64;
+  const uint32_t voff_w = r32 * pitch + h * 16;
+  const uint32_t voff_s = r32 * spitch + h * 2;
+
+  floatx16 acc[B];
+#pragma unroll
+  for (int g = 0; g < B; ++g)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[g][v] = 0.0f;
+
+  u32x4 wraw[D], xraw[D][B][4];
+  uint32_t wsr[D];
+  auto load = [&](int d, int q) {
+    const uint32_t c = (uint32_t)(wave + NW * q);
+    wraw[d] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)voff_w, (int)(c * 32), 0);
+    wsr[d] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)voff_s, (int)(c * 4), 0);
+#pragma unroll
+    for (int g = 0; g < B; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xraw[d][g][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, (int)(voff_x + 16 * j), (int)((uint32_t)g * 32 * xpitch + c * 128), 0);
+  };
+  auto compute = [&](int d, int q) {
+    // upper lane half of a 32-element last chunk: no elements (its loads read the next
+    // row or zeros), so both its weights and its activations are forced to zero
+    const bool dead = h == 1 && (int64_t)(wave + NW * q) * 64 + 32 >= p.K;
+    const uint32_t sw = dead ? 0u : wsr[d];
+    const float s_lo = e4m3_decode(sw & 0xFFu);
+    const float s_hi = e4m3_decode((sw >> 8) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t wf = decode8_bf16(wraw[d][j], j < 2 ? s_lo : s_hi);
+#pragma unroll
+      for (int g = 0; g < B; ++g) {
+        const u32x4 xv = dead ? u32x4{0u, 0u, 0u, 0u} : xraw[d][g][j];
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, __builtin_bit_cast(bf16x8_t, xv), acc[g], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nq) load(d, d);
+  for (int q = 0; q < nq; q += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (q + d < nq) {
+        compute(d, q + d);
+        if (q + d + D < nq) load(d, q + d + D);
+      }
+    }
+  }
+
+  // Partial sums: block by block, every wave writes its part, the owner wave (block
+  // number % 4) adds the four in wave order and stores.
+  const bool n_vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < B; ++g) {
+    float* rb = red[g & 1][0];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rb[(wave * 16 + v) * 64 + lane] = acc[g][v];
+    __syncthreads();
+    if (wave == g % NW) {
+      const int64_t m = m0 + g * 32 + r32;
+      if (m < p.M) {
+        uint16_t* orow = p.out + m * p.N;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int64_t n = n0 + 8 * qd + 4 * h;
+          uint32_t b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * qd + e;
+            float s = rb[(0 * 16 + v) * 64 + lane];
+            s += rb[(1 * 16 + v) * 64 + lane];
+            s += rb[(2 * 16 + v) * 64 + lane];
+            s += rb[(3 * 16 + v) * 64 + lane];
+            b[e] = bf16_rne(s * p.alpha);
+          }
+          if (n_vec && n + 3 < p.N) {
+            *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
+  (void)dev;
+  // workgroup shape: 32 weight rows x 32B activation rows, B the smallest of 1, 2, 4 that
+  // covers min(M, 128) rows
+  const int B = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
+  const int64_t wgs = ((p.N + 31) / 32) * ((p.M + 32 * B - 1) / (32 * B));
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs), block(256);
+  if (B == 1) hipLaunchKernelGGL((gemm_w4a16_kernel<1, 6>), grid, block, 0, stream, p);
+  else if (B == 2) hipLaunchKernelGGL((gemm_w4a16_kernel<2, 4>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((gemm_w4a16_kernel<4, 2>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -25,6 +25,17 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
 
+struct W4A16Problem {
+  const uint16_t* x;  // bf16 [M, K]
+  const uint8_t* w_packed;
+  const uint8_t* w_scales;
+  uint16_t* out;
+  int64_t M, N, K;
+  float alpha;  // the weights' global scale
+};
+
+hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev);
+
 hipError_t launch_amax(const void* x, int64_t n, float* out, hipStream_t stream,
                        const LaunchInfo& dev);
 

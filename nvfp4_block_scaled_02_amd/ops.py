@@ -82,6 +82,27 @@ def gemm(a_packed: torch.Tensor, a_scales: torch.Tensor, a_global_scale: float,
     return out
 
 
+def gemm_w4a16(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
+               w_global_scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """W4A16 GEMM: bf16 [M, N] = w_gs * x @ W_hat^T with x bf16 (not quantized)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_packed, "w_packed", torch.uint8, 2)
+    _need(w_scales, "w_scales", torch.uint8, 2)
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if tuple(w_packed.shape) != (N, K // 2) or tuple(w_scales.shape) != (N, K // 16):
+        raise ValueError("weight shapes do not match x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape must be [M, N]")
+    lib = load_library()
+    check(lib.nvfp4_gemm_w4a16(_ptr(x), _ptr(w_packed), _ptr(w_scales), float(w_global_scale),
+                               M, N, K, _ptr(out), _stream(stream)), "nvfp4_gemm_w4a16")
+    return out
+
+
 def linear_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().nvfp4_linear_workspace_bytes(M, K))
 

@@ -325,17 +325,22 @@ def linear_ref(x_bits, a_gs, w_packed, w_scales, w_gs):
     return (ap, as_), ref, absref
 
 
-def w4a16_ref(x_bits, w_packed, w_scales, w_gs) -> np.ndarray:
+def w4a16_ref(x_bits, w_packed, w_scales, w_gs, *, with_abs: bool = True):
     """Dequantise-only product (bf16 activations kept unquantised), float64.
 
     The pages' fallback on devices without the fused kernel ("BFL (fp8r / nvfp4)",
     text under the Kernels table): weights are dequantised to the compute dtype every
     forward pass and the layer runs as an ordinary linear, so results differ slightly
-    from the fused W4A4 kernel.
+    from the fused W4A4 kernel. Reading: the product uses the exactly decoded weights
+    (q * s * w_gs); a bf16 x times a decoded weight is exact in float64, as is every
+    partial sum far below the acceptance bound. Returns ``(ref, absref)`` with
+    ``absref = |X| @ |W_hat|^T`` (global scale included) for the tolerance (or None).
     """
     X = bf16_bits_to_f32(x_bits).astype(np.float64)
     W = dequantize(w_packed, w_scales, w_gs)
-    return X @ W.T
+    ref = X @ W.T
+    absref = np.abs(X) @ np.abs(W).T if with_abs else None
+    return ref, absref
 
 
 def nvfp4_bytes(rows: int, K: int) -> int:

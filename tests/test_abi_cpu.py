@@ -100,6 +100,34 @@ def test_gemm_validation(lib):
     assert call({7: 0}) == L.SUCCESS
 
 
+def test_gemm_w4a16_validation(lib):
+    g = lib.nvfp4_gemm_w4a16
+    args = [P16, P16b, P16b, 1.0, 8, 8, 64, P16, NULL]
+
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return g(*a)
+
+    assert call({0: NULL}) == L.INVALID_VALUE
+    assert call({1: NULL}) == L.INVALID_VALUE
+    assert call({2: NULL}) == L.INVALID_VALUE
+    assert call({7: NULL}) == L.INVALID_VALUE
+    assert call({3: 0.0}) == L.INVALID_VALUE
+    assert call({3: 2.0**91}) == L.INVALID_VALUE
+    assert call({6: 48}) == L.INVALID_SHAPE   # K % 32 != 0
+    assert call({6: 40}) == L.INVALID_SHAPE
+    assert call({6: 2**23}) == L.INVALID_SHAPE
+    assert call({4: -1}) == L.INVALID_SHAPE
+    assert call({0: ODD}) == L.MISALIGNED
+    assert call({1: ODD}) == L.MISALIGNED
+    assert call({2: ctypes.c_void_p(0x20002)}) == L.MISALIGNED
+    assert call({7: ODD}) == L.MISALIGNED
+    assert call({4: 0}) == L.SUCCESS
+    assert call({5: 0}) == L.SUCCESS
+
+
 def test_linear_validation_and_workspace(lib):
     ws = lib.nvfp4_linear_workspace_bytes
     assert ws(4608, 3072) == (4608 * 3072 // 2) + ((4608 * 3072 // 16 + 255) // 256 * 256)

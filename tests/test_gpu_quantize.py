@@ -47,7 +47,7 @@ def test_workload_activations_and_weights_bit_exact(name):
 
 def test_amax_exact_on_odd_lengths():
     rng = np.random.default_rng(5)
-    for n in [1, 7, 8, 9, 1000, 4097, 123457]:
+    for n in [1, 7, 8, 9, 1000, 4097, 123457, 3000001]:
         v = to_bf16_bits((rng.standard_normal(n) * np.exp(rng.uniform(-5, 5))).astype(np.float32))
         say("amax", n)
         got = to_host(nv.amax(bf16_to_dev(v)))[0]

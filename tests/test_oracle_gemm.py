@@ -129,7 +129,7 @@ def test_w4a16_differs_from_w4a4_but_stays_close():
     x, ags, ap, as_ = _q(rng, M, K)
     _, wgs, wp, ws = _q(rng, N, K, scale=0.02)
     w4a4, absref = O.gemm_ref(ap, as_, ags, wp, ws, wgs)
-    w4a16 = O.w4a16_ref(x, wp, ws, wgs)
+    w4a16, _ = O.w4a16_ref(x, wp, ws, wgs, with_abs=False)
     diff = np.abs(w4a4 - w4a16)
     assert diff.max() > 0
     # activation quantisation error per element is at most one scale step (6/448 of
@@ -138,3 +138,57 @@ def test_w4a16_differs_from_w4a4_but_stays_close():
     Xh = O.dequantize(ap, as_, ags)
     bound = np.abs(X - Xh) @ np.abs(O.dequantize(wp, ws, wgs)).T
     assert np.all(diff <= bound * (1 + 1e-9) + 1e-30)
+
+
+def test_w4a16_brute_force_rationals():
+    """The W4A16 reference against exact rational arithmetic: each output is
+    w_gs * sum_k x_k * e2m1(q_k) * e4m3(s_block) ("BFL (fp8r / nvfp4)", text under the
+    Kernels table: weights dequantised, activations left as they are)."""
+    rng = np.random.default_rng(31)
+    K = 32
+    x = to_bf16_bits(rng.standard_normal((3, K)).astype(np.float32))
+    _, wgs, wp, ws = _q(rng, 4, K, scale=0.02)
+    ref, absref = O.w4a16_ref(x, wp, ws, wgs)
+    xf = O.bf16_bits_to_f32(x)
+    wc = O.unpack_codes(wp)
+    g = Fraction(float(wgs))
+    for m in range(3):
+        for n in range(4):
+            want = Fraction(0)
+            want_abs = Fraction(0)
+            for k in range(K):
+                q = S.e2m1_magnitude_value(int(wc[n, k]) & 7) * (-1 if int(wc[n, k]) & 8 else 1)
+                w = q * S.e4m3_value(int(ws[n, k // 16])) * g
+                want += Fraction(float(xf[m, k])) * w
+                want_abs += abs(Fraction(float(xf[m, k])) * w)
+            assert ref[m, n] == float(want)
+            assert absref[m, n] == float(want_abs)
+
+
+def test_w4a16_identity_weights_reproduce_activations():
+    """W = c * I with c on the E2M1 grid and w_gs = 2^-6: out = x exactly scaled by c."""
+    rng = np.random.default_rng(32)
+    K = 64
+    x = to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32))
+    eye = to_bf16_bits((np.eye(K) * 3.0).astype(np.float32))
+    wgs = np.float32(2.0**-6)
+    wp, ws = O.quantize(eye, wgs)
+    ref, _ = O.w4a16_ref(x, wp, ws, wgs, with_abs=False)
+    assert np.array_equal(ref, O.bf16_bits_to_f32(x).astype(np.float64) * 3.0)
+
+
+def test_w4a16_on_grid_activations_equals_w4a4():
+    """Activations that already lie on the NVFP4 grid (dequantised under a power-of-two
+    global scale, so they are exact in bf16) give the same product through both paths."""
+    rng = np.random.default_rng(33)
+    M, N, K = 6, 7, 96
+    x0 = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    ags = np.float32(2.0**-4)
+    ap, as_ = O.quantize(x0, ags)
+    xd = O.dequantize(ap, as_, ags)
+    x = to_bf16_bits(xd.astype(np.float32))
+    assert np.array_equal(O.bf16_bits_to_f32(x).astype(np.float64), xd)  # exact in bf16
+    _, wgs, wp, ws = _q(rng, N, K, scale=0.02)
+    w4a4, _ = O.gemm_ref(ap, as_, ags, wp, ws, wgs, with_abs=False)
+    w4a16, _ = O.w4a16_ref(x, wp, ws, wgs, with_abs=False)
+    assert np.array_equal(w4a4, w4a16)

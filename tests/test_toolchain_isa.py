@@ -47,3 +47,29 @@ def test_every_decoding_kernel_converts_all_four_bytes(gemm_asm):
                 m = re.search(r"op_sel:\[(\d),(\d),\d\]", line)
                 sels[(m.group(1), m.group(2)) if m else ("0", "0")] += 1
         assert len(sels) == 4 and len(set(sels.values())) == 1, (name, dict(sels))
+
+
+@pytest.fixture(scope="module")
+def w4a16_asm(tmp_path_factory):
+    from nvfp4_block_scaled_02_amd import build as B
+
+    out = str(tmp_path_factory.mktemp("isa") / "gemm_w4a16.s")
+    cmd = [B.hipcc(), *B.compile_flags(), "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, "gemm_w4a16.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return open(out).read()
+
+
+def test_w4a16_kernels_convert_all_four_bytes(w4a16_asm):
+    """The W4A16 weight decode goes through the fp4 -> fp32 conversion: same check."""
+    kernels = _kernels(w4a16_asm)
+    decoding = {k: v for k, v in kernels.items() if "v_cvt_scalef32_pk_f32_fp4" in v}
+    assert decoding and all("w4a16" in k for k in decoding), list(kernels)
+    for name, body in decoding.items():
+        sels = Counter()
+        for line in body.splitlines():
+            if "v_cvt_scalef32_pk_f32_fp4" in line:
+                m = re.search(r"op_sel:\[(\d),(\d),\d\]", line)
+                sels[(m.group(1), m.group(2)) if m else ("0", "0")] += 1
+        assert len(sels) == 4 and len(set(sels.values())) == 1, (name, dict(sels))
