@@ -1,4 +1,5 @@
-"""CPU oracle for the NVFP4 W4A4 linear path -- test infrastructure, not product.
+"""CPU oracle for the NVFP4 W4A4 linear path (and the MXFP8 path) -- test
+infrastructure, not product.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. It shares no code with the HIP library: no
@@ -7,5 +8,7 @@ kernels, headers, tables, constants generators or pre/post-processing.
 * ``oracle.nvfp4_oracle``  -- vectorised NumPy oracle (quantize, dequantize, GEMM
   reference in float64, exact int64 GEMM, tolerance check).
 * ``oracle.scalar_oracle`` -- exact ``Fraction`` brute force used to pin the former.
+* ``oracle.mxfp8_oracle``  -- MXFP8 (OCP microscaling, E4M3 elements, 32-element
+  blocks, E8M0 scales) quantize, dequantize and GEMM reference.
 """
-from . import nvfp4_oracle, scalar_oracle  # noqa: F401
+from . import mxfp8_oracle, nvfp4_oracle, scalar_oracle  # noqa: F401
