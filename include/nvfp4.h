@@ -125,6 +125,38 @@ int nvfp4_gemm_w4a16(const void* x_bf16, const void* w_packed, const void* w_sca
                      float w_global_scale, int64_t M, int64_t N, int64_t K, void* out_bf16,
                      void* stream);
 
+/*
+ * MXFP8 (OCP microscaling) path: the second microscaling format of the zubnet.ai page
+ * (paragraph 1: Open Compute Project standard, 8-bit E4M3/E5M2 elements, 32-element
+ * blocks sharing one scale). Conventions of this library (the page names the OCP
+ * standard; these follow its format definition):
+ *   - elements are OCP E4M3 ("FN", max 448), one byte each, row-major [rows, K];
+ *   - each 32-element block along K shares an E8M0 scale byte (value 2^(byte - 127),
+ *     0xFF never produced), row-major [rows, K/32];
+ *   - quantization: e = floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block:
+ *     e = -127, byte 0); element = E4M3 nearest to x / 2^e, ties to even, saturating at
+ *     448, sign copied (-0 -> 0x80);
+ *   - GEMM: out = bf16_RNE(sum_k a_k w_k) with a_k, w_k the decoded values, no tensor
+ *     scale; any result within 2^-10 * sum_k |a_k w_k| + 1 bf16 ulp of the exact value is
+ *     correct and the library's result is deterministic for a given shape.
+ *
+ * nvfp4_mxfp8_quantize: x_bf16 [M, K] (16-byte aligned) -> codes uint8 [M, K] (16-byte
+ * aligned) and scales uint8 [M, K/32]. K % 32 == 0. Bit-exact to the rule above.
+ */
+int nvfp4_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes, void* scales,
+                         void* stream);
+
+/*
+ * nvfp4_mxfp8_gemm: out_bf16 [M, N] = A_hat [M, K] W_hat [N, K]^T with both operands MXFP8
+ * (activations a_codes/a_scales, weights w_codes/w_scales as produced by
+ * nvfp4_mxfp8_quantize). K % 128 == 0 and (max(M, N) + 256) * K < 2^31, else
+ * NVFP4_ERROR_INVALID_SHAPE; codes and out 16-byte aligned, scales 4-byte aligned.
+ * Runs on gfx950's block-scaled fp8 MFMA, which applies the E8M0 scales itself.
+ */
+int nvfp4_mxfp8_gemm(const void* a_codes, const void* a_scales, const void* w_codes,
+                     const void* w_scales, int64_t M, int64_t N, int64_t K, void* out_bf16,
+                     void* stream);
+
 /* Workspace bytes nvfp4_linear needs for an [M, K] activation (packed + scales, each
  * rounded up to 256 bytes). Returns 0 for invalid shapes. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);

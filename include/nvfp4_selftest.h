@@ -41,6 +41,13 @@ int nvfp4_selftest_division(unsigned long long* mismatches, uint32_t* first16, v
 int nvfp4_selftest_block_scale(const float* amax, float global_scale, uint8_t* codes, float* d,
                                int64_t n, void* stream);
 
+/* Every binary32 pattern except NaN and Inf, clamped to [-448, 448] as the MXFP8
+ * quantizer does: adds to *mismatches (device, starts at 0) the count where the gfx950 fp8
+ * conversion and the software E4M3 encoder (sign copied, nearest, ties to even) differ;
+ * up to 16 offending patterns land in first16 (device, 16 entries). */
+int nvfp4_selftest_mxfp8_e4m3_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                         void* stream);
+
 /* The GEMM's operand decode: packed[nbytes] holds 2*nbytes E2M1 codes (low nibble
  * first); scales[nbytes / 4] holds one E4M3 code per 4 packed bytes. Writes 2*nbytes
  * f16 bit patterns of code value * scale to hw_f16 (conversion-instruction decode) and

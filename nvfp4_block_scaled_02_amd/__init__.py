@@ -6,6 +6,7 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`gemm`      -- block-scaled W4A4 GEMM, bf16 output
 * :func:`linear`    -- fused quantize + GEMM through a workspace
 * :func:`gemm_w4a16` -- NVFP4 weights x bf16 activations (not quantized), bf16 output
+* :func:`mxfp8_quantize`, :func:`mxfp8_gemm` -- the MXFP8 (OCP microscaling) path
 * :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
 """
 from ._lib import NVFP4Error, load_library  # noqa: F401
@@ -17,6 +18,8 @@ from .ops import (  # noqa: F401
     global_scale_from_amax,
     linear,
     linear_workspace_bytes,
+    mxfp8_gemm,
+    mxfp8_quantize,
     quantize,
     workspace_views,
 )

@@ -37,6 +37,8 @@ SIGNATURES = {
     "nvfp4_quantize": (_int, [_vp, _i64, _i64, _f32, _vp, _vp, _vp]),
     "nvfp4_gemm": (_int, [_vp, _vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_mxfp8_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "nvfp4_mxfp8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_linear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_linear": (_int, [_vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp,
                             ctypes.c_size_t, _vp]),
@@ -45,6 +47,7 @@ SIGNATURES = {
     "nvfp4_selftest_e2m1_encode": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "nvfp4_selftest_e2m1_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_division": (_int, [_vp, _vp, _vp]),
+    "nvfp4_selftest_mxfp8_e4m3_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_block_scale": (_int, [_vp, _f32, _vp, _vp, _i64, _vp]),
     "nvfp4_selftest_decode": (_int, [_vp, _vp, _vp, _vp, _i64, _vp]),
 }

@@ -43,91 +43,6 @@ namespace nvfp4 {
 
 namespace {
 
-// Epilogue shared by the GEMM kernels: lane holds, for weight group i and activation
-// group g, output row m = m_base + 32g + (lane % 32) and columns
-// n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is scaled by
-// alpha in fp32, rounded to nearest even bf16 and stored (8 bytes per lane when the row
-// pitch allows). Only column quads q in [q0, q1) are stored.
-template <int FM, int FN>
-__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
-                                           int64_t m_base, int64_t n_base, int lane, int q0 = 0,
-                                           int q1 = 4) {
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-  const bool n_vec = (p.N & 3) == 0;
-#pragma unroll
-  for (int g = 0; g < FM; ++g) {
-    const int64_t m = m_base + g * 32 + r32;
-    if (m >= p.M) continue;
-    uint16_t* orow = p.out + m * p.N;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q < q0 || q >= q1) continue;
-        const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
-        if (n_vec && n + 3 < p.N) {
-          *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
-        }
-      }
-    }
-  }
-}
-
-// The same stores through LDS: one 32-row group of the wave's blocks at a time is
-// written, rounded, into the wave's own LDS area `blk` (32 x FN*32 bf16, row-major) and
-// read back as 16-byte row pieces, so each store instruction writes whole row segments
-// (FN*64 bytes per row) instead of 16-byte pieces of 32 rows. `blk` must not be used by
-// other waves; LDS order within the wave makes the round trip safe without a barrier.
-template <int FM, int FN>
-__device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
-                                               int64_t m_base, int64_t n_base, int lane,
-                                               uint16_t* blk) {
-  constexpr int W = FN * 32;          // columns of the wave's blocks
-  constexpr int kPieces = 32 * W / 8;  // 16-byte pieces per 32-row group
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-  const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
-#pragma unroll
-  for (int g = 0; g < FM; ++g) {
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
-        *(u32x2*)&blk[r32 * W + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-      }
-    const int64_t m_row = m_base + g * 32;
-#pragma unroll
-    for (int it = 0; it < (kPieces + 63) / 64; ++it) {
-      const int c = it * 64 + lane;
-      if (c < kPieces) {
-        const int r = c / (W / 8), col = (c % (W / 8)) * 8;
-        const int64_t m = m_row + r, n = n_base + col;
-        if (m < p.M) {
-          const u32x4 v = *(const u32x4*)&blk[r * W + col];
-          if (n_vec && n + 7 < p.N) {
-            *(u32x4*)&p.out[m * p.N + n] = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < p.N) p.out[m * p.N + n + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    }
-  }
-}
-
 template <int BM, int BN, int KC>
 struct alignas(16) GemmSmem {
   uint8_t x[2][KC][BM * 32];   // activations, fragment order
@@ -366,7 +281,6 @@ struct alignas(16) GemmSmem3 {
 };
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
 
 // One direct-to-LDS load per lane: 16 (or 4) bytes from src to lds_base + lane * 16 (4).
 __device__ __forceinline__ void dma_load16(const void* src, void* lds_base) {
@@ -568,64 +482,22 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
 // group, 64 slots of 16 bytes in MFMA lane order; scale bytes as 32-bit words [row][chunk].
 template <int BM, int BN>
 struct alignas(16) GemmSmemFit {
-  uint8_t x[3][2][BM * 32];  // activations: [stage buffer][chunk][fragment order]
-  uint8_t w[3][2][BN * 32];  // weights
-  uint32_t xs[3][BM * 2];    // scale words: [row][chunk], 4 scale bytes per word
-  uint32_t ws[3][BN * 2];
+  uint8_t x[4][2][BM * 32];  // activations: [stage buffer][chunk][fragment order]
+  uint8_t w[4][2][BN * 32];  // weights
+  uint32_t xs[4][BM * 2];    // scale words: [row][chunk], 4 scale bytes per word
+  uint32_t ws[4][BN * 2];
 };
-
-// Wait until at most n of this wave's vector memory operations are outstanding (n < 16;
-// expcnt and lgkmcnt left free). Loads complete in issue order.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
-}
-
-// Direct-to-LDS buffer loads: each lane reads 16 (4) bytes at voff + soff and writes
-// them to lds_base + lane * 16 (4).
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
-                                                  uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 16, (int)voff, (int)soff, 0, 0);
-}
-__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void* lds_base,
-                                                 uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 4, (int)voff, (int)soff, 0, 0);
-}
-
-#ifndef NVFP4_GEMM_XCD_GROUP
-#define NVFP4_GEMM_XCD_GROUP 4
-#endif
-// Workgroup -> tile. Consecutive workgroups go to the 8 XCDs in turn and each XCD has its
-// own L2, so workgroup b takes tile (b % 8) * (T / 8) + b / 8 of an order in which each
-// XCD's share is contiguous; that order walks groups of G tile rows column by column, so
-// an XCD's tiles share few activation and weight rows. (T % 8 != 0: plain order.)
-__device__ __forceinline__ void tile_order(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcd = 8, G = NVFP4_GEMM_XCD_GROUP;
-  const int T = tiles_m * tiles_n;
-  if (G <= 0 || T % kXcd != 0) {
-    tm = b / tiles_n;
-    tn = b % tiles_n;
-    return;
-  }
-  const int q = (b % kXcd) * (T / kXcd) + b / kXcd;
-  const int per_group = G * tiles_n;
-  const int gm0 = (q / per_group) * G;
-  const int rows = min(tiles_m - gm0, G);
-  const int r = q % per_group;
-  tm = gm0 + r % rows;
-  tn = r / rows;
-}
 
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
 // (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
 //
-// Stage t lives in LDS buffer t % 3; its loads are issued during stage t-2, spread over
-// the first k-steps. At the end of stage t each wave waits until its loads for stage t+1
-// have landed (those for t+2 stay in flight) and the workgroup meets at a barrier; by then
-// every wave has consumed its LDS reads of stage t, whose buffer the loads issued during
-// stage t+1 overwrite. The first chunk of stage t+1 is read and its first k-step decoded
-// during the second chunk of stage t.
+// Stage t lives in LDS buffer t % 4; its loads are issued during stage t-3, spread over
+// the first k-steps. At the end of stage t each wave waits until every load it issued
+// before stage t has landed (stages up to t+2; those for t+3 stay in flight) and the
+// workgroup meets at a barrier. So stage t+1 is complete in LDS throughout stage t, whose
+// second chunk reads stage t+1's first chunk and decodes its first k-step; and by the
+// barrier every wave has consumed its reads of stage t, whose buffer the loads issued
+// during stage t+1 overwrite.
 template <int BM, int BN>
 __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int NW = 4;
@@ -759,11 +631,13 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     if (par == 0) sf[slot] = decode8<true>(sraw[j], j < 2 ? ssc.xx : ssc.yy);
   };
 
-  // prologue: stages 0 and 1 into buffers 0 and 1
+  // prologue: stages 0, 1 and 2 into buffers 0, 1 and 2
 #pragma unroll
   for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : 0, 1);
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   read_chunk(0, 0, wave_m);
@@ -771,9 +645,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 
   int buf = 0;
   for (int t = 0; t < nk; ++t) {
-    const int nbuf = buf == 2 ? 0 : buf + 1;    // stage t + 1
-    const int lbuf = nbuf == 2 ? 0 : nbuf + 1;  // stage t + 2
-    const int lstage = t + 2 < nk ? t + 2 : nk - 1;
+    const int nbuf = (buf + 1) & 3;  // stage t + 1 (complete since the end of stage t - 2)
+    const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
+    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;

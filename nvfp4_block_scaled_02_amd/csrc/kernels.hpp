@@ -36,6 +36,14 @@ struct W4A16Problem {
 
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev);
 
+// MXFP8: codes/scales use GemmProblem's a_packed/a_scales/w_packed/w_scales (one byte
+// per element, one E8M0 byte per 32 elements); alpha is 1.
+hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
+                              hipStream_t stream, const LaunchInfo& dev);
+hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
+hipError_t launch_mx_selftest_e4m3_exhaustive(unsigned long long* count, uint32_t* first,
+                                              hipStream_t stream);
+
 hipError_t launch_amax(const void* x, int64_t n, float* out, hipStream_t stream,
                        const LaunchInfo& dev);
 

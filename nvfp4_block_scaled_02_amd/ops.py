@@ -103,6 +103,47 @@ def gemm_w4a16(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
     return out
 
 
+def mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor | None = None,
+                   scales: torch.Tensor | None = None, stream=None):
+    """MXFP8 quantization: bf16 [M, K] -> E4M3 codes uint8 [M, K] + E8M0 scales [M, K/32]."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    if tuple(codes.shape) != (M, K) or tuple(scales.shape) != (M, K // 32):
+        raise ValueError("codes must be [M, K] and scales [M, K/32]")
+    lib = load_library()
+    check(lib.nvfp4_mxfp8_quantize(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream)),
+          "nvfp4_mxfp8_quantize")
+    return codes, scales
+
+
+def mxfp8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+               w_scales: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """MXFP8 GEMM: bf16 [M, N] = A_hat @ W_hat^T on the block-scaled fp8 MFMA."""
+    for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"),
+                 (w_scales, "w_scales")):
+        _need(t, n, torch.uint8, 2)
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    if tuple(w_codes.shape) != (N, K) or tuple(a_scales.shape) != (M, K // 32) or \
+            tuple(w_scales.shape) != (N, K // 32):
+        raise ValueError("operand shapes are inconsistent")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape must be [M, N]")
+    lib = load_library()
+    check(lib.nvfp4_mxfp8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
+                               M, N, K, _ptr(out), _stream(stream)), "nvfp4_mxfp8_gemm")
+    return out
+
+
 def linear_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().nvfp4_linear_workspace_bytes(M, K))
 

@@ -128,6 +128,35 @@ def test_gemm_w4a16_validation(lib):
     assert call({5: 0}) == L.SUCCESS
 
 
+def test_mxfp8_validation(lib):
+    q = lib.nvfp4_mxfp8_quantize
+    assert q(NULL, 4, 64, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 48, P16, P16b, NULL) == L.INVALID_SHAPE   # K % 32 != 0
+    assert q(P16, -1, 64, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(ODD, 4, 64, P16, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 4, 64, ODD, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 0, 64, P16, P16b, NULL) == L.SUCCESS
+    g = lib.nvfp4_mxfp8_gemm
+    args = [P16, P16b, P16, P16b, 8, 8, 128, P16, NULL]
+
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return g(*a)
+
+    assert call({0: NULL}) == L.INVALID_VALUE
+    assert call({3: NULL}) == L.INVALID_VALUE
+    assert call({6: 64}) == L.INVALID_SHAPE       # K % 128 != 0
+    assert call({6: 0}) == L.INVALID_SHAPE
+    assert call({4: 2**23, 6: 256}) == L.INVALID_SHAPE  # 32-bit offsets exceeded
+    assert call({0: ODD}) == L.MISALIGNED
+    assert call({1: ctypes.c_void_p(0x20002)}) == L.MISALIGNED
+    assert call({7: ODD}) == L.MISALIGNED
+    assert call({4: 0}) == L.SUCCESS
+    assert call({5: 0}) == L.SUCCESS
+
+
 def test_linear_validation_and_workspace(lib):
     ws = lib.nvfp4_linear_workspace_bytes
     assert ws(4608, 3072) == (4608 * 3072 // 2) + ((4608 * 3072 // 16 + 255) // 256 * 256)
