@@ -458,9 +458,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
 
   // every load has landed and every wave is past its last LDS read (the loop ends with
   // a full wait and a barrier), so the stage buffers can stage the stores
-  static_assert(NW * 32 * FN * 32 * 2 <= sizeof(sm.x), "store staging fits");
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
   store_tile_lds<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
-                         (uint16_t*)&sm.x[0][0][0] + wave * 32 * FN * 32);
+                         (uint16_t*)&sm.x[0][0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- fit-tile path: 288 x 192 tiles ------------------------------------------------------
@@ -703,9 +703,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     for (int v = 0; v < 16; ++v) accs[i][v] += xch[(((wave ^ 2) * FN + i) * 16 + v) * 64 + lane];
 
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
-  static_assert(NW * 32 * FN * 32 * 2 <= sizeof(sm.w), "store staging fits");
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.w), "store staging fits");
   store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane,
-                         (uint16_t*)&sm.w[0][0][0] + wave * 32 * FN * 32);
+                         (uint16_t*)&sm.w[0][0][0] + wave * 32 * kStoreRowPad(FN));
   // group GS: wave m = 0 stores column quads 0-1 of every block, m = 1 quads 2-3
   store_tile<1, FN>(*(const floatx16(*)[FN][1])&accs, p, (int64_t)m0 + GS * 32, n_base, lane,
                     wave_m * 2, wave_m * 2 + 2);

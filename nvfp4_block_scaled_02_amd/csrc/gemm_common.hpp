@@ -112,16 +112,21 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
 }
 
 // The same stores through LDS: one 32-row group of the wave's blocks at a time is
-// written, rounded, into the wave's own LDS area `blk` (32 x FN*32 bf16, row-major) and
-// read back as 16-byte row pieces, so each store instruction writes whole row segments
-// (FN*64 bytes per row) instead of 16-byte pieces of 32 rows. `blk` must not be used by
-// other waves; LDS order within the wave makes the round trip safe without a barrier.
+// written, rounded, into the wave's own LDS area `blk` (32 rows of FN*32 bf16, rows
+// kStoreRowPad(FN) elements apart) and read back as 16-byte row pieces, so each store
+// instruction writes whole row segments (FN*64 bytes per row) instead of 16-byte pieces
+// of 32 rows. The 16-byte row padding puts the 32 rows a lane group writes at once in
+// different LDS banks. `blk` must not be used by other waves; LDS order within the wave
+// makes the round trip safe without a barrier.
+constexpr int kStoreRowPad(int fn) { return fn * 32 + 8; }
+
 template <int FM, int FN>
 __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
                                                int64_t m_base, int64_t n_base, int lane,
                                                uint16_t* blk) {
-  constexpr int W = FN * 32;          // columns of the wave's blocks
-  constexpr int kPieces = 32 * W / 8;  // 16-byte pieces per 32-row group
+  constexpr int W = FN * 32;            // columns of the wave's blocks
+  constexpr int RS = kStoreRowPad(FN);  // row stride in the staging area
+  constexpr int kPieces = 32 * W / 8;   // 16-byte pieces per 32-row group
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
@@ -134,7 +139,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
         uint32_t b[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
-        *(u32x2*)&blk[r32 * W + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
       }
     const int64_t m_row = m_base + g * 32;
 #pragma unroll
@@ -144,7 +149,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
         const int r = c / (W / 8), col = (c % (W / 8)) * 8;
         const int64_t m = m_row + r, n = n_base + col;
         if (m < p.M) {
-          const u32x4 v = *(const u32x4*)&blk[r * W + col];
+          const u32x4 v = *(const u32x4*)&blk[r * RS + col];
           if (n_vec && n + 7 < p.N) {
             *(u32x4*)&p.out[m * p.N + n] = v;
           } else {

@@ -99,21 +99,33 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
 // the second block in bytes 16-31; byte 0 of its scale register is the E8M0 scale of row
 // r, block h. Both operands use this mapping.
 //
-// Stage (64 elements of K) layout in LDS: per 32-row group, two 1 KiB pieces (block
-// half 0 and 1) of 64 lane slots of 16 bytes, so a lane reads its fragment with two
-// conflict-free 16-byte reads; per row, the 32-bit word of the 4 scale bytes (128
-// elements) that contains the stage's two. Four stage buffers; loads (direct-to-LDS
-// buffer loads, rows past M or N read as zero) are issued three stages ahead; at the end
-// of stage t each wave waits for every load it issued before stage t (stage t+3's stay
-// in flight) and the workgroup meets at a barrier, so stage t+1, whose fragments are read
-// during stage t, is always complete.
+// Loads. The direct-to-LDS path costs by the cache lines an instruction touches rather
+// than by its bytes, so every load reads whole 64-byte row segments: a code load takes
+// 16 rows x the stage's 64 bytes (4 lanes per row), a scale load 64 rows x 16 bytes (the
+// scales of 512 elements, 8 stages), issued once every 8 stages. Rows past M or N read as
+// zero (buffer range checks).
+//
+// Stage (64 elements of K) layout in LDS: each 16-row piece is 1 KiB, row r's 64 bytes at
+// 64 r, its 16-byte chunk c stored at slot c ^ mx_swz(r) so that the fragment reads (two
+// 16-byte reads per lane and block, chunks h and h + 2 of row r) hit distinct banks. Four
+// code buffers, filled three stages ahead; two scale buffers of 8 stages, filled 8 stages
+// ahead. At the end of stage t each wave waits for every load it issued before stage t
+// and the workgroup meets at a barrier, so stage t+1, whose fragments are read during
+// stage t, is always complete.
+//
+// Each stage issues its MFMAs, loads and LDS reads in one fixed interleaved order (one
+// load and one or two reads after each MFMA) so that the matrix core never waits behind a
+// burst of memory instructions.
 template <int BM, int BN>
 struct alignas(16) MxSmem {
   uint8_t x[4][BM * 64];
   uint8_t w[4][BN * 64];
-  uint32_t xs[4][BM];
-  uint32_t ws[4][BN];
+  uint8_t xs[2][BM * 16];
+  uint8_t ws[2][BN * 16];
 };
+
+// chunk swizzle of a 64-byte LDS row by its index r (0..15) within its 1 KiB piece
+__device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
@@ -125,12 +137,16 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   __shared__ MxSmem<BM, BN> sm;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int kPa = 2 * BM / 32, kPw = 2 * BN / 32, kSa = BM / 64, kSw = BN / 64;
+  constexpr int kPa = BM / 16, kPw = BN / 16;  // 1 KiB code pieces per stage
+  constexpr int kSa = BM / 64, kSw = BN / 64;  // 1 KiB scale pieces per 8 stages
   static_assert(kPa % NW == 0 && kPw % NW == 0 && kSa % NW == 0 && kSw % NW == 0,
                 "loads divide evenly among waves");
-  constexpr int kPaW = kPa / NW, kPwW = kPw / NW, kSaW = kSa / NW, kSwW = kSw / NW;
-  constexpr int kLoadsPerWave = kPaW + kPwW + kSaW + kSwW;
-  static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
+  constexpr int kPaW = kPa / NW, kPwW = kPw / NW;
+  constexpr int kLoads = kPaW + kPwW;          // code loads per wave per stage
+  constexpr int kSLoads = (kSa + kSw) / NW;    // scale loads per wave per 8 stages
+  constexpr int kMfma = FN * FM;
+  static_assert(kLoads + kSLoads <= kMfma, "at most one load after each MFMA");
+  static_assert(kLoads + kSLoads < 64, "one stage of loads fits the vmcnt counter");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,35 +162,41 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
   const int nk = (int)(p.K / 64);
-  const uint32_t pitch = (uint32_t)p.K;        // code bytes per row
+  const int ngrp = (nk + 7) >> 3;                 // groups of 8 stages
+  const uint32_t pitch = (uint32_t)p.K;          // code bytes per row
   const uint32_t spitch = (uint32_t)(p.K >> 5);  // scale bytes per row
 
   const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
   const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const uint32_t voff_p = r32 * pitch + h * 16;
+  const int lr = lane >> 2;  // row of a code piece this lane loads
+  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ mx_swz(lr));
   const uint32_t voff_s = lane * spitch;
 
-  // Load j of this wave for `stage` into buffer `buf` (lists: packed x, packed w,
-  // scales x, scales w; wave w takes entries j' * NW + w of each).
-  auto issue = [&](int j, int stage, int buf) {
+  // Code load j of this wave for `stage` into buffer `buf`: piece j * NW + wave of the
+  // list (x pieces, then w pieces).
+  auto issue_codes = [&](int j, int stage, int buf) {
     if (j < kPaW) {
-      const int i = j * NW + wave, g = i >> 1, pc = i & 1;
-      buffer_load_lds16(rxp, &sm.x[buf][g * 2048 + pc * 1024], voff_p,
-                        (uint32_t)(m0 + 32 * g) * pitch + (uint32_t)stage * 64 + pc * 32);
-    } else if (j < kPaW + kPwW) {
-      const int i = (j - kPaW) * NW + wave, g = i >> 1, pc = i & 1;
-      buffer_load_lds16(rwp, &sm.w[buf][g * 2048 + pc * 1024], voff_p,
-                        (uint32_t)(n0 + 32 * g) * pitch + (uint32_t)stage * 64 + pc * 32);
-    } else if (j < kPaW + kPwW + kSaW) {
-      const int g = (j - kPaW - kPwW) * NW + wave;
-      buffer_load_lds4(rxs, &sm.xs[buf][g * 64], voff_s,
-                       (uint32_t)(m0 + 64 * g) * spitch + (uint32_t)(stage >> 1) * 4);
+      const int i = j * NW + wave;
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_c,
+                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
     } else {
-      const int g = (j - kPaW - kPwW - kSaW) * NW + wave;
-      buffer_load_lds4(rws, &sm.ws[buf][g * 64], voff_s,
-                       (uint32_t)(n0 + 64 * g) * spitch + (uint32_t)(stage >> 1) * 4);
+      const int i = (j - kPaW) * NW + wave;
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_c,
+                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+    }
+  };
+  // Scale load j of this wave for stage group `grp` into scale buffer `sbuf`.
+  auto issue_scales = [&](int j, int grp, int sbuf) {
+    if (j < kSa / NW) {
+      const int i = j * NW + wave;
+      buffer_load_lds16(rxs, &sm.xs[sbuf][i * 1024], voff_s,
+                        (uint32_t)(m0 + 64 * i) * spitch + (uint32_t)grp * 16);
+    } else {
+      const int i = (j - kSa / NW) * NW + wave;
+      buffer_load_lds16(rws, &sm.ws[sbuf][i * 1024], voff_s,
+                        (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)grp * 16);
     }
   };
 
@@ -189,78 +211,102 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   // fragments and scale bytes of two stages (by parity)
   v8i_t wf[2][FN], xf[2][FM];
   int wsc[2][FN], xsc[2][FM];
-  const int wfrag = wave_n * FN * 2048 + lane * 16;
-  const int xfrag = wave_m * FM * 2048 + lane * 16;
-  auto read_stage = [&](int par, int buf, int stage) {
-    const int sb = (stage & 1) * 2 + h;  // byte of the scale word: block h of this stage
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const u32x4 a = *(const u32x4*)&sm.w[buf][wfrag + i * 2048];
-      const u32x4 b = *(const u32x4*)&sm.w[buf][wfrag + i * 2048 + 1024];
-      wf[par][i] = v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-      wsc[par][i] = ((const uint8_t*)sm.ws[buf])[(wave_n * WTN + i * 32 + r32) * 4 + sb];
-    }
-#pragma unroll
-    for (int g = 0; g < FM; ++g) {
-      const u32x4 a = *(const u32x4*)&sm.x[buf][xfrag + g * 2048];
-      const u32x4 b = *(const u32x4*)&sm.x[buf][xfrag + g * 2048 + 1024];
-      xf[par][g] = v8i_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-      xsc[par][g] = ((const uint8_t*)sm.xs[buf])[(wave_m * WTM + g * 32 + r32) * 4 + sb];
+  // lane's first 16-byte chunk within a 32-row group (2 KiB); the second is 32 bytes over
+  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ mx_swz(r32 & 15));
+  const int fr1 = fr0 ^ 32;
+  // LDS reads of one stage in the order its MFMAs need them: w0, x0..x(FM-1), w1, ...
+  // Read k (of kReads) is a fragment half or a scale byte.
+  constexpr int kReads = 3 * (FN + FM);
+  auto read_one = [&](int k, int par, int buf, int stage) {
+    const int sbuf = (stage >> 3) & 1;
+    const int sbyte = (stage & 7) * 2 + h;
+    const int f = k / 3, part = k % 3;  // operand fragment f: w0, x0, x1, .., w1, w2, ..
+    const bool is_w = f == 0 || f > FM;
+    const int idx = f == 0 ? 0 : (f <= FM ? f - 1 : f - FM);
+    if (is_w) {
+      const uint8_t* base = &sm.w[buf][(wave_n * FN + idx) * 2048];
+      if (part == 0) {
+        const u32x4 a = *(const u32x4*)&base[fr0];
+        wf[par][idx][0] = (int)a.x; wf[par][idx][1] = (int)a.y; wf[par][idx][2] = (int)a.z; wf[par][idx][3] = (int)a.w;
+      } else if (part == 1) {
+        const u32x4 b = *(const u32x4*)&base[fr1];
+        wf[par][idx][4] = (int)b.x; wf[par][idx][5] = (int)b.y; wf[par][idx][6] = (int)b.z; wf[par][idx][7] = (int)b.w;
+      } else {
+        wsc[par][idx] = sm.ws[sbuf][(wave_n * WTN + idx * 32 + r32) * 16 + sbyte];
+      }
+    } else {
+      const uint8_t* base = &sm.x[buf][(wave_m * FM + idx) * 2048];
+      if (part == 0) {
+        const u32x4 a = *(const u32x4*)&base[fr0];
+        xf[par][idx][0] = (int)a.x; xf[par][idx][1] = (int)a.y; xf[par][idx][2] = (int)a.z; xf[par][idx][3] = (int)a.w;
+      } else if (part == 1) {
+        const u32x4 b = *(const u32x4*)&base[fr1];
+        xf[par][idx][4] = (int)b.x; xf[par][idx][5] = (int)b.y; xf[par][idx][6] = (int)b.z; xf[par][idx][7] = (int)b.w;
+      } else {
+        xsc[par][idx] = sm.xs[sbuf][(wave_m * WTM + idx * 32 + r32) * 16 + sbyte];
+      }
     }
   };
 
-  // prologue: stages 0, 1 and 2 into buffers 0, 1 and 2, then read stage 0
+  // prologue: scales of stages 0-7, codes of stages 0, 1 and 2, then read stage 0
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
+  for (int j = 0; j < kSLoads; ++j) issue_scales(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1);
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2);
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 1 ? 1 : nk - 1, 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 2 ? 2 : nk - 1, 2);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  read_stage(0, 0, 0);
+#pragma unroll
+  for (int k = 0; k < kReads; ++k) read_one(k, 0, 0, 0);
 
-  constexpr int kMfma = FN * FM;
-  constexpr int kReads = 3 * (FN + FM);
-  // One stage; `cur` (the register set of stage t's fragments) must be a constant, so
-  // the loop below runs two stages per iteration.
-  auto stage = [&](int t, int buf, const int cur) {
+  // One stage. `cur` (the register set of stage t's fragments) and `sload` (t % 8 == 0
+  // and a later stage group exists: load its scales into the other scale buffer) must be
+  // constants, so that the stage is one basic block whose order the scheduling barriers
+  // fix; the main loop runs 8 stages per iteration.
+  auto stage = [&](int t, int buf, const int cur, const bool sload) {
     const int nbuf = (buf + 1) & 3;  // stage t + 1
     const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
     const int lstage = t + 3 < nk ? t + 3 : nk - 1;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) issue(j, lstage, lbuf);
-    read_stage(cur ^ 1, nbuf, t + 1 < nk ? t + 1 : t);
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int g = 0; g < FM; ++g)
-        acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, wsc[cur][i], 0, xsc[cur][g]);
+    const int rstage = t + 1 < nk ? t + 1 : t;
+    const int sgrp = (t >> 3) + 1 < ngrp ? (t >> 3) + 1 : ngrp - 1;
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (q < kLoadsPerWave) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
-      if (q * 2 < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (fragment moves)
+      const int i = q / FM, g = q % FM;
+      acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, wsc[cur][i], 0, xsc[cur][g]);
+      if (q < kLoads) issue_codes(q, lstage, lbuf);
+      else if (q < kLoads + kSLoads && sload) issue_scales(q - kLoads, sgrp, ((t >> 3) + 1) & 1);
+#pragma unroll
+      for (int k = q * kReads / kMfma; k < (q + 1) * kReads / kMfma; ++k) read_one(k, cur ^ 1, nbuf, rstage);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kLoadsPerWave>();
+    if (sload) wait_vmcnt<kLoads + kSLoads>();
+    else wait_vmcnt<kLoads>();
     __builtin_amdgcn_s_barrier();
   };
-  int buf = 0;
-  for (int t = 0; t < nk; t += 2) {  // nk is even (K % 128 == 0)
-    stage(t, buf, 0);
-    stage(t + 1, (buf + 1) & 3, 1);
-    buf = (buf + 2) & 3;
+  // 8 stages per iteration (the code buffers cycle back to 0), then the last nk % 8
+  // stages two at a time (nk is even: K % 128 == 0); their scales were loaded with the
+  // group before, so they load none.
+  int t = 0;
+  for (; t + 8 <= nk; t += 8) {
+    stage(t, 0, 0, true);
+#pragma unroll
+    for (int u = 1; u < 8; ++u) stage(t + u, u & 3, u & 1, false);
+  }
+  for (; t < nk; t += 2) {
+    stage(t, t & 3, 0, false);
+    stage(t + 1, (t + 1) & 3, 1, false);
   }
 
   // drain the last (unused) loads before the stage buffers stage the stores
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  static_assert(NW * 32 * FN * 32 * 2 <= sizeof(sm.x), "store staging fits");
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
   store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN, lane,
-                         (uint16_t*)&sm.x[0][0] + wave * 32 * FN * 32);
+                         (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- self-test: the fp8 conversion against the software E4M3 encoder ----------------
