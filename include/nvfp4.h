@@ -105,6 +105,24 @@ int nvfp4_gemm(const void* a_packed, const void* a_scales, float a_global_scale,
                const void* w_packed, const void* w_scales, float w_global_scale,
                int64_t M, int64_t N, int64_t K, void* out_bf16, void* stream);
 
+/* Kernels nvfp4_gemm chooses among (reported by nvfp4_gemm_plan). */
+typedef enum {
+  NVFP4_GEMM_TILE256 = 0, /* 256 x 256 output tiles, direct-to-LDS loads (K % 128 == 0) */
+  NVFP4_GEMM_FIT = 1,     /* 288 x 192 output tiles (K % 128 == 0): 4608-row activations
+                             and FLUX widths split into whole multiples of 256 tiles */
+  NVFP4_GEMM_SPLITK = 2,  /* K split over a workgroup's waves: short activations */
+  NVFP4_GEMM_GENERIC = 3  /* 256 x 256 tiles, register-staged loads: any K % 16 == 0 */
+} nvfp4_gemm_kernel;
+
+/*
+ * The kernel nvfp4_gemm launches for an M x N x K product on a device with num_cus
+ * compute units (<= 0: 256, an MI355X), given 16-byte aligned packed operands and 4-byte
+ * aligned scales. Host only: no device call. Writes an nvfp4_gemm_kernel value to
+ * *kernel; returns NVFP4_ERROR_INVALID_VALUE for a null kernel pointer and
+ * NVFP4_ERROR_INVALID_SHAPE for shapes nvfp4_gemm rejects.
+ */
+int nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel);
+
 /*
  * W4A16 GEMM: NVFP4 weights, bf16 activations left unquantized, the pages' path for
  * hardware without the fused FP4 kernel ("BFL (fp8r / nvfp4)", text under the Kernels

@@ -5,6 +5,7 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`quantize`  -- bf16 [M, K] -> packed E2M1 [M, K/2] + E4M3 scales [M, K/16]
 * :func:`gemm`      -- block-scaled W4A4 GEMM, bf16 output
 * :func:`linear`    -- fused quantize + GEMM through a workspace
+* :func:`gemm_plan` -- which GEMM kernel a shape runs on (host only)
 * :func:`gemm_w4a16` -- NVFP4 weights x bf16 activations (not quantized), bf16 output
 * :func:`mxfp8_quantize`, :func:`mxfp8_gemm` -- the MXFP8 (OCP microscaling) path
 * :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
@@ -14,6 +15,7 @@ from .ops import (  # noqa: F401
     amax,
     calibrate,
     gemm,
+    gemm_plan,
     gemm_w4a16,
     global_scale_from_amax,
     linear,

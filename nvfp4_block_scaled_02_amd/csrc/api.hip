@@ -147,6 +147,17 @@ int nvfp4_gemm(const void* ap, const void* as, float ags, const void* wp, const 
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
+int nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel) {
+  if (!kernel) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  *kernel = nvfp4::plan_gemm(M, N, K, true, num_cus).kernel;
+  return NVFP4_SUCCESS;
+}
+
 int nvfp4_gemm_w4a16(const void* x, const void* wp, const void* ws, float wgs, int64_t M,
                      int64_t N, int64_t K, void* out, void* stream) {
   if (!x || !wp || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;

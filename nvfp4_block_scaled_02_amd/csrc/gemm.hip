@@ -478,14 +478,21 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
 // one program: 13.5 blocks of work per wave and k-step on average. At the end the two
 // partial sums of group 4 meet in LDS.
 //
-// LDS image of a stage (same fragment order as the 256x256 kernel): per chunk and 32-row
-// group, 64 slots of 16 bytes in MFMA lane order; scale bytes as 32-bit words [row][chunk].
+// Loads. The direct-to-LDS path costs by the cache lines an instruction touches rather
+// than by its bytes, so a code load reads whole 64-byte row segments (16 rows x the
+// stage's 64 bytes, 4 lanes per row) and a scale load 64 rows x 16 bytes (the scales of
+// two stages).
+//
+// LDS image of a stage: per 16-row piece 1 KiB, row r's 64 bytes (chunk 0, then chunk 1)
+// at 64 r, its 16-byte pieces q = 2 * chunk + half swizzled to slot q ^ chunk_swz(r).
+// Scales: 16 bytes per row for a pair of stages, activation rows (rounded up to whole
+// 64-row pieces) first, then weight rows; three pair buffers.
 template <int BM, int BN>
 struct alignas(16) GemmSmemFit {
-  uint8_t x[4][2][BM * 32];  // activations: [stage buffer][chunk][fragment order]
-  uint8_t w[4][2][BN * 32];  // weights
-  uint32_t xs[4][BM * 2];    // scale words: [row][chunk], 4 scale bytes per word
-  uint32_t ws[4][BN * 2];
+  static constexpr int kScaleRowsX = (BM + 63) / 64 * 64;
+  uint8_t x[4][BM * 64];  // activations: [stage buffer][16-row piece]
+  uint8_t w[4][BN * 64];  // weights
+  uint8_t sc[3][(kScaleRowsX + BN) * 16];  // scale bytes: [pair buffer][row][16]
 };
 
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
@@ -497,7 +504,10 @@ struct alignas(16) GemmSmemFit {
 // workgroup meets at a barrier. So stage t+1 is complete in LDS throughout stage t, whose
 // second chunk reads stage t+1's first chunk and decodes its first k-step; and by the
 // barrier every wave has consumed its reads of stage t, whose buffer the loads issued
-// during stage t+1 overwrite.
+// during stage t+1 overwrite. The scales of stage pair u (stages 2u, 2u+1) live in pair
+// buffer u % 3 and are loaded during stages 2u-4 and 2u-3 (one load per wave each), so
+// they are complete before stage 2u-1 first reads them, and their buffer's previous pair
+// was last read in stage 2u-5.
 template <int BM, int BN>
 __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int NW = 4;
@@ -510,15 +520,17 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int kSteps = 8;   // 16-element k-steps per stage (two chunks of 4)
   __shared__ GemmSmemFit<BM, BN> sm;
 
-  // Loads per stage: one 16-byte load per lane fills a (chunk, 32-row group) piece of 1 KB;
-  // one 4-byte load per lane fills the scale words of 32 rows. Four lists (packed x, packed
-  // w, scales x, scales w); wave w takes entries j * NW + w of each. Every wave issues the
-  // same number of loads, so the vmcnt wait counts the same; entries past a list repeat
-  // its last one, which writes the same bytes to the same place.
-  constexpr int kPa = 2 * GX, kPw = 2 * GW, kSa = GX, kSw = GW;
+  // Loads per stage: one 16-byte load per lane fills a 16-row code piece of 1 KiB. Two
+  // lists (packed x, packed w); wave w takes entries j * NW + w of each. Every wave issues
+  // the same number of loads, so the vmcnt wait counts the same; entries past a list
+  // repeat its last one, which writes the same bytes to the same place. Plus one scale
+  // load per wave: a pair's 2 * NW scale pieces (64 rows x 16 bytes) over its two stages.
+  constexpr int kPa = BM / 16, kPw = BN / 16;
   constexpr int kPaW = (kPa + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW;
-  constexpr int kSaW = (kSa + NW - 1) / NW, kSwW = (kSw + NW - 1) / NW;
-  constexpr int kLoadsPerWave = kPaW + kPwW + kSaW + kSwW;
+  constexpr int kRowsSx = GemmSmemFit<BM, BN>::kScaleRowsX;
+  constexpr int kSx = kRowsSx / 64;
+  static_assert(BN % 64 == 0 && kSx + BN / 64 == 2 * NW, "one scale load per wave and stage");
+  constexpr int kLoadsPerWave = kPaW + kPwW + 1;
   static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
   constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
 
@@ -536,6 +548,7 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
   const int nk = (int)(p.K / 128);
+  const int npair = (nk + 1) >> 1;
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
@@ -545,28 +558,31 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const uint32_t voff_p = r32 * pitch + h * 16;                   // 32 rows x 32 bytes
-  const uint32_t voff_s = (lane >> 1) * spitch + (lane & 1) * 4;  // 32 rows x 8 bytes
+  const int lr = lane >> 2;  // row of a code piece this lane loads
+  const uint32_t voff_p = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
+  const uint32_t voff_s = lane * spitch;
 
-  auto issue = [&](int j, int stage, int buf) {
+  // Scale piece `half` * NW + wave of stage pair `pair` into pair buffer `sb`; pieces below
+  // kSx hold activation rows, the rest weight rows (selects, no branch).
+  auto issue_scale = [&](int pair, int half, int sb) {
+    const int i = half * NW + wave;
+    const bool isx = i < kSx;
+    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024], voff_s, row * spitch + (uint32_t)pair * 16);
+  };
+  // Load j of this wave in stage t: code pieces of stage `stage` into buffer `buf`, the
+  // last one the stage's scale piece (pair `spair` into pair buffer `sb`).
+  auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
     if (j < kPaW) {
       const int i = min(j * NW + wave, kPa - 1);
-      const int c = i / GX, g = i % GX;
-      buffer_load_lds16(rxp, &sm.x[buf][c][g * 1024], voff_p,
-                        (uint32_t)(m0 + g * 32) * pitch + (uint32_t)stage * 64 + c * 32);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_p,
+                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
     } else if (j < kPaW + kPwW) {
       const int i = min((j - kPaW) * NW + wave, kPw - 1);
-      const int c = i / GW, g = i % GW;
-      buffer_load_lds16(rwp, &sm.w[buf][c][g * 1024], voff_p,
-                        (uint32_t)(n0 + g * 32) * pitch + (uint32_t)stage * 64 + c * 32);
-    } else if (j < kPaW + kPwW + kSaW) {
-      const int g = min((j - kPaW - kPwW) * NW + wave, kSa - 1);
-      buffer_load_lds4(rxs, &sm.xs[buf][g * 64], voff_s,
-                       (uint32_t)(m0 + g * 32) * spitch + (uint32_t)stage * 8);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_p,
+                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
     } else {
-      const int g = min((j - kPaW - kPwW - kSaW) * NW + wave, kSw - 1);
-      buffer_load_lds4(rws, &sm.ws[buf][g * 64], voff_s,
-                       (uint32_t)(n0 + g * 32) * spitch + (uint32_t)stage * 8);
+      issue_scale(spair, t & 1, sb);
     }
   };
 
@@ -584,36 +600,39 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   // Fragments of two chunks (by the wave's own chunk order: 0 = first, 1 = second) and
   // decoded operands of two k-steps.
   const int xg0 = wave_m ? GS + 1 : 0;  // first whole activation group of this wave
-  const int wfrag = (wave_n * FN * 64 + lane) * 16;
-  const int xfrag = (xg0 * 64 + lane) * 16;
-  const int sfrag = (GS * 64 + lane) * 16;
-  const int wsw = (wave_n * FN * 32 + r32) * 8 + 2 * h;  // scale byte offsets (chunk 0)
-  const int xsw = (xg0 * 32 + r32) * 8 + 2 * h;
-  const int ssw = (GS * 32 + r32) * 8 + 2 * h;
+  // lane's 16-byte piece of chunk 0 within a 32-row group (2 KiB); chunk 1's is 32 over
+  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
+  const int wfrag = wave_n * FN * 2048;
+  const int xfrag = xg0 * 2048;
+  const int sfrag = GS * 2048;
+  const int wsw = (kRowsSx + wave_n * FN * 32 + r32) * 16 + 2 * h;  // scale byte offsets
+  const int xsw = (xg0 * 32 + r32) * 16 + 2 * h;
+  const int ssw = (GS * 32 + r32) * 16 + 2 * h;
   u32x4 wraw[2][FN], xraw[2][FM], sraw;
   uint32_t wsr[2][FN], xsr[2][FM], ssr;
   half2_t wsc[FN], xsc[FM], ssc;
   half8_t wf[2][FN], xf[2][FM], sf[2];
   // read the fragments of chunk `c` (physical) of stage buffer `buf` as the wave's chunk
-  // `par`; the shared group only in its first chunk
-  auto read_chunk = [&](int par, int buf, int c) {
-    const uint8_t* wb = &sm.w[buf][c][wfrag];
-    const uint8_t* xb = &sm.x[buf][c][xfrag];
-    const uint8_t* wsb = (const uint8_t*)sm.ws[buf] + wsw + c * 4;
-    const uint8_t* xsb = (const uint8_t*)sm.xs[buf] + xsw + c * 4;
+  // `par`, with the scales of the stage (pair buffer `sb`, stage `sub` of the pair); the
+  // shared group only in its first chunk
+  auto read_chunk = [&](int par, int buf, int c, int sb, int sub) {
+    const int fr = fr0 ^ (32 * c);
+    const uint8_t* wb = &sm.w[buf][wfrag + fr];
+    const uint8_t* xb = &sm.x[buf][xfrag + fr];
+    const uint8_t* scb = &sm.sc[sb][sub * 8 + c * 4];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[par][i] = *(const u32x4*)(wb + i * 1024);
-      wsr[par][i] = *(const uint16_t*)(wsb + i * 256);
+      wraw[par][i] = *(const u32x4*)(wb + i * 2048);
+      wsr[par][i] = *(const uint16_t*)(scb + wsw + i * 512);
     }
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      xraw[par][f] = *(const u32x4*)(xb + f * 1024);
-      xsr[par][f] = *(const uint16_t*)(xsb + f * 256);
+      xraw[par][f] = *(const u32x4*)(xb + f * 2048);
+      xsr[par][f] = *(const uint16_t*)(scb + xsw + f * 512);
     }
     if (par == 0) {
-      sraw = *(const u32x4*)&sm.x[buf][c][sfrag];
-      ssr = *(const uint16_t*)((const uint8_t*)sm.xs[buf] + ssw + c * 4);
+      sraw = *(const u32x4*)&sm.x[buf][sfrag + fr];
+      ssr = *(const uint16_t*)(scb + ssw);
     }
   };
   auto decode_step = [&](int par, int j, int slot) {
@@ -631,16 +650,20 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     if (par == 0) sf[slot] = decode8<true>(sraw[j], j < 2 ? ssc.xx : ssc.yy);
   };
 
-  // prologue: stages 0, 1 and 2 into buffers 0, 1 and 2
+  // prologue: scales of pairs 0 and 1, codes of stages 0, 1 and 2
+  issue_scale(0, 0, 0);
+  issue_scale(0, 1, 0);
+  issue_scale(npair > 1 ? 1 : 0, 0, 1);
+  issue_scale(npair > 1 ? 1 : 0, 1, 1);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, 0, 0, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1);
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2);
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  read_chunk(0, 0, wave_m);
+  read_chunk(0, 0, wave_m, 0, 0);
   decode_step(0, 0, 0);
 
   int buf = 0;
@@ -648,16 +671,20 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     const int nbuf = (buf + 1) & 3;  // stage t + 1 (complete since the end of stage t - 2)
     const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
     const int lstage = t + 3 < nk ? t + 3 : nk - 1;
+    const int pair = t >> 1;
+    const int sb = pair % 3, sbn = ((t + 1) >> 1) % 3;        // pair buffers of t and t + 1
+    const int spair = pair + 2 < npair ? pair + 2 : npair - 1;  // pair loaded in this stage
+    const int sbl = (pair + 2) % 3;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;
       const int par = st >> 2, j = st & 3;
 #pragma unroll
       for (int l = 0; l < kLoadsPerStep; ++l)
-        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf);
+        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf, t, spair, sbl);
       if (j == 0) {  // the wave's second chunk of this stage, or its first of the next
-        if (par == 0) read_chunk(1, buf, wave_m ^ 1);
-        else read_chunk(0, nbuf, wave_m);
+        if (par == 0) read_chunk(1, buf, wave_m ^ 1, sb, t & 1);
+        else read_chunk(0, nbuf, wave_m, sbn, (t + 1) & 1);
       }
       decode_step(((st + 1) >> 2) & 1, (st + 1) & 3, cur ^ 1);
 #pragma unroll
@@ -690,7 +717,7 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   // them through LDS (the stage buffers are free now).
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  float* xch = (float*)&sm.x[0][0][0];
+  float* xch = (float*)&sm.x[0][0];
   static_assert(NW * FN * 16 * 64 * sizeof(float) <= sizeof(sm.x), "exchange fits");
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -705,7 +732,7 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.w), "store staging fits");
   store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane,
-                         (uint16_t*)&sm.w[0][0][0] + wave * 32 * kStoreRowPad(FN));
+                         (uint16_t*)&sm.w[0][0] + wave * 32 * kStoreRowPad(FN));
   // group GS: wave m = 0 stores column quads 0-1 of every block, m = 1 quads 2-3
   store_tile<1, FN>(*(const floatx16(*)[FN][1])&accs, p, (int64_t)m0 + GS * 32, n_base, lane,
                     wave_m * 2, wave_m * 2 + 2);
@@ -900,13 +927,27 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
 // kernels; calibrated on the 32x32x16 f16 MFMA, which issues every ~34 cycles back to
 // back and slows down once a wave has more than about 3 VALU instructions per MFMA (the
 // decode costs 8 VALU per fragment of 8 elements per lane).
+#ifndef NVFP4_GEMM_KC
+#define NVFP4_GEMM_KC 2
+#endif
+#ifndef NVFP4_GEMM_WM
+#define NVFP4_GEMM_WM 2
+#endif
+#ifndef NVFP4_GEMM_WN
+#define NVFP4_GEMM_WN 2
+#endif
+#ifndef NVFP4_FIT_BM
+#define NVFP4_FIT_BM 288
+#define NVFP4_FIT_BN 192
+#endif
+constexpr int kTileBM = 256, kTileBN = 256, kTileKC = NVFP4_GEMM_KC;
+constexpr int kFitBM = NVFP4_FIT_BM, kFitBN = NVFP4_FIT_BN;
+
 double mfma_cycles(double frags_per_mfma) {
   const double v = 8.0 * frags_per_mfma;
   return 34.0 + (v > 3.0 ? 3.5 * (v - 3.0) : 0.0);
 }
 int64_t passes(int64_t wgs, int64_t cus) { return (wgs + cus - 1) / cus; }
-
-struct SplitShape { int a, b; };
 
 // Split-K workgroup shape for M activation rows: 32 x 32B outputs with B the smallest
 // of 1, 2, 4 that covers min(M, 128) rows (measured: wider shapes do not pay at these M).
@@ -928,56 +969,55 @@ hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s)
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  const bool aligned = ((uintptr_t)p.a_packed % 16 == 0) && ((uintptr_t)p.w_packed % 16 == 0) &&
-                       ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.w_scales % 4 == 0);
-#ifndef NVFP4_GEMM_KC
-#define NVFP4_GEMM_KC 2
-#endif
-#ifndef NVFP4_GEMM_WM
-#define NVFP4_GEMM_WM 2
-#endif
-#ifndef NVFP4_GEMM_WN
-#define NVFP4_GEMM_WN 2
-#endif
-  constexpr int BM = 256, BN = 256, KC = NVFP4_GEMM_KC;
-#ifndef NVFP4_FIT_BM
-#define NVFP4_FIT_BM 288
-#define NVFP4_FIT_BN 192
-#endif
-  constexpr int FBM = NVFP4_FIT_BM, FBN = NVFP4_FIT_BN;
-  const bool fast = aligned && (p.K % (64 * KC) == 0);
-  const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
+  constexpr int BM = kTileBM, BN = kTileBN, KC = kTileKC;
+  constexpr int FBM = kFitBM, FBN = kFitBN;
+  GemmPlan plan{};
+  cus = cus > 0 ? cus : 256;
+  const bool fast = aligned && (K % (64 * KC) == 0);
   // 32-bit buffer offsets (with one tile of rows past the end) for the fit and split-K kernels
-  const bool fits32 = (p.M + FBM) * (p.K / 2) < ((int64_t)1 << 31) &&
-                      (p.N + FBN) * (p.K / 2) < ((int64_t)1 << 31);
-  const int64_t nk = p.K / 128;
+  const bool fits32 = (M + FBM) * (K / 2) < ((int64_t)1 << 31) &&
+                      (N + FBN) * (K / 2) < ((int64_t)1 << 31);
+  const int64_t nk = K / 128;
   // tiled kernels: one tile per compute unit at a time, plus epilogue and prologue
-  const int64_t t256 = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const int64_t tfit = ((p.M + FBM - 1) / FBM) * ((p.N + FBN - 1) / FBN);
+  const int64_t t256 = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t tfit = ((M + FBM - 1) / FBM) * ((N + FBN - 1) / FBN);
   const double c256 = fast ? (double)passes(t256, cus) * (nk * 128 * mfma_cycles(0.5) + 20000.0) : 1e300;
-  const bool fit_ok = aligned && p.K % 128 == 0 && fits32;
+  const bool fit_ok = aligned && K % 128 == 0 && fits32;
   const double cfit = fit_ok ? (double)passes(tfit, cus) * (nk * 108 * mfma_cycles(7.5 / 13.5) + 20000.0) : 1e300;
   // Few tiles (short activations): the tiled kernels would leave most compute units
   // idle for a whole K loop; split K inside the workgroup instead.
-  const bool split_ok = aligned && p.K % 32 == 0 && fits32;
-  const bool use_split = split_ok && tfit * 4 <= cus;
+  const bool split_ok = aligned && K % 32 == 0 && fits32;
+  plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
+  plan.split = splitk_shape(M);
 #ifdef NVFP4_GEMM_FORCE_TILE
   // development switch: 0 = 256x256, 1 = fit tile, 2 = split-K
-  if (NVFP4_GEMM_FORCE_TILE == 2 && split_ok) return launch_splitk(p, stream, splitk_shape(p.M));
-  if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) {
-    hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
-  if (NVFP4_GEMM_FORCE_TILE == 0) return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
+  if (NVFP4_GEMM_FORCE_TILE == 2 && split_ok) plan.kernel = NVFP4_GEMM_SPLITK;
+  else if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) plan.kernel = NVFP4_GEMM_FIT;
+  return plan;
 #endif
-  if (use_split) return launch_splitk(p, stream, splitk_shape(p.M));
-  if (cfit <= c256 && fit_ok) {
-    if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_fit_kernel<FBM, FBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
-    return hipGetLastError();
+  if (split_ok && tfit * 4 <= cus) plan.kernel = NVFP4_GEMM_SPLITK;
+  else if (fit_ok && cfit <= c256) plan.kernel = NVFP4_GEMM_FIT;
+  return plan;
+}
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
+  const bool aligned = ((uintptr_t)p.a_packed % 16 == 0) && ((uintptr_t)p.w_packed % 16 == 0) &&
+                       ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.w_scales % 4 == 0);
+  const GemmPlan plan = plan_gemm(p.M, p.N, p.K, aligned, dev.num_cus);
+  switch (plan.kernel) {
+    case NVFP4_GEMM_SPLITK:
+      return launch_splitk(p, stream, plan.split);
+    case NVFP4_GEMM_FIT: {
+      const int64_t tfit = ((p.M + kFitBM - 1) / kFitBM) * ((p.N + kFitBN - 1) / kFitBN);
+      if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_fit_kernel<kFitBM, kFitBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    default:
+      return launch_tile<kTileBM, kTileBN, kTileKC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(
+          p, stream, plan.kernel == NVFP4_GEMM_TILE256);
   }
-  return launch_tile<BM, BN, KC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(p, stream, fast);
 }
 
 hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,

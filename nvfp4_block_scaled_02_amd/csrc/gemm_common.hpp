@@ -191,6 +191,14 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
 // own L2, so workgroup b takes tile (b % 8) * (T / 8) + b / 8 of an order in which each
 // XCD's share is contiguous; that order walks groups of G tile rows column by column, so
 // an XCD's tiles share few activation and weight rows. (T % 8 != 0: plain order.)
+// Chunk swizzle of a 64-byte LDS row by its index r (0..15) within a 1 KiB piece of 16
+// rows: the row's 16-byte chunk q is stored at slot q ^ chunk_swz(r). A lane (h, r) of an
+// MFMA fragment reads chunk h or h + 2 of row r; with this swizzle the 16-byte reads of
+// any 8 or 16 consecutive lanes fall in distinct LDS banks (32- or 64-bank view), and a
+// direct-to-LDS load whose lane l fetches chunk (l % 4) ^ chunk_swz(l / 4) of row l / 4
+// writes the piece in this order.
+__device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
+
 __device__ __forceinline__ void tile_order(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int kXcd = 8, G = NVFP4_GEMM_XCD_GROUP;
   const int T = tiles_m * tiles_n;

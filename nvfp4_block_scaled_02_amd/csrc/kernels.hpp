@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/nvfp4.h"
+
 namespace nvfp4 {
 
 struct LaunchInfo {
@@ -24,6 +26,15 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
+
+// The kernel launch_gemm picks for a shape (values of nvfp4_gemm_kernel in nvfp4.h), and
+// the split-K workgroup shape (32a weight rows x 32b activation rows) when it splits.
+struct SplitShape { int a, b; };
+struct GemmPlan {
+  int kernel;
+  SplitShape split;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus);
 
 struct W4A16Problem {
   const uint16_t* x;  // bf16 [M, K]

@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
 // zero (buffer range checks).
 //
 // Stage (64 elements of K) layout in LDS: each 16-row piece is 1 KiB, row r's 64 bytes at
-// 64 r, its 16-byte chunk c stored at slot c ^ mx_swz(r) so that the fragment reads (two
+// 64 r, its 16-byte chunk c stored at slot c ^ chunk_swz(r) so that the fragment reads (two
 // 16-byte reads per lane and block, chunks h and h + 2 of row r) hit distinct banks. Four
 // code buffers, filled three stages ahead; two scale buffers of 8 stages, filled 8 stages
 // ahead. At the end of stage t each wave waits for every load it issued before stage t
@@ -123,9 +123,6 @@ struct alignas(16) MxSmem {
   uint8_t xs[2][BM * 16];
   uint8_t ws[2][BN * 16];
 };
-
-// chunk swizzle of a 64-byte LDS row by its index r (0..15) within its 1 KiB piece
-__device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
@@ -171,7 +168,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
   const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
   const int lr = lane >> 2;  // row of a code piece this lane loads
-  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ mx_swz(lr));
+  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
   const uint32_t voff_s = lane * spitch;
 
   // Code load j of this wave for `stage` into buffer `buf`: piece j * NW + wave of the
@@ -212,7 +209,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   v8i_t wf[2][FN], xf[2][FM];
   int wsc[2][FN], xsc[2][FM];
   // lane's first 16-byte chunk within a 32-row group (2 KiB); the second is 32 bytes over
-  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ mx_swz(r32 & 15));
+  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
   const int fr1 = fr0 ^ 32;
   // LDS reads of one stage in the order its MFMAs need them: w0, x0..x(FM-1), w1, ...
   // Read k (of kReads) is a fragment half or a scale byte.

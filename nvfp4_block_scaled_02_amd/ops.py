@@ -144,6 +144,17 @@ def mxfp8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Ten
     return out
 
 
+GEMM_KERNELS = {0: "tile256", 1: "fit", 2: "splitk", 3: "generic"}
+
+
+def gemm_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
+    """Name of the kernel :func:`gemm` launches for an M x N x K product with aligned
+    operands on a device with ``num_cus`` compute units (0: 256, an MI355X). Host only."""
+    kind = ctypes.c_int(-1)
+    check(load_library().nvfp4_gemm_plan(M, N, K, num_cus, ctypes.byref(kind)), "nvfp4_gemm_plan")
+    return GEMM_KERNELS[kind.value]
+
+
 def linear_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().nvfp4_linear_workspace_bytes(M, K))
 

@@ -100,6 +100,31 @@ def test_gemm_validation(lib):
     assert call({7: 0}) == L.SUCCESS
 
 
+def test_gemm_plan_routes_shapes(lib):
+    """The planner (host only) sends the FLUX activations (4608 rows) to the 288 x 192
+    tile, short activations to split-K, and shapes whose tile count fits 256-tile passes
+    better to the 256 x 256 tile; K % 128 != 0 needs the register-staged kernel."""
+    def plan(M, N, K, cus=0):
+        k = ctypes.c_int(-1)
+        st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
+        return st, k.value
+
+    FIT, TILE, SPLIT, GEN = 1, 0, 2, 3
+    for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
+                    (4608, 9216, 3072), (2600, 1650, 128)]:
+        assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
+    for M in (1, 17, 256, 1000):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    assert plan(4096, 4096, 128) == (L.SUCCESS, TILE)
+    assert plan(600, 700, 208) == (L.SUCCESS, GEN)   # K % 32 == 16: no split-K either
+    assert plan(4608, 3072, 3008) == (L.SUCCESS, GEN)
+    # fewer compute units: the same M = 1000 product is worth tiling
+    assert plan(1000, 3072, 3072, 32) == (L.SUCCESS, FIT)
+    assert plan(8, 8, 40)[0] == L.INVALID_SHAPE
+    assert plan(-1, 8, 64)[0] == L.INVALID_SHAPE
+    assert lib.nvfp4_gemm_plan(8, 8, 64, 0, None) == L.INVALID_VALUE
+
+
 def test_gemm_w4a16_validation(lib):
     g = lib.nvfp4_gemm_w4a16
     args = [P16, P16b, P16b, 1.0, 8, 8, 64, P16, NULL]

@@ -65,6 +65,27 @@ def test_gemm_small_shapes_in_full(M, N, K):
     _assert_close(got, ap, as_, ags, wp, ws, wgs, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,kernel", [
+    # 288 x 192 tiles: one stage (K = 128), an odd number of stages, ragged by one row
+    # and column, and several scale pairs with an odd count
+    (2600, 1650, 128, "fit"), (2900, 1500, 384, "fit"), (2305, 1537, 256, "fit"),
+    (2000, 2000, 1152, "fit"),
+    (4096, 4096, 128, "tile256"),
+    (600, 700, 208, "generic"),
+])
+def test_gemm_tiled_kernels_in_full(M, N, K, kernel):
+    assert nv.gemm_plan(M, N, K) == kernel
+    rng = np.random.default_rng(M * 17 + N * 3 + K)
+    x = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ags, wgs, ap, as_, wp, ws = _operands(x, w)
+    say("gemm", kernel, M, N, K)
+    out, ok = _gemm_dev(ap, as_, ags, wp, ws, wgs)
+    got = to_host(out)
+    assert ok(), "write outside out"
+    _assert_close(got, ap, as_, ags, wp, ws, wgs, f"{kernel} {M}x{N}x{K}")
+
+
 def test_gemm_exact_cases():
     """Closed forms: zero operands give exact zeros; W = 3 * I reproduces the dequantised
     activations (the epilogue rounds them to bf16)."""
