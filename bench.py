@@ -9,9 +9,12 @@ does. Inputs are resident in HBM when timing starts.
 Prints one JSON line (rank 0) with the step throughput in TFLOP/s (2*M*N*K per step),
 the dominant kernel's roofline (GEMM vs the f16 dense MFMA peak), the quantize kernel's
 HBM bandwidth on rotated buffers (for the workload's activation and for a large
-4608 x 12288 activation), and the CPU oracle timed on a bounded sample.
+4608 x 12288 activation), context rows (the GEMM at every M = 4608 FLUX shape and a
+4-image batch, short activations, hipBLASLt bf16 at the same shape, the MXFP8 and W4A16
+paths) and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
+                    [--no-context] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -38,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="attn_out")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context rows (other shapes, hipBLASLt, MXFP8, W4A16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rotate-mb", type=int, default=1024,
                     help="bytes of rotated activation buffers for the quantize bandwidth leg")
@@ -47,7 +52,8 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["gemm.hip", "quantize.hip", "codec.hpp"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "quantize.hip", "codec.hpp"]
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA
 
 
 def kernel_source_hash() -> str:
@@ -108,6 +114,112 @@ def cpu_baseline(wl, d, ags, wgs, seconds):
                   f"NumPy quantize (1 thread) + float64 GEMM reference ({cores} BLAS threads), "
                   f"{t_total:.1f} s",
     }
+
+
+def time_launches(fn, n, stream):
+    """Average ms of n back-to-back launches of fn on `stream` (HIP events on that
+    stream), after 3 untimed ones."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def context_legs(nv, lib, stream, n):
+    """Context rows (not the metric): every M = 4608 FLUX linear of the workload set, short
+    activations, hipBLASLt bf16 at the metric's shape, and the MXFP8 and W4A16 paths.
+    Operands are device-generated N(0, 1) activations and N(0, 0.02) weights, quantized
+    by the library; GEMM times are warm (operands resident)."""
+    import torch
+
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(7)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = {"gemm": {}, "short_activations": {}}
+
+    def operands(M, N, K):
+        x = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        ags, wgs = nv.calibrate(x), nv.calibrate(w)
+        ap, as_ = nv.quantize(x, ags)
+        wp, ws = nv.quantize(w, wgs)
+        return x, w, ags, wgs, ap, as_, wp, ws
+
+    def nvfp4_gemm_ms(M, N, K, ops):
+        _, _, ags, wgs, ap, as_, wp, ws = ops
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        args = (P(ap), P(as_), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(o), sp)
+        return time_launches(lambda: lib.nvfp4_gemm(*args), n, stream)
+
+    for name in ["attn_out", "mlp_up_static", "qkv", "mlp_down", "batch4_up"]:
+        wl = make(name)
+        M, N, K = wl.M, wl.N, wl.K
+        ops = operands(M, N, K)
+        ms = nvfp4_gemm_ms(M, N, K, ops)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out["gemm"][name] = {"M": M, "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K),
+                             "avg_ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                             "frac_f16_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+        if name == "attn_out":
+            x, w, ags, wgs, ap, as_, wp, ws = ops
+            # hipBLASLt bf16 GEMM of the unquantized operands at the same shape
+            wt = w.t().contiguous()
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ms_b = time_launches(lambda: torch.matmul(x, wt, out=y), n, stream)
+            out["hipblaslt_bf16_matmul"] = {"shape": [M, N, K], "avg_ms": round(ms_b, 5),
+                                            "TFLOP/s": round(2.0 * M * N * K / (ms_b * 1e-3) / 1e12, 1)}
+            # MXFP8 path (E4M3 elements, E8M0 scales per 32) on the same operands
+            ac, asx = nv.mxfp8_quantize(x)
+            wc, wsx = nv.mxfp8_quantize(w)
+            y8 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            a8 = (P(ac), P(asx), P(wc), P(wsx), M, N, K, P(y8), sp)
+            ms8 = time_launches(lambda: lib.nvfp4_mxfp8_gemm(*a8), n, stream)
+            q8 = (P(x), M, K, P(ac), P(asx), sp)
+            msq8 = time_launches(lambda: lib.nvfp4_mxfp8_quantize(*q8), n, stream)
+            tf8 = 2.0 * M * N * K / (ms8 * 1e-3) / 1e12
+            out["mxfp8"] = {"shape": [M, N, K], "gemm_avg_ms": round(ms8, 5), "gemm_TFLOP/s": round(tf8, 1),
+                            "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                            "quantize_avg_ms_warm": round(msq8, 5),
+                            "quantize_GB/s_warm": round((2 + 1 + 1 / 32) * M * K / (msq8 * 1e-3) / 1e9, 1)}
+            # W4A16: NVFP4 weights, bf16 activations
+            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)
+            ms16 = time_launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, stream)
+            out["w4a16"] = {"shape": [M, N, K], "avg_ms": round(ms16, 5),
+                            "TFLOP/s": round(2.0 * M * N * K / (ms16 * 1e-3) / 1e12, 1)}
+            del x, w, wt, y, ac, asx, wc, wsx, y8, y16
+        del ops
+    # short activations: the weights dominate the bytes (K/2 + K/16 bytes per weight row)
+    N, K = 3072, 3072
+    w = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    wgs = nv.calibrate(w)
+    wp, ws = nv.quantize(w, wgs)
+    for M in (1, 17, 256, 1000):
+        x = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+        ags = nv.calibrate(x)
+        ap, as_ = nv.quantize(x, ags)
+        ms = nvfp4_gemm_ms(M, N, K, (x, w, ags, wgs, ap, as_, wp, ws))
+        y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)
+        ms16 = time_launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, stream)
+        wbytes = N * (K // 2 + K // 16)
+        out["short_activations"][f"M={M}"] = {
+            "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K), "w4a4_avg_ms": round(ms, 5),
+            "w4a4_weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "w4a16_avg_ms": round(ms16, 5),
+            "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+    return out
 
 
 def main():
@@ -299,6 +411,10 @@ def main():
         "precision": "E2M1 x E4M3 operands decoded exactly to f16, f16 MFMA, fp32 accumulate, "
                      "bf16 output",
     }
+    if not args.no_context:
+        del x, qp, qs, work, out
+        torch.cuda.empty_cache()
+        result["context"] = context_legs(nv, lib, stream, max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, ags, wgs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
