@@ -10,8 +10,8 @@ Prints one JSON line (rank 0) with the step throughput in TFLOP/s (2*M*N*K per s
 the dominant kernel's roofline (GEMM vs the f16 dense MFMA peak), the quantize kernel's
 HBM bandwidth on rotated buffers (for the workload's activation and for a large
 4608 x 12288 activation), context rows (the GEMM at every M = 4608 FLUX shape and a
-4-image batch, short activations, hipBLASLt bf16 at the same shape, the MXFP8 and W4A16
-paths) and the CPU oracle timed on a bounded sample.
+4-image batch, short activations, hipBLASLt bf16 at the same shape, the MXFP8, rowwise
+FP8 and W4A16 paths) and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
                     [--no-context] [--no-cpu-baseline]
@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="attn_out")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the context rows (other shapes, hipBLASLt, MXFP8, W4A16)")
+                    help="skip the context rows (other shapes, hipBLASLt, MXFP8, fp8r, W4A16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rotate-mb", type=int, default=1024,
                     help="bytes of rotated activation buffers for the quantize bandwidth leg")
@@ -135,7 +135,8 @@ def time_launches(fn, n, stream):
 
 def context_legs(nv, lib, stream, n):
     """Context rows (not the metric): every M = 4608 FLUX linear of the workload set, short
-    activations, hipBLASLt bf16 at the metric's shape, and the MXFP8 and W4A16 paths.
+    activations, hipBLASLt bf16 at the metric's shape, and the MXFP8, rowwise FP8 and W4A16
+    paths.
     Operands are device-generated N(0, 1) activations and N(0, 0.02) weights, quantized
     by the library; GEMM times are warm (operands resident)."""
     import torch
@@ -192,6 +193,20 @@ def context_legs(nv, lib, stream, n):
                             "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                             "quantize_avg_ms_warm": round(msq8, 5),
                             "quantize_GB/s_warm": round((2 + 1 + 1 / 32) * M * K / (msq8 * 1e-3) / 1e9, 1)}
+            # rowwise FP8 (fp8r): E4M3 with one fp32 scale per row, unit-scaled fp8 MFMA
+            rc, rs = nv.fp8r_quantize(x)
+            wrc, wrs = nv.fp8r_quantize(w)
+            yr = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ar = (P(rc), P(rs), P(wrc), P(wrs), M, N, K, P(yr), sp)
+            msr = time_launches(lambda: lib.nvfp4_fp8r_gemm(*ar), n, stream)
+            qr = (P(x), M, K, P(rc), P(rs), sp)
+            msqr = time_launches(lambda: lib.nvfp4_fp8r_quantize(*qr), n, stream)
+            tfr = 2.0 * M * N * K / (msr * 1e-3) / 1e12
+            out["fp8r"] = {"shape": [M, N, K], "gemm_avg_ms": round(msr, 5), "gemm_TFLOP/s": round(tfr, 1),
+                           "frac_fp8_peak": round(tfr / PEAK_FP8_TFLOPS, 4),
+                           "quantize_avg_ms_warm": round(msqr, 5),
+                           "quantize_GB/s_warm": round((3 * M * K + 4 * M) / (msqr * 1e-3) / 1e9, 1)}
+            del rc, rs, wrc, wrs, yr
             # W4A16: NVFP4 weights, bf16 activations
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)

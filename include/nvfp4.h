@@ -175,6 +175,39 @@ int nvfp4_mxfp8_gemm(const void* a_codes, const void* a_scales, const void* w_co
                      const void* w_scales, int64_t M, int64_t N, int64_t K, void* out_bf16,
                      void* stream);
 
+/*
+ * Rowwise FP8 ("fp8r") path: the other scheme of the "BFL (fp8r / nvfp4)" page (scheme
+ * list, fp8r item: an E4M3 weight and one fp32 weight_scale per row, activations quantized
+ * to E4M3 per row at run time; Kernels table, fp8r row: a scaled matmul with rowwise
+ * scales). Conventions of this library where the page is silent:
+ *   - scale of a row: s = RN32(amax / 448) (448 = the largest E4M3 value), 1.0 for an
+ *     all-zero row; dequantize direction, x ~ e4m3(code) * s;
+ *   - element: the E4M3 value nearest to RN32(x / s) (IEEE division), ties to even,
+ *     clamped to +-448, sign copied (-0 -> 0x80);
+ *   - layouts: codes uint8 [rows, K] row-major, scales fp32 [rows];
+ *   - GEMM: out = bf16_RNE(s_a[m] * s_w[n] * sum_k e4m3(a[m,k]) e4m3(w[n,k])); any result
+ *     within 2^-10 * sum_k |a_k w_k| + 1 bf16 ulp of the exact value is correct and the
+ *     library's result is deterministic for a given shape.
+ *
+ * nvfp4_fp8r_quantize: x_bf16 [M, K] (16-byte aligned) -> codes uint8 [M, K] (16-byte
+ * aligned) and scales fp32 [M] (4-byte aligned). K >= 16, K % 16 == 0. Bit-exact to the
+ * rule above (weights are quantized offline with the same call).
+ */
+int nvfp4_fp8r_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes, void* scales,
+                        void* stream);
+
+/*
+ * nvfp4_fp8r_gemm: out_bf16 [M, N] = diag(a_scales) Qa Qw^T diag(w_scales) with activations
+ * a_codes [M, K] / a_scales fp32 [M] and weights w_codes [N, K] / w_scales fp32 [N] as
+ * produced by nvfp4_fp8r_quantize. K % 128 == 0 and (max(M, N) + 256) * K < 2^31, else
+ * NVFP4_ERROR_INVALID_SHAPE; codes and out 16-byte aligned, scales 4-byte aligned. Runs
+ * on gfx950's block-scaled fp8 MFMA with unit block scales; the row and column scales are
+ * applied in the epilogue.
+ */
+int nvfp4_fp8r_gemm(const void* a_codes, const void* a_scales, const void* w_codes,
+                    const void* w_scales, int64_t M, int64_t N, int64_t K, void* out_bf16,
+                    void* stream);
+
 /* Workspace bytes nvfp4_linear needs for an [M, K] activation (packed + scales, each
  * rounded up to 256 bytes). Returns 0 for invalid shapes. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);

@@ -8,12 +8,15 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`gemm_plan` -- which GEMM kernel a shape runs on (host only)
 * :func:`gemm_w4a16` -- NVFP4 weights x bf16 activations (not quantized), bf16 output
 * :func:`mxfp8_quantize`, :func:`mxfp8_gemm` -- the MXFP8 (OCP microscaling) path
+* :func:`fp8r_quantize`, :func:`fp8r_gemm` -- the rowwise FP8 path
 * :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
 """
 from ._lib import NVFP4Error, load_library  # noqa: F401
 from .ops import (  # noqa: F401
     amax,
     calibrate,
+    fp8r_gemm,
+    fp8r_quantize,
     gemm,
     gemm_plan,
     gemm_w4a16,

@@ -40,6 +40,8 @@ SIGNATURES = {
     "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_mxfp8_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_mxfp8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_fp8r_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "nvfp4_fp8r_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_linear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_linear": (_int, [_vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp,
                             ctypes.c_size_t, _vp]),

@@ -24,7 +24,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_w4a16.hip", "mxfp8.hip", "amax.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_w4a16.hip", "mxfp8.hip", "fp8r.hip", "amax.hip"]
 ARCH = "gfx950"
 
 

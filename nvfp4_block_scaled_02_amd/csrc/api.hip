@@ -220,6 +220,45 @@ int nvfp4_mxfp8_gemm(const void* ac, const void* as, const void* wc, const void*
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
+int nvfp4_fp8r_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
+                        void* stream) {
+  if (!x || !codes || !scales) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return NVFP4_ERROR_MISALIGNED;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_fp8r_quantize(x, M, K, codes, scales, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_fp8r_gemm(const void* ac, const void* as, const void* wc, const void* ws, int64_t M,
+                    int64_t N, int64_t K, void* out, void* stream) {
+  if (!ac || !as || !wc || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (K % 128 != 0) return NVFP4_ERROR_INVALID_SHAPE;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  // 32-bit buffer offsets, with one 256-row tile past the end (codes and fp32 scales)
+  if ((M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
+    return NVFP4_ERROR_INVALID_SHAPE;
+  if (!aligned(ac, 16) || !aligned(wc, 16) || !aligned(out, 16) || !aligned(as, 4) ||
+      !aligned(ws, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  if (M == 0 || N == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  nvfp4::GemmProblem p{(const uint8_t*)ac, (const uint8_t*)as, (const uint8_t*)wc,
+                       (const uint8_t*)ws, (uint16_t*)out, M, N, K, 1.0f};
+  hipError_t e = nvfp4::launch_fp8r_gemm(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
   if (check_shape(M, K)) return 0;
   return round_up((size_t)(M * K / 2), 256) + round_up((size_t)(M * K / 16), 256);

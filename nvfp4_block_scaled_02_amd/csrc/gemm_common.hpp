@@ -120,7 +120,11 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
 // makes the round trip safe without a barrier.
 constexpr int kStoreRowPad(int fn) { return fn * 32 + 8; }
 
-template <int FM, int FN>
+//
+// kRowCol: instead of the scalar alpha, each output (m, n) is scaled by a_scales[m] *
+// w_scales[n], read as fp32 arrays [M] and [N] (rowwise-scaled products); entries past M
+// or N read as zero through range-checked buffer loads.
+template <int FM, int FN, bool kRowCol = false>
 __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
                                                int64_t m_base, int64_t n_base, int lane,
                                                uint16_t* blk) {
@@ -130,6 +134,23 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
+  float sx[FM];
+  u32x4 sw[FN][4];
+  if constexpr (kRowCol) {
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.a_scales, (uint32_t)(p.M * 4));
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w_scales, (uint32_t)(p.N * 4));
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+      sx[g] = u2f(__builtin_amdgcn_raw_buffer_load_b32(rsx, (int)((m_base + g * 32 + r32) * 4), 0, 0));
+    // one dword per column (a 16-byte load straddling N could read as zero as a whole)
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sw[i][q][e] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)((n_base + i * 32 + 8 * q + 4 * h + e) * 4), 0, 0);
+  }
 #pragma unroll
   for (int g = 0; g < FM; ++g) {
 #pragma unroll
@@ -138,7 +159,10 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
       for (int q = 0; q < 4; ++q) {
         uint32_t b[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (kRowCol) b[e] = bf16_rne(acc[i][g][4 * q + e] * sx[g] * u2f(sw[i][q][e]));
+          else b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+        }
         *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
       }
     const int64_t m_row = m_base + g * 32;

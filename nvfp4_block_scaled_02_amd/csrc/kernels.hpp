@@ -52,6 +52,11 @@ hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const La
 hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
                               hipStream_t stream, const LaunchInfo& dev);
 hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
+// Rowwise FP8: codes as above, scales fp32 [rows] (GemmProblem's a_scales/w_scales point
+// to fp32 arrays); alpha unused.
+hipError_t launch_fp8r_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
+                                hipStream_t stream, const LaunchInfo& dev);
+hipError_t launch_fp8r_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
 hipError_t launch_mx_selftest_e4m3_exhaustive(unsigned long long* count, uint32_t* first,
                                               hipStream_t stream);
 

@@ -128,7 +128,12 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 // Requires K % 128 == 0, 16-byte aligned codes, 4-byte aligned scales, and
 // (rows + one tile) x K below 2^31 for both operands (32-bit buffer offsets).
-template <int BM, int BN>
+//
+// kRowwise: the rowwise FP8 product of the "BFL (fp8r / nvfp4)" page (fp8r item and
+// Kernels table row: E4M3 operands with one fp32 scale per row). The per-row scales leave
+// the K-sum, so the MFMA runs with unit block scales (E8M0 127, no scale loads) and the
+// epilogue multiplies each output by a_scales[m] * w_scales[n] (fp32 arrays).
+template <int BM, int BN, bool kRowwise>
 __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   constexpr int NW = 4, WM = 2, WN = 2;
   __shared__ MxSmem<BM, BN> sm;
@@ -140,7 +145,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
                 "loads divide evenly among waves");
   constexpr int kPaW = kPa / NW, kPwW = kPw / NW;
   constexpr int kLoads = kPaW + kPwW;          // code loads per wave per stage
-  constexpr int kSLoads = (kSa + kSw) / NW;    // scale loads per wave per 8 stages
+  constexpr int kSLoads = kRowwise ? 0 : (kSa + kSw) / NW;  // scale loads per wave per 8 stages
   constexpr int kMfma = FN * FM;
   static_assert(kLoads + kSLoads <= kMfma, "at most one load after each MFMA");
   static_assert(kLoads + kSLoads < 64, "one stage of loads fits the vmcnt counter");
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
       } else if (part == 1) {
         const u32x4 b = *(const u32x4*)&base[fr1];
         wf[par][idx][4] = (int)b.x; wf[par][idx][5] = (int)b.y; wf[par][idx][6] = (int)b.z; wf[par][idx][7] = (int)b.w;
-      } else {
+      } else if (!kRowwise) {
         wsc[par][idx] = sm.ws[sbuf][(wave_n * WTN + idx * 32 + r32) * 16 + sbyte];
       }
     } else {
@@ -239,7 +244,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
       } else if (part == 1) {
         const u32x4 b = *(const u32x4*)&base[fr1];
         xf[par][idx][4] = (int)b.x; xf[par][idx][5] = (int)b.y; xf[par][idx][6] = (int)b.z; xf[par][idx][7] = (int)b.w;
-      } else {
+      } else if (!kRowwise) {
         xsc[par][idx] = sm.xs[sbuf][(wave_m * WTM + idx * 32 + r32) * 16 + sbyte];
       }
     }
@@ -273,7 +278,8 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
     for (int q = 0; q < kMfma; ++q) {
       const int i = q / FM, g = q % FM;
       acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, wsc[cur][i], 0, xsc[cur][g]);
+          wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+          kRowwise ? 127 : xsc[cur][g]);
       if (q < kLoads) issue_codes(q, lstage, lbuf);
       else if (q < kLoads + kSLoads && sload) issue_scales(q - kLoads, sgrp, ((t >> 3) + 1) & 1);
 #pragma unroll
@@ -302,8 +308,8 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
-  store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN, lane,
-                         (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+  store_tile_lds<FM, FN, kRowwise>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN,
+                                   lane, (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- self-test: the fp8 conversion against the software E4M3 encoder ----------------
@@ -348,7 +354,16 @@ hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const Launch
   constexpr int BM = 256, BN = 256;
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8r_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
+  (void)dev;
+  constexpr int BM = 256, BN = 256;
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -144,6 +144,48 @@ def mxfp8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Ten
     return out
 
 
+def fp8r_quantize(x: torch.Tensor, codes: torch.Tensor | None = None,
+                  scales: torch.Tensor | None = None, stream=None):
+    """Rowwise FP8 quantization: bf16 [M, K] -> E4M3 codes uint8 [M, K] + fp32 scales [M]."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, 2)
+    _need(scales, "scales", torch.float32, 1)
+    if tuple(codes.shape) != (M, K) or tuple(scales.shape) != (M,):
+        raise ValueError("codes must be [M, K] and scales [M]")
+    lib = load_library()
+    check(lib.nvfp4_fp8r_quantize(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream)),
+          "nvfp4_fp8r_quantize")
+    return codes, scales
+
+
+def fp8r_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+              w_scales: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Rowwise FP8 GEMM: bf16 [M, N] = diag(a_scales) Qa Qw^T diag(w_scales)."""
+    _need(a_codes, "a_codes", torch.uint8, 2)
+    _need(w_codes, "w_codes", torch.uint8, 2)
+    _need(a_scales, "a_scales", torch.float32, 1)
+    _need(w_scales, "w_scales", torch.float32, 1)
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    if tuple(w_codes.shape) != (N, K) or tuple(a_scales.shape) != (M,) or \
+            tuple(w_scales.shape) != (N,):
+        raise ValueError("operand shapes are inconsistent")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape must be [M, N]")
+    lib = load_library()
+    check(lib.nvfp4_fp8r_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
+                              M, N, K, _ptr(out), _stream(stream)), "nvfp4_fp8r_gemm")
+    return out
+
+
 GEMM_KERNELS = {0: "tile256", 1: "fit", 2: "splitk", 3: "generic"}
 
 

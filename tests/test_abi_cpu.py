@@ -153,6 +153,39 @@ def test_gemm_w4a16_validation(lib):
     assert call({5: 0}) == L.SUCCESS
 
 
+def test_fp8r_validation(lib):
+    q = lib.nvfp4_fp8r_quantize
+    assert q(NULL, 4, 64, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 64, NULL, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 64, P16, NULL, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 40, P16, P16b, NULL) == L.INVALID_SHAPE   # K % 16 != 0
+    assert q(P16, -1, 64, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(ODD, 4, 64, P16, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 4, 64, ODD, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 4, 64, P16, ctypes.c_void_p(0x20002), NULL) == L.MISALIGNED
+    assert q(P16, 0, 64, P16, P16b, NULL) == L.SUCCESS
+    g = lib.nvfp4_fp8r_gemm
+    args = [P16, P16b, P16, P16b, 8, 8, 128, P16, NULL]
+
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return g(*a)
+
+    for k in (0, 1, 2, 3, 7):
+        assert call({k: NULL}) == L.INVALID_VALUE
+    assert call({6: 64}) == L.INVALID_SHAPE     # K % 128 != 0
+    assert call({6: 40}) == L.INVALID_SHAPE
+    assert call({4: -1}) == L.INVALID_SHAPE
+    assert call({4: 2**24}) == L.INVALID_SHAPE   # (M + 256) * K >= 2^31
+    assert call({0: ODD}) == L.MISALIGNED
+    assert call({1: ctypes.c_void_p(0x20002)}) == L.MISALIGNED
+    assert call({7: ODD}) == L.MISALIGNED
+    assert call({4: 0}) == L.SUCCESS
+    assert call({5: 0}) == L.SUCCESS
+
+
 def test_mxfp8_validation(lib):
     q = lib.nvfp4_mxfp8_quantize
     assert q(NULL, 4, 64, P16, P16b, NULL) == L.INVALID_VALUE
