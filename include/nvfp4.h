@@ -241,6 +241,38 @@ int nvfp4_amax(const void* x_bf16, int64_t n, float* amax_out, void* stream);
  * negative or non-finite amax. */
 float nvfp4_global_scale_from_amax(float amax);
 
+/*
+ * Device-resident global scales: a dynamic activation scale ("calibrated" input_scale,
+ * "BFL (fp8r / nvfp4)", nvfp4 item) computed and consumed on the device, with no host
+ * round trip. All calls are asynchronous on `stream`; gs pointers are device memory,
+ * 4-byte aligned.
+ *
+ * nvfp4_calibrate_device: gs_device[0] = RN32(amax / 2688) for the n bf16 values of
+ * x_bf16 (16-byte aligned), clamped into [2^-90, 2^90]; 1.0 when amax == 0. Inside the
+ * clamp range (any tensor with amax in [2^-78, 2^101]) this equals
+ * nvfp4_global_scale_from_amax(amax). The clamp keeps extreme tensors quantizable.
+ *
+ * nvfp4_quantize_devgs: nvfp4_quantize with the global scale read from gs_device[0]
+ * when the kernel runs (a value outside [2^-90, 2^90] is clamped into it; NaN and values
+ * <= 0 read as 1.0). Bit-exact to nvfp4_quantize with that value.
+ *
+ * nvfp4_gemm_devgs: nvfp4_gemm with alpha = RN32(a_gs_device[0] * w_gs_device[0]) read
+ * when the kernel runs; bit-exact to nvfp4_gemm with the same two values. The values
+ * must be finite and > 0.
+ *
+ * nvfp4_linear_devgs: nvfp4_linear with both global scales device-resident.
+ */
+int nvfp4_calibrate_device(const void* x_bf16, int64_t n, float* gs_device, void* stream);
+int nvfp4_quantize_devgs(const void* x_bf16, int64_t M, int64_t K, const float* gs_device,
+                         void* packed, void* scales, void* stream);
+int nvfp4_gemm_devgs(const void* a_packed, const void* a_scales, const float* a_gs_device,
+                     const void* w_packed, const void* w_scales, const float* w_gs_device,
+                     int64_t M, int64_t N, int64_t K, void* out_bf16, void* stream);
+int nvfp4_linear_devgs(const void* x_bf16, const float* a_gs_device, const void* w_packed,
+                       const void* w_scales, const float* w_gs_device, int64_t M, int64_t N,
+                       int64_t K, void* out_bf16, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,11 +10,14 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`mxfp8_quantize`, :func:`mxfp8_gemm` -- the MXFP8 (OCP microscaling) path
 * :func:`fp8r_quantize`, :func:`fp8r_gemm` -- the rowwise FP8 path
 * :func:`amax`, :func:`calibrate`, :func:`global_scale_from_amax` -- global scales
+* :func:`calibrate_device` -- a global scale kept on the device (quantize, gemm and
+  linear accept it in place of a float)
 """
 from ._lib import NVFP4Error, load_library  # noqa: F401
 from .ops import (  # noqa: F401
     amax,
     calibrate,
+    calibrate_device,
     fp8r_gemm,
     fp8r_quantize,
     gemm,

@@ -47,6 +47,11 @@ SIGNATURES = {
                             ctypes.c_size_t, _vp]),
     "nvfp4_amax": (_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_global_scale_from_amax": (_f32, [_f32]),
+    "nvfp4_calibrate_device": (_int, [_vp, _i64, _vp, _vp]),
+    "nvfp4_quantize_devgs": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_gemm_devgs": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_linear_devgs": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
+                                  ctypes.c_size_t, _vp]),
     "nvfp4_selftest_e2m1_encode": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "nvfp4_selftest_e2m1_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_division": (_int, [_vp, _vp, _vp]),

@@ -1,6 +1,9 @@
 // Tensor amax for calibrating a global scale (the pages' calibrated fp32 input_scale and
 // stored weight_scale_2, "BFL (fp8r / nvfp4)", nvfp4 item): max |x| over a bf16 tensor.
 //
+// Device-side calibration (launch_calibrate) adds a one-lane kernel that turns the amax
+// into the global scale in place, so a dynamic scale never visits the host.
+//
 // Two launches on the caller's stream: a one-lane kernel clears the result, then a
 // grid-stride kernel (two workgroups per CU) reduces four independent 16-byte loads per
 // lane and step, reduces each wave with cross-lane moves and the workgroup through LDS,
@@ -15,6 +18,13 @@ namespace nvfp4 {
 namespace {
 
 __global__ void clear_kernel(uint32_t* out) { *out = 0u; }
+
+// In place: the amax (as fp32) becomes the global scale RN(amax / 2688) clamped into
+// [2^-90, 2^90] (1 for amax == 0), the host's formula evaluated on the device.
+__global__ void gs_from_amax_kernel(float* v) {
+  const float a = *v;
+  *v = a > 0.0f ? clamp_global_scale(a / 2688.0f) : 1.0f;
+}
 
 __device__ __forceinline__ uint32_t abs_max_bf16x2(uint32_t acc, uint32_t w) {
   // |lo| and |hi| as fp32 bit patterns; integer max is the fp32 max for these.
@@ -86,6 +96,14 @@ hipError_t launch_amax(const void* x, int64_t n, float* out, hipStream_t stream,
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const u32x4*)x,
                      nvec, (const uint16_t*)x + nvec * 8, ntail, (uint32_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const void* x, int64_t n, float* gs, hipStream_t stream,
+                            const LaunchInfo& dev) {
+  hipError_t e = launch_amax(x, n, gs, stream, dev);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gs_from_amax_kernel, dim3(1), dim3(1), 0, stream, gs);
   return hipGetLastError();
 }
 

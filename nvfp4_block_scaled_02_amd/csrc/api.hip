@@ -301,6 +301,79 @@ int nvfp4_amax(const void* x, int64_t n, float* amax_out, void* stream) {
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
+// ---- device-resident global scales -------------------------------------------------------
+
+int nvfp4_calibrate_device(const void* x, int64_t n, float* gs_device, void* stream) {
+  if (!x || !gs_device) return NVFP4_ERROR_INVALID_VALUE;
+  if (n < 0) return NVFP4_ERROR_INVALID_SHAPE;
+  if (!aligned(x, 16) || !aligned(gs_device, 4)) return NVFP4_ERROR_MISALIGNED;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_calibrate(x, n, gs_device, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_quantize_devgs(const void* x, int64_t M, int64_t K, const float* gs_device, void* packed,
+                         void* scales, void* stream) {
+  if (!x || !packed || !scales || !gs_device) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(gs_device, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_quantize(x, M, K, 1.0f, packed, scales, (hipStream_t)stream, info,
+                                        gs_device);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_gemm_devgs(const void* ap, const void* as, const float* ags_device, const void* wp,
+                     const void* ws, const float* wgs_device, int64_t M, int64_t N, int64_t K,
+                     void* out, void* stream) {
+  if (!ags_device || !wgs_device) return NVFP4_ERROR_INVALID_VALUE;
+  if (!aligned(ags_device, 4) || !aligned(wgs_device, 4)) return NVFP4_ERROR_MISALIGNED;
+  int s = validate_gemm(ap, as, 1.0f, wp, ws, 1.0f, M, N, K, out);
+  if (s) return s;
+  if (M == 0 || N == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  nvfp4::GemmProblem p{(const uint8_t*)ap, (const uint8_t*)as, (const uint8_t*)wp,
+                       (const uint8_t*)ws, (uint16_t*)out, M, N, K, 1.0f, ags_device, wgs_device};
+  hipError_t e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_linear_devgs(const void* x, const float* ags_device, const void* wp, const void* ws,
+                       const float* wgs_device, int64_t M, int64_t N, int64_t K, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !workspace || !ags_device || !wgs_device) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  const size_t packed_bytes = round_up((size_t)(M * K / 2), 256);
+  uint8_t* ap = (uint8_t*)workspace;
+  uint8_t* as = ap + packed_bytes;
+  s = validate_gemm(ap, as, 1.0f, wp, ws, 1.0f, M, N, K, out);
+  if (s) return s;
+  if (!aligned(x, 16) || !aligned(ags_device, 4) || !aligned(wgs_device, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  if (workspace_bytes < nvfp4_linear_workspace_bytes(M, K)) return NVFP4_ERROR_WORKSPACE;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_quantize(x, M, K, 1.0f, ap, as, (hipStream_t)stream, info, ags_device);
+  if (e != hipSuccess) return hip_fail(e);
+  if (N == 0) return NVFP4_SUCCESS;
+  nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
+                       M, N, K, 1.0f, ags_device, wgs_device};
+  e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
 // ---- self-test entry points ----------------------------------------------------------
 
 int nvfp4_selftest_e2m1_encode(const float* y, uint8_t* hw_codes, uint8_t* sw_codes, int64_t n,

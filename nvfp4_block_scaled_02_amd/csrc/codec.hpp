@@ -131,4 +131,12 @@ NVFP4_HD uint32_t e2m1_encode_sw(float x, float y) {
   return sign | e2m1_magnitude_encode(__builtin_fabsf(y));
 }
 
+// Global scales read from device memory: clamped into [2^-90, 2^90], the range in which
+// the quantizer's divisions are exact (NaN, and anything not above 0, read as 1).
+constexpr float kGsMin = 0x1p-90f, kGsMax = 0x1p90f;
+NVFP4_HD float clamp_global_scale(float gs) {
+  if (!(gs > 0.0f)) return 1.0f;
+  return gs < kGsMin ? kGsMin : (gs > kGsMax ? kGsMax : gs);
+}
+
 }  // namespace nvfp4

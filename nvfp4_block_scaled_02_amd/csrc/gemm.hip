@@ -850,6 +850,7 @@ __global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
   // Partial sums: block by block, every wave writes its part, the owner wave (block
   // number % 4) adds the four in wave order and stores.
   const bool n_vec = (p.N & 3) == 0;
+  const float alpha = gemm_alpha(p);
 #pragma unroll
   for (int i = 0; i < A; ++i)
 #pragma unroll
@@ -874,7 +875,7 @@ __global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
               s += rb[(1 * 16 + v) * 64 + lane];
               s += rb[(2 * 16 + v) * 64 + lane];
               s += rb[(3 * 16 + v) * 64 + lane];
-              b[e] = bf16_rne(s * p.alpha);
+              b[e] = bf16_rne(s * alpha);
             }
             if (n_vec && n + 3 < p.N) {
               *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};

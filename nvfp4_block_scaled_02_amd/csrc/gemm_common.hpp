@@ -78,6 +78,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is scaled by
 // alpha in fp32, rounded to nearest even bf16 and stored (8 bytes per lane when the row
 // pitch allows). Only column quads q in [q0, q1) are stored.
+// The epilogue scale: RN(a_global * w_global), from the launch arguments or, when the
+// global scales are device-resident, from device memory.
+__device__ __forceinline__ float gemm_alpha(const GemmProblem& p) {
+  return p.a_gs_dev != nullptr ? (*p.a_gs_dev) * (*p.w_gs_dev) : p.alpha;
+}
+
 template <int FM, int FN>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
                                            int64_t m_base, int64_t n_base, int lane, int q0 = 0,
@@ -85,6 +91,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 3) == 0;
+  const float alpha = gemm_alpha(p);
 #pragma unroll
   for (int g = 0; g < FM; ++g) {
     const int64_t m = m_base + g * 32 + r32;
@@ -98,7 +105,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
         const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
         uint32_t b[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * alpha);
         if (n_vec && n + 3 < p.N) {
           *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
         } else {
@@ -134,6 +141,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
+  const float alpha = kRowCol ? 1.0f : gemm_alpha(p);
   float sx[FM];
   u32x4 sw[FN][4];
   if constexpr (kRowCol) {
@@ -161,7 +169,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (kRowCol) b[e] = bf16_rne(acc[i][g][4 * q + e] * sx[g] * u2f(sw[i][q][e]));
-          else b[e] = bf16_rne(acc[i][g][4 * q + e] * p.alpha);
+          else b[e] = bf16_rne(acc[i][g][4 * q + e] * alpha);
         }
         *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
       }

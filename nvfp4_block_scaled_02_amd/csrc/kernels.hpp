@@ -12,8 +12,11 @@ struct LaunchInfo {
   int num_cus;  // compute units of the current device
 };
 
+// gs_dev non-null: the global scale is read on the device from *gs_dev (clamped into
+// [2^-90, 2^90], NaN read as 1) and `gs` is ignored.
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,
-                           void* scales, hipStream_t stream, const LaunchInfo& dev);
+                           void* scales, hipStream_t stream, const LaunchInfo& dev,
+                           const float* gs_dev = nullptr);
 
 struct GemmProblem {
   const uint8_t* a_packed;
@@ -23,6 +26,10 @@ struct GemmProblem {
   uint16_t* out;
   int64_t M, N, K;
   float alpha;  // RN(a_global * w_global)
+  // Device-resident global scales (both set, or both null): alpha is then
+  // RN(*a_gs_dev * *w_gs_dev), read by the kernel.
+  const float* a_gs_dev;
+  const float* w_gs_dev;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
@@ -62,6 +69,10 @@ hipError_t launch_mx_selftest_e4m3_exhaustive(unsigned long long* count, uint32_
 
 hipError_t launch_amax(const void* x, int64_t n, float* out, hipStream_t stream,
                        const LaunchInfo& dev);
+// amax of x, then in place the global scale from it: RN(amax / 2688) clamped into
+// [2^-90, 2^90], 1 for amax == 0.
+hipError_t launch_calibrate(const void* x, int64_t n, float* gs, hipStream_t stream,
+                            const LaunchInfo& dev);
 
 // self-test support
 hipError_t launch_selftest_encode(const float* y, uint8_t* hw, uint8_t* sw, int64_t n,

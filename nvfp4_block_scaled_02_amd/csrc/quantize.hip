@@ -67,7 +67,12 @@ __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__
                                                        uint32_t* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
                                                        int64_t nhalves, float gs, float den,
-                                                       float rden) {
+                                                       float rden, const float* gs_dev) {
+  if (gs_dev != nullptr) {  // device-resident global scale: same arithmetic as the host's
+    gs = clamp_global_scale(*gs_dev);
+    den = 6.0f * gs;
+    rden = 1.0f / den;
+  }
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * UNROLL;
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nhalves;
        base += stride) {
@@ -108,7 +113,8 @@ __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,
-                           void* scales, hipStream_t stream, const LaunchInfo& dev) {
+                           void* scales, hipStream_t stream, const LaunchInfo& dev,
+                           const float* gs_dev) {
   const int64_t nhalves = M * (K / 16) * 2;
   if (nhalves == 0) return hipSuccess;
 #ifndef NVFP4_QUANT_UNROLL
@@ -127,7 +133,8 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
   const int64_t cap = (int64_t)dev.num_cus * NVFP4_QUANT_WG_PER_CU;
   const int grid = (int)(want < cap ? want : cap);
   hipLaunchKernelGGL((quantize_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const u32x4*)x, (uint32_t*)packed, (uint8_t*)scales, nhalves, gs, den, rden);
+                     (const u32x4*)x, (uint32_t*)packed, (uint8_t*)scales, nhalves, gs, den, rden,
+                     gs_dev);
   return hipGetLastError();
 }
 

@@ -36,9 +36,24 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
-def quantize(x: torch.Tensor, global_scale: float, packed: torch.Tensor | None = None,
+def _dev_scale(v, name: str):
+    """A device-resident global scale (a float32 tensor with one element) or None for a
+    host float."""
+    if not isinstance(v, torch.Tensor):
+        return None
+    if v.dtype != torch.float32 or v.numel() != 1:
+        raise TypeError(f"{name} as a tensor must be float32 with one element")
+    if not v.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    return v
+
+
+def quantize(x: torch.Tensor, global_scale, packed: torch.Tensor | None = None,
              scales: torch.Tensor | None = None, stream=None):
-    """NVFP4-quantize bf16 ``x`` [M, K] -> (packed uint8 [M, K/2], scales uint8 [M, K/16])."""
+    """NVFP4-quantize bf16 ``x`` [M, K] -> (packed uint8 [M, K/2], scales uint8 [M, K/16]).
+
+    ``global_scale`` is a float, or a device float32 tensor of one element (read by the
+    kernel, no host round trip; see :func:`calibrate_device`)."""
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
     if K % 16:
@@ -52,15 +67,21 @@ def quantize(x: torch.Tensor, global_scale: float, packed: torch.Tensor | None =
     if tuple(packed.shape) != (M, K // 2) or tuple(scales.shape) != (M, K // 16):
         raise ValueError("output shapes do not match x")
     lib = load_library()
-    check(lib.nvfp4_quantize(_ptr(x), M, K, float(global_scale), _ptr(packed), _ptr(scales),
-                             _stream(stream)), "nvfp4_quantize")
+    gsd = _dev_scale(global_scale, "global_scale")
+    if gsd is not None:
+        check(lib.nvfp4_quantize_devgs(_ptr(x), M, K, _ptr(gsd), _ptr(packed), _ptr(scales),
+                                       _stream(stream)), "nvfp4_quantize_devgs")
+    else:
+        check(lib.nvfp4_quantize(_ptr(x), M, K, float(global_scale), _ptr(packed), _ptr(scales),
+                                 _stream(stream)), "nvfp4_quantize")
     return packed, scales
 
 
-def gemm(a_packed: torch.Tensor, a_scales: torch.Tensor, a_global_scale: float,
-         w_packed: torch.Tensor, w_scales: torch.Tensor, w_global_scale: float,
+def gemm(a_packed: torch.Tensor, a_scales: torch.Tensor, a_global_scale,
+         w_packed: torch.Tensor, w_scales: torch.Tensor, w_global_scale,
          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Block-scaled W4A4 GEMM: bf16 [M, N] = a_gs * w_gs * A_hat @ W_hat^T."""
+    """Block-scaled W4A4 GEMM: bf16 [M, N] = a_gs * w_gs * A_hat @ W_hat^T. The global
+    scales are both floats or both device float32 tensors of one element."""
     for t, n in ((a_packed, "a_packed"), (a_scales, "a_scales"), (w_packed, "w_packed"),
                  (w_scales, "w_scales")):
         _need(t, n, torch.uint8, 2)
@@ -76,9 +97,17 @@ def gemm(a_packed: torch.Tensor, a_scales: torch.Tensor, a_global_scale: float,
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape must be [M, N]")
     lib = load_library()
-    check(lib.nvfp4_gemm(_ptr(a_packed), _ptr(a_scales), float(a_global_scale), _ptr(w_packed),
-                         _ptr(w_scales), float(w_global_scale), M, N, K, _ptr(out),
-                         _stream(stream)), "nvfp4_gemm")
+    ad, wd = _dev_scale(a_global_scale, "a_global_scale"), _dev_scale(w_global_scale, "w_global_scale")
+    if (ad is None) != (wd is None):
+        raise TypeError("global scales must be both floats or both device tensors")
+    if ad is not None:
+        check(lib.nvfp4_gemm_devgs(_ptr(a_packed), _ptr(a_scales), _ptr(ad), _ptr(w_packed),
+                                   _ptr(w_scales), _ptr(wd), M, N, K, _ptr(out), _stream(stream)),
+              "nvfp4_gemm_devgs")
+    else:
+        check(lib.nvfp4_gemm(_ptr(a_packed), _ptr(a_scales), float(a_global_scale), _ptr(w_packed),
+                             _ptr(w_scales), float(w_global_scale), M, N, K, _ptr(out),
+                             _stream(stream)), "nvfp4_gemm")
     return out
 
 
@@ -201,10 +230,11 @@ def linear_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().nvfp4_linear_workspace_bytes(M, K))
 
 
-def linear(x: torch.Tensor, a_global_scale: float, w_packed: torch.Tensor,
-           w_scales: torch.Tensor, w_global_scale: float, out: torch.Tensor | None = None,
+def linear(x: torch.Tensor, a_global_scale, w_packed: torch.Tensor,
+           w_scales: torch.Tensor, w_global_scale, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Fused NVFP4 linear: quantize x under a_global_scale, then the W4A4 GEMM."""
+    """Fused NVFP4 linear: quantize x under a_global_scale, then the W4A4 GEMM. The global
+    scales are both floats or both device float32 tensors of one element."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_packed, "w_packed", torch.uint8, 2)
     _need(w_scales, "w_scales", torch.uint8, 2)
@@ -222,9 +252,17 @@ def linear(x: torch.Tensor, a_global_scale: float, w_packed: torch.Tensor,
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape must be [M, N]")
     lib = load_library()
-    check(lib.nvfp4_linear(_ptr(x), float(a_global_scale), _ptr(w_packed), _ptr(w_scales),
-                           float(w_global_scale), M, N, K, _ptr(out), _ptr(workspace),
-                           workspace.numel(), _stream(stream)), "nvfp4_linear")
+    ad, wd = _dev_scale(a_global_scale, "a_global_scale"), _dev_scale(w_global_scale, "w_global_scale")
+    if (ad is None) != (wd is None):
+        raise TypeError("global scales must be both floats or both device tensors")
+    if ad is not None:
+        check(lib.nvfp4_linear_devgs(_ptr(x), _ptr(ad), _ptr(w_packed), _ptr(w_scales), _ptr(wd),
+                                     M, N, K, _ptr(out), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)), "nvfp4_linear_devgs")
+    else:
+        check(lib.nvfp4_linear(_ptr(x), float(a_global_scale), _ptr(w_packed), _ptr(w_scales),
+                               float(w_global_scale), M, N, K, _ptr(out), _ptr(workspace),
+                               workspace.numel(), _stream(stream)), "nvfp4_linear")
     return out
 
 
@@ -251,6 +289,20 @@ def amax(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch
 def global_scale_from_amax(a: float) -> float:
     """RN32(amax / 2688) computed by the library (1.0 for amax == 0)."""
     return float(load_library().nvfp4_global_scale_from_amax(float(a)))
+
+
+def calibrate_device(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Global scale of a bf16 tensor computed and kept on the device: a float32 tensor of
+    one element holding RN32(amax / 2688) clamped into [2^-90, 2^90] (1 for an all-zero
+    tensor). Asynchronous; pass it straight to :func:`quantize`, :func:`gemm` or
+    :func:`linear`."""
+    _need(x, "x", torch.bfloat16, x.dim())
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _dev_scale(out, "out")
+    check(load_library().nvfp4_calibrate_device(_ptr(x), x.numel(), _ptr(out), _stream(stream)),
+          "nvfp4_calibrate_device")
+    return out
 
 
 def calibrate(x: torch.Tensor, stream=None) -> float:

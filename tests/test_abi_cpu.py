@@ -186,6 +186,38 @@ def test_fp8r_validation(lib):
     assert call({5: 0}) == L.SUCCESS
 
 
+def test_device_scale_validation(lib):
+    c = lib.nvfp4_calibrate_device
+    assert c(NULL, 64, P16b, NULL) == L.INVALID_VALUE
+    assert c(P16, 64, NULL, NULL) == L.INVALID_VALUE
+    assert c(P16, -1, P16b, NULL) == L.INVALID_SHAPE
+    assert c(ODD, 64, P16b, NULL) == L.MISALIGNED
+    assert c(P16, 64, ctypes.c_void_p(0x20002), NULL) == L.MISALIGNED
+    q = lib.nvfp4_quantize_devgs
+    assert q(P16, 4, 64, NULL, P16, P16b, NULL) == L.INVALID_VALUE
+    assert q(P16, 4, 40, P16b, P16, P16b, NULL) == L.INVALID_SHAPE
+    assert q(P16, 4, 64, ctypes.c_void_p(0x20002), P16, P16b, NULL) == L.MISALIGNED
+    assert q(P16, 0, 64, P16b, P16, P16b, NULL) == L.SUCCESS
+    g = lib.nvfp4_gemm_devgs
+    args = [P16, P16b, P16b, P16, P16b, P16b, 8, 8, 64, P16, NULL]
+
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return g(*a)
+
+    for k in (0, 1, 2, 3, 4, 5, 9):
+        assert call({k: NULL}) == L.INVALID_VALUE
+    assert call({8: 40}) == L.INVALID_SHAPE
+    assert call({2: ctypes.c_void_p(0x20002)}) == L.MISALIGNED
+    assert call({6: 0}) == L.SUCCESS
+    li = lib.nvfp4_linear_devgs
+    assert li(P16, NULL, P16, P16b, P16b, 8, 8, 64, P16, P16, 1 << 20, NULL) == L.INVALID_VALUE
+    assert li(P16, P16b, P16, P16b, P16b, 8, 8, 64, P16, P16, 16, NULL) == L.WORKSPACE
+    assert li(P16, P16b, P16, P16b, P16b, 0, 8, 64, P16, P16, 1 << 20, NULL) == L.SUCCESS
+
+
 def test_mxfp8_validation(lib):
     q = lib.nvfp4_mxfp8_quantize
     assert q(NULL, 4, 64, P16, P16b, NULL) == L.INVALID_VALUE
