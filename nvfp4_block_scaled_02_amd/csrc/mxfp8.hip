@@ -312,6 +312,209 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
                                    lane, (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
+// ---- GEMM, 288 x 192 tiles ---------------------------------------------------------------
+//
+// The same product on 288 x 192 tiles: 4608 = 16 x 288 and every FLUX width (3072, 9216,
+// 12288) is a multiple of 192, so these products split into whole multiples of 256 tiles
+// (the 256 x 256 tile gives 216 tiles on 256 compute units for 4608 x 3072). The tile is
+// 9 x 6 blocks of 32 x 32; wave (m, n) owns weight groups 3n..3n+2 and activation groups
+// 0..3 (m = 0) or 5..8 (m = 1), and the middle activation group 4 is split by weight
+// block: wave (0, n) takes its blocks with weight groups 3n and 3n+1, wave (1, n) the one
+// with 3n+2. So the waves issue 14 and 13 MFMAs per stage (the 256 x 256 tile: 16) and no
+// partial sums need to meet. Loads, LDS layout and the stage pipeline are those of the
+// 256 x 256 kernel: 4 code buffers of 30 KiB and 2 scale buffers of 8 KiB (activation
+// scale rows rounded up to whole 64-row pieces), 136 KiB in all.
+template <int BM, int BN>
+struct alignas(16) MxFitSmem {
+  static constexpr int kScaleRowsX = (BM + 63) / 64 * 64;
+  uint8_t x[4][BM * 64];
+  uint8_t w[4][BN * 64];
+  uint8_t sc[2][(kScaleRowsX + BN) * 16];
+};
+
+// One wave's program; kS = number of middle-group blocks this wave owns (2 or 1).
+template <int BM, int BN, bool kRowwise, int kS>
+__device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, BN>& sm, int lane,
+                                            int wave, int m0, int n0) {
+  constexpr int NW = 4;
+  constexpr int GX = BM / 32, GW = BN / 32;
+  static_assert(GX * 32 == BM && GW * 32 == BN && GX % 2 == 1 && GW % 2 == 0, "fit tile shape");
+  constexpr int FM = GX / 2;  // whole activation groups per wave
+  constexpr int FN = GW / 2;  // weight groups per wave
+  constexpr int GS = FM;      // the middle activation group
+  constexpr int kI0 = kS == FN - 1 ? 0 : FN - kS;  // first weight block of the middle group
+  constexpr int kPa = BM / 16, kPw = BN / 16;
+  constexpr int kPaW = (kPa + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW;
+  constexpr int kLoads = kPaW + kPwW;
+  constexpr int kRowsSx = MxFitSmem<BM, BN>::kScaleRowsX;
+  constexpr int kSx = kRowsSx / 64;
+  static_assert(BN % 64 == 0 && (kSx + BN / 64) % NW == 0, "scale pieces divide among waves");
+  constexpr int kSLoads = kRowwise ? 0 : (kSx + BN / 64) / NW;
+  constexpr int kMfma = FN * FM + kS;
+  static_assert(kLoads + kSLoads <= kMfma && kLoads + kSLoads < 16, "loads fit the schedule");
+
+  const int wave_n = wave & 1;
+  const int wave_m = wave >> 1;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const int nk = (int)(p.K / 64);
+  const int ngrp = (nk + 7) >> 3;
+  const uint32_t pitch = (uint32_t)p.K;
+  const uint32_t spitch = (uint32_t)(p.K >> 5);
+
+  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
+  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const int lr = lane >> 2;
+  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
+  const uint32_t voff_s = lane * spitch;
+
+  auto issue_codes = [&](int j, int stage, int buf) {
+    if (j < kPaW) {
+      const int i = min(j * NW + wave, kPa - 1);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_c,
+                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+    } else {
+      const int i = min((j - kPaW) * NW + wave, kPw - 1);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_c,
+                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+    }
+  };
+  // scale piece j * NW + wave (64 rows x 16 bytes): activation rows first, then weight
+  // rows (selects, no branch)
+  auto issue_scales = [&](int j, int grp, int sbuf) {
+    const int i = j * NW + wave;
+    const bool isx = i < kSx;
+    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sbuf][i * 1024], voff_s, row * spitch + (uint32_t)grp * 16);
+  };
+
+  floatx16 acc[FN][FM], accs[kS];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accs[s][v] = 0.0f;
+
+  // fragments: weights FN, activations FM + the middle group (index FM)
+  v8i_t wf[2][FN], xf[2][FM + 1];
+  int wsc[2][FN], xsc[2][FM + 1];
+  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
+  const int fr1 = fr0 ^ 32;
+  const int xg0 = wave_m ? GS + 1 : 0;
+  // LDS reads of a stage in the order the MFMAs need them: w0, x0..x(FM-1), w1, .., the
+  // middle group last; read k is a fragment half or a scale byte
+  constexpr int kFrags = FN + FM + 1;
+  constexpr int kReads = 3 * kFrags;
+  auto read_one = [&](int k, int par, int buf, int stage) {
+    const int sbuf = (stage >> 3) & 1;
+    const int sbyte = (stage & 7) * 2 + h;
+    const int f = k / 3, part = k % 3;
+    const bool is_w = f == 0 || (f > FM && f < kFrags - 1);
+    const int idx = f == 0 ? 0 : (f <= FM ? f - 1 : (f < kFrags - 1 ? f - FM : FM));
+    const int grp = is_w ? wave_n * FN + idx : (idx < FM ? xg0 + idx : GS);
+    const uint8_t* base = is_w ? &sm.w[buf][grp * 2048] : &sm.x[buf][grp * 2048];
+    if (part < 2) {
+      const u32x4 a = *(const u32x4*)&base[part ? fr1 : fr0];
+      const int o = 4 * part;
+      if (is_w) {
+        wf[par][idx][o] = (int)a.x; wf[par][idx][o + 1] = (int)a.y;
+        wf[par][idx][o + 2] = (int)a.z; wf[par][idx][o + 3] = (int)a.w;
+      } else {
+        xf[par][idx][o] = (int)a.x; xf[par][idx][o + 1] = (int)a.y;
+        xf[par][idx][o + 2] = (int)a.z; xf[par][idx][o + 3] = (int)a.w;
+      }
+    } else if (!kRowwise) {
+      const int row = is_w ? kRowsSx + grp * 32 + r32 : grp * 32 + r32;
+      const int v = sm.sc[sbuf][row * 16 + sbyte];
+      if (is_w) wsc[par][idx] = v;
+      else xsc[par][idx] = v;
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kSLoads; ++j) issue_scales(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 1 ? 1 : nk - 1, 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 2 ? 2 : nk - 1, 2);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int k = 0; k < kReads; ++k) read_one(k, 0, 0, 0);
+
+  auto stage = [&](int t, int buf, const int cur, const bool sload) {
+    const int nbuf = (buf + 1) & 3;
+    const int lbuf = (buf + 3) & 3;
+    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
+    const int rstage = t + 1 < nk ? t + 1 : t;
+    const int sgrp = (t >> 3) + 1 < ngrp ? (t >> 3) + 1 : ngrp - 1;
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      if (q < FN * FM) {
+        const int i = q / FM, g = q % FM;
+        acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+            kRowwise ? 127 : xsc[cur][g]);
+      } else {
+        const int sidx = q - FN * FM, i = kI0 + sidx;
+        accs[sidx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            wf[cur][i], xf[cur][FM], accs[sidx], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+            kRowwise ? 127 : xsc[cur][FM]);
+      }
+      if (q < kLoads) issue_codes(q, lstage, lbuf);
+      else if (q < kLoads + kSLoads && sload) issue_scales(q - kLoads, sgrp, ((t >> 3) + 1) & 1);
+#pragma unroll
+      for (int k = q * kReads / kMfma; k < (q + 1) * kReads / kMfma; ++k) read_one(k, cur ^ 1, nbuf, rstage);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sload) wait_vmcnt<kLoads + kSLoads>();
+    else wait_vmcnt<kLoads>();
+    __builtin_amdgcn_s_barrier();
+  };
+  int t = 0;
+  for (; t + 8 <= nk; t += 8) {
+    stage(t, 0, 0, true);
+#pragma unroll
+    for (int u = 1; u < 8; ++u) stage(t + u, u & 3, u & 1, false);
+  }
+  for (; t < nk; t += 2) {
+    stage(t, t & 3, 0, false);
+    stage(t + 1, (t + 1) & 3, 1, false);
+  }
+
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  uint16_t* blk = (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN);
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
+  const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
+  store_tile_lds<FM, FN, kRowwise>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane, blk);
+  store_tile_lds<1, kS, kRowwise>(*(const floatx16(*)[kS][1])&accs, p, (int64_t)m0 + GS * 32,
+                                  n_base + kI0 * 32, lane, blk);
+}
+
+template <int BM, int BN, bool kRowwise>
+__global__ void __launch_bounds__(256) gemm_mx_fit_kernel(GemmProblem p) {
+  __shared__ MxFitSmem<BM, BN> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  int tile_m, tile_n;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  constexpr int FN = BN / 64;
+  if ((wave >> 1) == 0) mx_fit_wave<BM, BN, kRowwise, FN - 1>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
+  else mx_fit_wave<BM, BN, kRowwise, 1>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
+}
+
 // ---- self-test: the fp8 conversion against the software E4M3 encoder ----------------
 
 // Every binary32 pattern except NaN and Inf: y clamped to [-448, 448] as the quantizer
@@ -349,22 +552,37 @@ hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* codes, 
   return hipGetLastError();
 }
 
-hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  (void)dev;
-  constexpr int BM = 256, BN = 256;
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+namespace {
+
+// 288 x 192 or 256 x 256 tiles: the fit tile issues 14 MFMAs per wave and stage (the
+// other 16), so it wins unless it needs more passes over the compute units.
+template <bool kRowwise>
+hipError_t launch_fp8_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
+  const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
+  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const int64_t tfit = ((p.M + 287) / 288) * ((p.N + 191) / 192);
+  const bool fit32 = (p.M + 320) * p.K < ((int64_t)1 << 31) && (p.N + 192) * p.K < ((int64_t)1 << 31);
+  const int64_t pass256 = (t256 + cus - 1) / cus, passfit = (tfit + cus - 1) / cus;
+  if (fit32 && passfit * 14 <= pass256 * 16) {
+    if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_mx_fit_kernel<288, 192, kRowwise>), dim3((unsigned)tfit), dim3(256), 0,
+                       stream, p);
+  } else {
+    if (t256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_mx_kernel<256, 256, kRowwise>), dim3((unsigned)t256), dim3(256), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
+  return launch_fp8_gemm<false>(p, stream, dev);
+}
+
 hipError_t launch_fp8r_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  (void)dev;
-  constexpr int BM = 256, BN = 256;
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_fp8_gemm<true>(p, stream, dev);
 }
 
 hipError_t launch_mx_selftest_e4m3_exhaustive(unsigned long long* count, uint32_t* first,

@@ -89,6 +89,8 @@ def _gemm_dev(ac, as_, wc, ws, guard=True):
 @pytest.mark.parametrize("M,N,K", [
     (64, 128, 256), (1, 64, 128), (17, 72, 128), (256, 256, 256), (300, 520, 384),
     (513, 261, 1024), (255, 257, 128), (7, 3, 128), (130, 1030, 640),
+    (600, 400, 1152), (289, 193, 640),
+    (4096, 4096, 128),   # runs on the 256 x 256 kernel (one pass; the fit tile needs two)
 ])
 def test_gemm_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 13 + N * 7 + K)

@@ -86,6 +86,11 @@ def _gemm_dev(ac, as_, wc, ws, guard=True):
 @pytest.mark.parametrize("M,N,K", [
     (64, 128, 256), (1, 64, 128), (17, 72, 128), (256, 256, 256), (300, 520, 384),
     (513, 260, 1024), (255, 257, 128), (7, 3, 128),
+    # 288 x 192 tiles with ragged edges and several 8-stage scale groups (K = 1152)
+    (600, 400, 1152), (289, 193, 640),
+    # 4096 x 4096: 256 x 256 tiles need one pass over 256 compute units, 288 x 192 two,
+    # so this one runs on the 256 x 256 kernel
+    (4096, 4096, 128),
 ])
 def test_gemm_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 11 + N * 5 + K)
