@@ -167,10 +167,176 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
   }
 }
 
+// ---- tiled form for long activations -------------------------------------------------
+//
+// 256 x 256 output tiles, 2 x 2 waves of 128 x 128 (4 x 4 blocks of 32 x 32), the bf16
+// MFMA with the decoded weights as its A operand. A stage is 64 elements of K:
+//  * activations: 256 rows x 128 bytes (bf16). A direct-to-LDS load fills 8 rows x 128
+//    bytes (8 lanes per row, 1 KiB). In LDS each row's 16-byte chunk c sits at slot
+//    c ^ x_swz(r) (r = row within its 32-row group), so the fragment reads (lane (h, r)
+//    reads chunk 4h + j on k-step j) hit distinct banks;
+//  * weights: 256 rows x 32 bytes of codes (per 32-row group 64 slots of 16 bytes in
+//    MFMA lane order, loaded as 32 rows x 32 bytes) and 256 rows x 4 scale bytes.
+// Three stage buffers (3 x 41 KiB); stage t+2's loads are issued during stage t; at the
+// end of stage t each wave waits for the loads it issued before stage t and the
+// workgroup meets at a barrier, so stage t+1 is complete when it starts. A stage reads
+// its fragments k-step by k-step, one k-step ahead of its MFMAs.
+__device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+template <int BM, int BN>
+struct alignas(16) W4A16Smem {
+  uint8_t x[3][BM * 128];
+  uint8_t w[3][BN * 32];
+  uint8_t ws[3][BN * 4];
+};
+
+// Requires K % 64 == 0, 16-byte aligned x, codes and out, 4-byte aligned scales, and
+// (M + 256) * K * 2 and (N + 256) * K / 2 below 2^31 (32-bit buffer offsets).
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) gemm_w4a16_tile_kernel(W4A16Problem p) {
+  constexpr int NW = 4, WM = 2, WN = 2;
+  __shared__ W4A16Smem<BM, BN> sm;
+  constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+  constexpr int kPx = BM / 8, kPw = BN / 32, kPs = BN / 64;  // loads per stage
+  static_assert(kPx % NW == 0 && kPw % NW == 0 && kPs % NW == 0, "loads divide among waves");
+  constexpr int kPxW = kPx / NW, kPwW = kPw / NW, kPsW = kPs / NW;
+  constexpr int kLoads = kPxW + kPwW + kPsW;
+  static_assert(kLoads < 16, "one stage of loads fits the vmcnt immediate");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_n = wave % WN;
+  const int wave_m = wave / WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  int tile_m, tile_n;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int nk = (int)(p.K / 64);
+  const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * xpitch);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const int xr = lane >> 3;  // row (within 8) of an activation load
+  const uint32_t voff_w = r32 * pitch + h * 16;
+  const uint32_t voff_s = lane * spitch;
+
+  // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
+  auto issue = [&](int j, int stage, int buf) {
+    if (j < kPxW) {
+      const int i = j * NW + wave;  // rows 8i .. 8i+7 of the tile
+      const int row = 8 * i + xr;
+      const uint32_t voff = xr * xpitch + 16 * ((lane & 7) ^ x_swz(row & 31));
+      buffer_load_lds16(rx, &sm.x[buf][i * 1024], voff, (uint32_t)(m0 + 8 * i) * xpitch + (uint32_t)stage * 128);
+    } else if (j < kPxW + kPwW) {
+      const int i = (j - kPxW) * NW + wave;  // weight group i
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], voff_w, (uint32_t)(n0 + 32 * i) * pitch + (uint32_t)stage * 32);
+    } else {
+      const int i = (j - kPxW - kPwW) * NW + wave;  // weight rows 64i .. 64i+63
+      buffer_load_lds4(rs, &sm.ws[buf][i * 256], voff_s, (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)stage * 4);
+    }
+  };
+
+  floatx16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  const int xs0 = 16 * ((4 * h) ^ x_swz(r32));  // k-step j: slot offset xs0 ^ (16 j)
+  u32x4 wraw[FN];
+  float wsc_lo[FN], wsc_hi[FN];
+  bf16x8_t wf[2][FN], xf[2][FM];
+  auto read_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      wraw[i] = *(const u32x4*)&sm.w[buf][(wave_n * FN + i) * 1024 + lane * 16];
+      const uint32_t sw = *(const uint16_t*)&sm.ws[buf][(wave_n * FN * 32 + i * 32 + r32) * 4 + 2 * h];
+      wsc_lo[i] = e4m3_decode(sw & 0xFFu);
+      wsc_hi[i] = e4m3_decode(sw >> 8);
+    }
+  };
+  auto read_x = [&](int slot, int buf, int j) {
+#pragma unroll
+    for (int g = 0; g < FM; ++g) {
+      const u32x4 v = *(const u32x4*)&sm.x[buf][(wave_m * FM + g) * 4096 + r32 * 128 + (xs0 ^ (16 * j))];
+      xf[slot][g] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  auto decode_w = [&](int slot, int j) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wf[slot][i] = decode8_bf16(wraw[i][j], j < 2 ? wsc_lo[i] : wsc_hi[i]);
+  };
+
+  // prologue: stages 0 and 1
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, nk > 1 ? 1 : 0, 1);
+  wait_vmcnt<kLoads>();
+  __builtin_amdgcn_s_barrier();
+
+  int buf = 0;
+  for (int t = 0; t < nk; ++t) {
+    const int lbuf = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
+    const int lstage = t + 2 < nk ? t + 2 : nk - 1;
+    read_w(buf);
+    read_x(0, buf, 0);
+    decode_w(0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cur = j & 1;
+      if (j < 3) {
+        read_x(cur ^ 1, buf, j + 1);
+        decode_w(cur ^ 1, j + 1);
+      }
+#pragma unroll
+      for (int l = 0; l < (kLoads + 3) / 4; ++l)
+        if (j * ((kLoads + 3) / 4) + l < kLoads) issue(j * ((kLoads + 3) / 4) + l, lstage, lbuf);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
+    }
+    wait_vmcnt<kLoads>();
+    __builtin_amdgcn_s_barrier();
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  GemmProblem q{};
+  q.out = p.out;
+  q.M = p.M;
+  q.N = p.N;
+  q.K = p.K;
+  q.alpha = p.alpha;
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
+  store_tile_lds<FM, FN>(acc, q, (int64_t)m0 + wave_m * FM * 32, (int64_t)n0 + wave_n * FN * 32, lane,
+                         (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
-  (void)dev;
+  // long activations: the tiled kernel when its tiles cover at least a quarter of the
+  // compute units (as the W4A4 planner)
+  const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
+  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const bool fits32 = (p.M + 256) * p.K * 2 < ((int64_t)1 << 31) && (p.N + 256) * (p.K / 2) < ((int64_t)1 << 31);
+  const bool aligned = (uintptr_t)p.x % 16 == 0 && (uintptr_t)p.w_packed % 16 == 0 &&
+                       (uintptr_t)p.w_scales % 4 == 0;
+  if (p.K % 64 == 0 && fits32 && aligned && tiles * 4 > cus) {
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   // workgroup shape: 32 weight rows x 32B activation rows, B the smallest of 1, 2, 4 that
   // covers min(M, 128) rows
   const int B = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);

@@ -36,6 +36,9 @@ def _check(got, x, wp, ws, wgs, label):
 @pytest.mark.parametrize("M,N,K", [
     (1, 64, 64), (17, 72, 128), (33, 100, 96), (64, 3000, 224), (130, 70, 256),
     (5, 5, 32), (300, 200, 1056), (64, 128, 256),
+    # enough 256 x 256 tiles (more than a quarter of the compute units) for the tiled
+    # kernel: ragged by one row and column, one stage (K = 64), several stages
+    (2049, 2081, 64), (2300, 2000, 192), (2304, 2048, 640),
 ])
 def test_w4a16_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
