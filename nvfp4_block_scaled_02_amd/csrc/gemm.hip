@@ -270,99 +270,82 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
   store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
-// ---- fast path: direct-to-LDS loads, three LDS stages, one pipeline across stages ----
-
-template <int BM, int BN, int KC>
-struct alignas(16) GemmSmem3 {
-  uint8_t x[3][KC][BM * 32];
-  uint8_t w[3][KC][BN * 32];
-  uint32_t xs[3][KC][BM];
-  uint32_t ws[3][KC][BN];
+// ---- 256 x 256 tiles: direct-to-LDS loads, four code stages, one pipeline across stages ----
+//
+// 2 x 2 waves of 128 x 128 (4 x 4 blocks of 32 x 32). Loads, LDS image and stage pipeline
+// are the fit kernel's (below): code loads of 16 rows x the stage's 64 bytes (4 lanes per
+// row) into 1 KiB pieces whose 16-byte chunks are swizzled by chunk_swz, scale loads of
+// 64 rows x 16 bytes (a pair of stages) into three pair buffers, four code buffers filled
+// three stages ahead, one wait and barrier per stage; range-checked buffer loads, so a
+// ragged tile needs no clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS.
+template <int BM, int BN>
+struct alignas(16) GemmSmem256 {
+  uint8_t x[4][BM * 64];
+  uint8_t w[4][BN * 64];
+  uint8_t sc[3][(BM + BN) * 16];
 };
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
+// Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
+// (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
+  constexpr int NW = 4, WM = 2, WN = 2;
+  __shared__ GemmSmem256<BM, BN> sm;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int kSteps = 8;  // 16-element k-steps per stage (two chunks of 4)
+  constexpr int kPa = BM / 16, kPw = BN / 16;
+  static_assert(kPa % NW == 0 && kPw % NW == 0, "code pieces divide among waves");
+  constexpr int kPaW = kPa / NW, kPwW = kPw / NW;
+  constexpr int kSx = BM / 64;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && kSx + BN / 64 == 2 * NW, "one scale load per wave and stage");
+  constexpr int kLoadsPerWave = kPaW + kPwW + 1;
+  static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
+  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
 
-// One direct-to-LDS load per lane: 16 (or 4) bytes from src to lds_base + lane * 16 (4).
-__device__ __forceinline__ void dma_load16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma_load4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
-}
-
-// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0; other counters free).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Requires K % (64 * KC) == 0, 16-byte aligned packed operands and 4-byte aligned scales.
-//
-// Stage t (64*KC elements of K) lives in LDS buffer t % 3. Its direct-to-LDS loads are
-// issued during stage t-2, spread over the k-steps; at the end of every stage each wave
-// waits for its own loads and the workgroup synchronises, so stage t+1 is complete in
-// LDS while stage t computes. That lets the k-step pipeline run across stage
-// boundaries: the first chunk of stage t+1 is read and its first k-step decoded while
-// the last MFMAs of stage t run. Each lane of a load instruction fills one 16-byte slot
-// of the fragment layout (32 rows x 32 bytes per instruction), so the LDS image is
-// identical to the register-staged kernel's.
-template <int BM, int BN, int KC, int WM, int WN, bool kHw>
-__global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
-  constexpr int NW = WM * WN;
-  __shared__ GemmSmem3<BM, BN, KC> sm;
-  constexpr int WTM = BM / WM;
-  constexpr int WTN = BN / WN;
-  constexpr int FM = WTM / 32;
-  constexpr int FN = WTN / 32;
-  constexpr int kSteps = 4 * KC;
-  static_assert(KC % 2 == 0, "chunk parity must repeat every stage");
-  // Per stage: KC*BM/32 + KC*BN/32 packed loads and KC*BM/64 + KC*BN/64 scale loads.
-  constexpr int kPa = KC * BM / 32, kPw = KC * BN / 32, kSa = KC * BM / 64, kSw = KC * BN / 64;
-  static_assert(kPa % NW == 0 && kPw % NW == 0 && kSa % NW == 0 && kSw % NW == 0,
-                "loads must divide evenly among waves");
-  constexpr int kLoadsPerWave = (kPa + kPw + kSa + kSw) / NW;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_n = wave % WN;
   const int wave_m = wave / WN;
   const int h = lane >> 5;
   const int r32 = lane & 31;
 
-  const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t tile_m = blockIdx.x / tiles_n;
-  const int64_t tile_n = blockIdx.x % tiles_n;
-  const int64_t m0 = tile_m * BM;
-  const int64_t n0 = tile_n * BN;
-  const int64_t nk = p.K / (64 * KC);
-  const int64_t pitch = p.K >> 1;
-  const int64_t spitch = p.K >> 4;
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  int tile_m, tile_n;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM;
+  const int n0 = tile_n * BN;
+  const int nk = (int)(p.K / 128);
+  const int npair = (nk + 1) >> 1;
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
 
-  // The j-th load of this wave for stage `stage` into LDS buffer `buf`. The load list is
-  // [packed x | packed w | scales x | scales w]; load number j*NW + wave.
-  auto issue = [&](int j, int64_t stage, int buf) {
-    int i = j * NW + wave;
-    if (j * NW < kPa) {  // packed activations: (chunk, 32-row group)
-      const int kc = i / (BM / 32), g = i % (BM / 32);
-      int64_t row = m0 + g * 32 + r32;
-      row = row < p.M ? row : p.M - 1;
-      dma_load16(p.a_packed + row * pitch + (stage * KC + kc) * 32 + h * 16, &sm.x[buf][kc][g * 1024]);
-    } else if (j * NW < kPa + kPw) {
-      i -= kPa;
-      const int kc = i / (BN / 32), g = i % (BN / 32);
-      int64_t row = n0 + g * 32 + r32;
-      row = row < p.N ? row : p.N - 1;
-      dma_load16(p.w_packed + row * pitch + (stage * KC + kc) * 32 + h * 16, &sm.w[buf][kc][g * 1024]);
-    } else if (j * NW < kPa + kPw + kSa) {  // scales: (chunk, 64-row group), 4 bytes per row
-      i -= kPa + kPw;
-      const int kc = i / (BM / 64), g = i % (BM / 64);
-      int64_t row = m0 + g * 64 + lane;
-      row = row < p.M ? row : p.M - 1;
-      dma_load4(p.a_scales + row * spitch + (stage * KC + kc) * 4, &sm.xs[buf][kc][g * 64]);
+  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
+  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const int lr = lane >> 2;
+  const uint32_t voff_p = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
+  const uint32_t voff_s = lane * spitch;
+
+  auto issue_scale = [&](int pair, int half, int sb) {
+    const int i = half * NW + wave;
+    const bool isx = i < kSx;
+    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024], voff_s, row * spitch + (uint32_t)pair * 16);
+  };
+  auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
+    if (j < kPaW) {
+      const int i = j * NW + wave;
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_p,
+                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+    } else if (j < kPaW + kPwW) {
+      const int i = (j - kPaW) * NW + wave;
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_p,
+                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
     } else {
-      i -= kPa + kPw + kSa;
-      const int kc = i / (BN / 64), g = i % (BN / 64);
-      int64_t row = n0 + g * 64 + lane;
-      row = row < p.N ? row : p.N - 1;
-      dma_load4(p.w_scales + row * spitch + (stage * KC + kc) * 4, &sm.ws[buf][kc][g * 64]);
+      issue_scale(spair, t & 1, sb);
     }
   };
 
@@ -374,65 +357,83 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
 
-  // fragments of two chunks (by chunk parity) and decoded operands of two k-steps
+  // fragments of two chunks (by chunk order) and decoded operands of two k-steps
+  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
+  const int wfrag = wave_n * FN * 2048;
+  const int xfrag = wave_m * FM * 2048;
+  const int wsw = (BM + wave_n * WTN + r32) * 16 + 2 * h;
+  const int xsw = (wave_m * WTM + r32) * 16 + 2 * h;
   u32x4 wraw[2][FN], xraw[2][FM];
   uint32_t wsr[2][FN], xsr[2][FM];
   half2_t wsc[FN], xsc[FM];
   half8_t wf[2][FN], xf[2][FM];
-  auto read_chunk = [&](int par, int buf, int kc) {
+  auto read_chunk = [&](int par, int buf, int c, int sb, int sub) {
+    const int fr = fr0 ^ (32 * c);
+    const uint8_t* wb = &sm.w[buf][wfrag + fr];
+    const uint8_t* xb = &sm.x[buf][xfrag + fr];
+    const uint8_t* scb = &sm.sc[sb][sub * 8 + c * 4];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[par][i] = *(const u32x4*)&sm.w[buf][kc][((wave_n * FN + i) * 64 + lane) * 16];
-      wsr[par][i] = *(const uint16_t*)((const uint8_t*)&sm.ws[buf][kc][wave_n * WTN + i * 32 + r32] + 2 * h);
+      wraw[par][i] = *(const u32x4*)(wb + i * 2048);
+      wsr[par][i] = *(const uint16_t*)(scb + wsw + i * 512);
     }
 #pragma unroll
     for (int g = 0; g < FM; ++g) {
-      xraw[par][g] = *(const u32x4*)&sm.x[buf][kc][((wave_m * FM + g) * 64 + lane) * 16];
-      xsr[par][g] = *(const uint16_t*)((const uint8_t*)&sm.xs[buf][kc][wave_m * WTM + g * 32 + r32] + 2 * h);
+      xraw[par][g] = *(const u32x4*)(xb + g * 2048);
+      xsr[par][g] = *(const uint16_t*)(scb + xsw + g * 512);
     }
   };
   auto decode_step = [&](int par, int j, half8_t* wo, half8_t* xo) {
     if (j == 0) {
 #pragma unroll
-      for (int i = 0; i < FN; ++i) wsc[i] = scales_to_f16<kHw>(wsr[par][i]);
+      for (int i = 0; i < FN; ++i) wsc[i] = scales_to_f16<true>(wsr[par][i]);
 #pragma unroll
-      for (int g = 0; g < FM; ++g) xsc[g] = scales_to_f16<kHw>(xsr[par][g]);
+      for (int g = 0; g < FM; ++g) xsc[g] = scales_to_f16<true>(xsr[par][g]);
     }
 #pragma unroll
-    for (int i = 0; i < FN; ++i) wo[i] = decode8<kHw>(wraw[par][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
+    for (int i = 0; i < FN; ++i) wo[i] = decode8<true>(wraw[par][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
 #pragma unroll
-    for (int g = 0; g < FM; ++g) xo[g] = decode8<kHw>(xraw[par][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
+    for (int g = 0; g < FM; ++g) xo[g] = decode8<true>(xraw[par][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
   };
 
-  // prologue: stages 0 and 1 into buffers 0 and 1
+  // prologue: scales of pairs 0 and 1, codes of stages 0, 1 and 2
+  issue_scale(0, 0, 0);
+  issue_scale(0, 1, 0);
+  issue_scale(npair > 1 ? 1 : 0, 0, 1);
+  issue_scale(npair > 1 ? 1 : 0, 1, 1);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, 0, 0);
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, 0, 0, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) issue(j, nk > 1 ? 1 : 0, 1);
-  wait_dma();
-  __syncthreads();
-  read_chunk(0, 0, 0);
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  read_chunk(0, 0, 0, 0, 0);
   decode_step(0, 0, wf[0], xf[0]);
 
   constexpr int kMfmaPerStep = FN * FM;
   constexpr int kReadsPerChunk = 2 * (FN + FM);
-  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
   int buf = 0;
-  for (int64_t t = 0; t < nk; ++t) {
-    const int nbuf = buf == 2 ? 0 : buf + 1;     // stage t + 1
-    const int lbuf = nbuf == 2 ? 0 : nbuf + 1;   // stage t + 2
-    const int64_t lstage = t + 2 < nk ? t + 2 : nk - 1;
+  for (int t = 0; t < nk; ++t) {
+    const int nbuf = (buf + 1) & 3;  // stage t + 1 (complete since the end of stage t - 1)
+    const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
+    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
+    const int pair = t >> 1;
+    const int sb = pair % 3, sbn = ((t + 1) >> 1) % 3;
+    const int spair = pair + 2 < npair ? pair + 2 : npair - 1;
+    const int sbl = (pair + 2) % 3;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;
       const int chunk = st >> 2, j = st & 3;
 #pragma unroll
       for (int l = 0; l < kLoadsPerStep; ++l)
-        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf);
+        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf, t, spair, sbl);
       const bool reads = j == 0;
-      if (reads) {  // next chunk: the rest of this stage, then the first chunk of the next
-        if (chunk + 1 < KC) read_chunk((chunk + 1) & 1, buf, chunk + 1);
-        else read_chunk(0, nbuf, 0);
+      if (reads) {  // next chunk: the second of this stage, then the first of the next
+        if (chunk == 0) read_chunk(1, buf, 1, sb, t & 1);
+        else read_chunk(0, nbuf, 0, sbn, (t + 1) & 1);
       }
       // decode of the next k-step (the first k-step of the next stage after the last)
       if (st + 1 < kSteps) decode_step((st + 1) >> 2 & 1, (st + 1) & 3, wf[cur ^ 1], xf[cur ^ 1]);
@@ -446,21 +447,23 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_dma_kernel(GemmProblem p) {
       for (int q = 0; q < kMfmaPerStep; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         if (reads && q < kReadsPerChunk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        if (q < kLoadsPerStep) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
+        if (q < kLoadsPerStep && st * kLoadsPerStep + q < kLoadsPerWave)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
         __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_dma();
-    __syncthreads();
+    wait_vmcnt<kLoadsPerWave>();
+    __builtin_amdgcn_s_barrier();
     buf = nbuf;
   }
 
-  // every load has landed and every wave is past its last LDS read (the loop ends with
-  // a full wait and a barrier), so the stage buffers can stage the stores
+  // drain the last (unused) loads before the stage buffers stage the stores
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
-  store_tile_lds<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
-                         (uint16_t*)&sm.x[0][0][0] + wave * 32 * kStoreRowPad(FN));
+  store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN, lane,
+                         (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- fit-tile path: 288 x 192 tiles ------------------------------------------------------
@@ -895,8 +898,7 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool fast) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (fast)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, KC, WM, WN, true>), dim3((unsigned)tiles),
-                       dim3(64 * WM * WN), 0, stream, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, WM, WN, true, false>), dim3((unsigned)tiles),
                        dim3(64 * WM * WN), 0, stream, p);
@@ -975,10 +977,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   constexpr int FBM = kFitBM, FBN = kFitBN;
   GemmPlan plan{};
   cus = cus > 0 ? cus : 256;
-  const bool fast = aligned && (K % (64 * KC) == 0);
-  // 32-bit buffer offsets (with one tile of rows past the end) for the fit and split-K kernels
+  // 32-bit buffer offsets (with one tile of rows past the end) for the 256x256, fit and
+  // split-K kernels
   const bool fits32 = (M + FBM) * (K / 2) < ((int64_t)1 << 31) &&
                       (N + FBN) * (K / 2) < ((int64_t)1 << 31);
+  const bool fits32_256 = (M + BM) * (K / 2) < ((int64_t)1 << 31) &&
+                          (N + BN) * (K / 2) < ((int64_t)1 << 31);
+  const bool fast = aligned && (K % (64 * KC) == 0) && fits32_256;
   const int64_t nk = K / 128;
   // tiled kernels: one tile per compute unit at a time, plus epilogue and prologue
   const int64_t t256 = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
