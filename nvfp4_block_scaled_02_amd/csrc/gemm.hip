@@ -14,13 +14,17 @@
 // bits), so f16 (2.5 PFLOP/s dense) is the fastest exact MFMA type.
 //
 // Structure:
-//  * Packed 4-bit tiles and scale bytes stream from HBM into LDS (double-buffered);
-//    decode happens in registers right before the MFMA, so LDS holds 4-bit data and its
-//    traffic stays 4x below an f16-staged design.
-//  * LDS layout of a packed tile: for every 32-row group and 64-element K chunk, 64
-//    slots of 16 bytes in MFMA lane order (slot h*32 + r holds row r, bytes
-//    [16h, 16h+16) of the chunk). A wave reads its operand fragment with one 16-byte
-//    LDS load per lane at address lane*16: no bank conflicts.
+//  * Packed 4-bit tiles and scale bytes stream from HBM into LDS (four stage buffers in
+//    the direct-to-LDS kernels, two in the register-staged one); decode happens in
+//    registers right before the MFMA, so LDS holds 4-bit data and its traffic stays 4x
+//    below an f16-staged design.
+//  * LDS layout of a packed tile: a lane reads its operand fragment for a 64-element
+//    chunk (row r, bytes [16h, 16h+16) of the chunk) with one 16-byte LDS load, free of
+//    bank conflicts. The direct-to-LDS kernels (256 x 256 and 288 x 192 tiles) keep each
+//    row's 64 bytes of a stage together in 1 KiB pieces of 16 rows with the 16-byte
+//    chunks swizzled (chunk_swz), because their loads read whole 64-byte row segments;
+//    the register-staged kernel stores 64 slots of 16 bytes per 32-row group and chunk
+//    in MFMA lane order.
 //  * K mapping: lane half h of a fragment feeds the MFMA's K slots [8h, 8h+8) with
 //    elements 32h + 8j .. 32h + 8j + 7 of the chunk on k-step j (j = 0..3). Both
 //    operands use the same mapping, so each product pairs equal k; each lane's 8

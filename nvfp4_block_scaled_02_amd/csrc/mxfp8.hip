@@ -12,6 +12,9 @@
 // Unlike NVFP4's E4M3-per-16 scales, these power-of-two per-32 scales are exactly what
 // v_mfma_scale_f32_32x32x64_f8f6f4 applies, so the GEMM needs no decode: the fp8 codes go
 // from HBM through LDS straight into the matrix core (fp8 rate, 2x the f16 rate).
+//
+// The same GEMM kernels, with unit block scales and a per-row x per-column scale
+// epilogue, run the rowwise FP8 ("fp8r") product; its quantizer is in fp8r.hip.
 #include "gemm_common.hpp"
 
 namespace nvfp4 {
