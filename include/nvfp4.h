@@ -111,7 +111,9 @@ typedef enum {
   NVFP4_GEMM_FIT = 1,     /* 288 x 192 output tiles (K % 128 == 0): 4608-row activations
                              and FLUX widths split into whole multiples of 256 tiles */
   NVFP4_GEMM_SPLITK = 2,  /* K split over a workgroup's waves: short activations */
-  NVFP4_GEMM_GENERIC = 3  /* 256 x 256 tiles, register-staged loads: any K % 16 == 0 */
+  NVFP4_GEMM_GENERIC = 3, /* 256 x 256 tiles, register-staged loads: any K % 16 == 0 */
+  NVFP4_GEMM_TILE128 = 4  /* 128 x 192 output tiles (K % 128 == 0): activations of a few
+                             hundred to a few thousand rows */
 } nvfp4_gemm_kernel;
 
 /*

@@ -274,14 +274,18 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
   store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
-// ---- 256 x 256 tiles: direct-to-LDS loads, four code stages, one pipeline across stages ----
+// ---- 256 x 256 and 128 x 192 tiles: direct-to-LDS loads, four code stages, one pipeline
+// across stages ----
 //
-// 2 x 2 waves of 128 x 128 (4 x 4 blocks of 32 x 32). Loads, LDS image and stage pipeline
+// 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
+// 2 x 3 for 128 x 192 (medium M: four times the tiles, so a few thousand rows still fill
+// the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
 // are the fit kernel's (below): code loads of 16 rows x the stage's 64 bytes (4 lanes per
 // row) into 1 KiB pieces whose 16-byte chunks are swizzled by chunk_swz, scale loads of
 // 64 rows x 16 bytes (a pair of stages) into three pair buffers, four code buffers filled
 // three stages ahead, one wait and barrier per stage; range-checked buffer loads, so a
-// ragged tile needs no clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS.
+// ragged tile needs no clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS at 256 x 256,
+// 4 x 20 KiB + 3 x 5 KiB = 95 KiB at 128 x 192.
 template <int BM, int BN>
 struct alignas(16) GemmSmem256 {
   uint8_t x[4][BM * 64];
@@ -302,7 +306,8 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   static_assert(kPa % NW == 0 && kPw % NW == 0, "code pieces divide among waves");
   constexpr int kPaW = kPa / NW, kPwW = kPw / NW;
   constexpr int kSx = BM / 64;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && kSx + BN / 64 == 2 * NW, "one scale load per wave and stage");
+  constexpr int kSp = kSx + BN / 64;  // scale pieces per pair of stages
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && kSp <= 2 * NW, "one scale load per wave and stage");
   constexpr int kLoadsPerWave = kPaW + kPwW + 1;
   static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
   constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
@@ -333,8 +338,10 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   const uint32_t voff_p = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
   const uint32_t voff_s = lane * spitch;
 
+  // scale piece half * NW + wave of a pair (slots past the last piece repeat it, writing
+  // the same bytes to the same place)
   auto issue_scale = [&](int pair, int half, int sb) {
-    const int i = half * NW + wave;
+    const int i = min(half * NW + wave, kSp - 1);
     const bool isx = i < kSx;
     const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
     buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024], voff_s, row * spitch + (uint32_t)pair * 16);
@@ -995,8 +1002,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   const double c256 = fast ? (double)passes(t256, cus) * (nk * 128 * mfma_cycles(0.5) + 20000.0) : 1e300;
   const bool fit_ok = aligned && K % 128 == 0 && fits32;
   const double cfit = fit_ok ? (double)passes(tfit, cus) * (nk * 108 * mfma_cycles(7.5 / 13.5) + 20000.0) : 1e300;
-  // Few tiles (short activations): the tiled kernels would leave most compute units
-  // idle for a whole K loop; split K inside the workgroup instead.
+  // 128 x 192 tiles (2 x 3 blocks per wave: more decode per MFMA, but 4x the tiles of
+  // 256 x 256) for activations too short to fill the chip with the larger tiles
+  const int64_t t128 = ((M + 127) / 128) * ((N + 191) / 192);
+  const double c128 = fast ? (double)passes(t128, cus) * (nk * 48 * mfma_cycles(5.0 / 6.0) + 20000.0) : 1e300;
+  // Few tiles and at most 512 rows (short activations): the tiled kernels would leave
+  // most compute units idle for a whole K loop; split K inside the workgroup instead
+  // (it reads the activations once per 32 weight rows, which stops paying beyond about
+  // 512 rows).
   const bool split_ok = aligned && K % 32 == 0 && fits32;
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
@@ -1006,8 +1019,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   else if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) plan.kernel = NVFP4_GEMM_FIT;
   return plan;
 #endif
-  if (split_ok && tfit * 4 <= cus) plan.kernel = NVFP4_GEMM_SPLITK;
-  else if (fit_ok && cfit <= c256) plan.kernel = NVFP4_GEMM_FIT;
+  if (split_ok && tfit * 4 <= cus && M <= 512) {
+    plan.kernel = NVFP4_GEMM_SPLITK;
+  } else if (fast || fit_ok) {
+    double best = c256;
+    if (fit_ok && cfit <= best) { plan.kernel = NVFP4_GEMM_FIT; best = cfit; }
+    if (fast && c128 < best) plan.kernel = NVFP4_GEMM_TILE128;
+  }
   return plan;
 }
 
@@ -1022,6 +1040,12 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
       const int64_t tfit = ((p.M + kFitBM - 1) / kFitBM) * ((p.N + kFitBN - 1) / kFitBN);
       if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
       hipLaunchKernelGGL((gemm_fit_kernel<kFitBM, kFitBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case NVFP4_GEMM_TILE128: {
+      const int64_t t = ((p.M + 127) / 128) * ((p.N + 191) / 192);
+      if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_dma_kernel<128, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
       return hipGetLastError();
     }
     default:

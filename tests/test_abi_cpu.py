@@ -109,16 +109,20 @@ def test_gemm_plan_routes_shapes(lib):
         st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    FIT, TILE, SPLIT, GEN = 1, 0, 2, 3
+    FIT, TILE, SPLIT, GEN, T128 = 1, 0, 2, 3, 4
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
-                    (4608, 9216, 3072), (2600, 1650, 128)]:
+                    (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
-    for M in (1, 17, 256, 1000):
+    for M in (1, 17, 256, 512):
         assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    for M in (600, 1000, 2000):   # a few hundred to a few thousand rows: 128 x 192 tiles
+        assert plan(M, 3072, 3072) == (L.SUCCESS, T128), M
+    assert plan(2600, 1650, 128) == (L.SUCCESS, T128)
     assert plan(4096, 4096, 128) == (L.SUCCESS, TILE)
+    assert plan(18432, 12288, 3072) == (L.SUCCESS, TILE)
     assert plan(600, 700, 208) == (L.SUCCESS, GEN)   # K % 32 == 16: no split-K either
     assert plan(4608, 3072, 3008) == (L.SUCCESS, GEN)
-    # fewer compute units: the same M = 1000 product is worth tiling
+    # fewer compute units: the same M = 1000 product is worth the larger tiles
     assert plan(1000, 3072, 3072, 32) == (L.SUCCESS, FIT)
     assert plan(8, 8, 40)[0] == L.INVALID_SHAPE
     assert plan(-1, 8, 64)[0] == L.INVALID_SHAPE

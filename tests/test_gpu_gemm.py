@@ -68,8 +68,11 @@ def test_gemm_small_shapes_in_full(M, N, K):
 @pytest.mark.parametrize("M,N,K,kernel", [
     # 288 x 192 tiles: one stage (K = 128), an odd number of stages, ragged by one row
     # and column, and several scale pairs with an odd count
-    (2600, 1650, 128, "fit"), (2900, 1500, 384, "fit"), (2305, 1537, 256, "fit"),
-    (2000, 2000, 1152, "fit"),
+    (2600, 3000, 128, "fit"), (2900, 3100, 384, "fit"), (2305, 3073, 256, "fit"),
+    (2000, 4000, 1152, "fit"),
+    # 128 x 192 tiles: the same cases at medium M
+    (1500, 2500, 128, "tile128"), (513, 1000, 640, "tile128"), (777, 385, 1152, "tile128"),
+    (600, 700, 256, "tile128"),
     (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])
