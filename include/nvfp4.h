@@ -210,6 +210,17 @@ int nvfp4_fp8r_gemm(const void* a_codes, const void* a_scales, const void* w_cod
                     const void* w_scales, int64_t M, int64_t N, int64_t K, void* out_bf16,
                     void* stream);
 
+/*
+ * Whether nvfp4_linear (and nvfp4_linear_devgs) run an M x N x K product as one kernel:
+ * the short-activation split-K GEMM first quantizing the bf16 activations into its LDS
+ * (for at most 32 rows and 16384 elements, where repeating that quantization in every
+ * workgroup along N costs less than a second launch), instead of the quantize kernel
+ * followed by nvfp4_gemm. num_cus as in nvfp4_gemm_plan. Host only.
+ * Writes 1 (one kernel) or 0 (two) to *fused; NVFP4_ERROR_INVALID_VALUE for a null
+ * pointer, NVFP4_ERROR_INVALID_SHAPE for shapes the linear rejects.
+ */
+int nvfp4_linear_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* fused);
+
 /* Workspace bytes nvfp4_linear needs for an [M, K] activation (packed + scales, each
  * rounded up to 256 bytes). Returns 0 for invalid shapes. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
@@ -223,7 +234,9 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
  *              best (16 required); it holds the quantized activations on return:
  *              packed [M, K/2] at offset 0, scales [M, K/16] at offset
  *              round_up(M*K/2, 256).
- * Other arguments as in nvfp4_quantize / nvfp4_gemm.
+ * Other arguments as in nvfp4_quantize / nvfp4_gemm. Short activations (where
+ * nvfp4_linear_plan reports 1) run as one kernel that quantizes inside the GEMM; the
+ * workspace and the output are bit-identical to the two-kernel form either way.
  */
 int nvfp4_linear(const void* x_bf16, float a_global_scale, const void* w_packed,
                  const void* w_scales, float w_global_scale, int64_t M, int64_t N, int64_t K,

@@ -37,6 +37,7 @@ SIGNATURES = {
     "nvfp4_quantize": (_int, [_vp, _i64, _i64, _f32, _vp, _vp, _vp]),
     "nvfp4_gemm": (_int, [_vp, _vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int)]),
+    "nvfp4_linear_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int)]),
     "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_mxfp8_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_mxfp8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),

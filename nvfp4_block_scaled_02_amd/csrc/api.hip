@@ -281,13 +281,31 @@ int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float
   nvfp4::LaunchInfo info;
   s = current_device(&info);
   if (s) return s;
-  hipError_t e = nvfp4::launch_quantize(x, M, K, ags, ap, as, (hipStream_t)stream, info);
-  if (e != hipSuccess) return hip_fail(e);
-  if (N == 0) return NVFP4_SUCCESS;
   nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
                        M, N, K, ags * wgs};
+  hipError_t e;
+  if (N > 0 && nvfp4::linear_fused(M, N, K, true, info.num_cus)) {
+    const float den = 6.0f * ags;
+    const nvfp4::FusedQuant fq{x, ags, den, 1.0f / den, nullptr, ap, as};
+    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream);
+    return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+  }
+  e = nvfp4::launch_quantize(x, M, K, ags, ap, as, (hipStream_t)stream, info);
+  if (e != hipSuccess) return hip_fail(e);
+  if (N == 0) return NVFP4_SUCCESS;
   e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_linear_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* fused) {
+  if (!fused) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  *fused = (M > 0 && N > 0 && nvfp4::linear_fused(M, N, K, true, num_cus)) ? 1 : 0;
+  return NVFP4_SUCCESS;
 }
 
 int nvfp4_amax(const void* x, int64_t n, float* amax_out, void* stream) {
@@ -365,11 +383,17 @@ int nvfp4_linear_devgs(const void* x, const float* ags_device, const void* wp, c
   nvfp4::LaunchInfo info;
   s = current_device(&info);
   if (s) return s;
-  hipError_t e = nvfp4::launch_quantize(x, M, K, 1.0f, ap, as, (hipStream_t)stream, info, ags_device);
-  if (e != hipSuccess) return hip_fail(e);
-  if (N == 0) return NVFP4_SUCCESS;
   nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
                        M, N, K, 1.0f, ags_device, wgs_device};
+  hipError_t e;
+  if (N > 0 && nvfp4::linear_fused(M, N, K, true, info.num_cus)) {
+    const nvfp4::FusedQuant fq{x, 1.0f, 6.0f, 1.0f / 6.0f, ags_device, ap, as};
+    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream);
+    return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+  }
+  e = nvfp4::launch_quantize(x, M, K, 1.0f, ap, as, (hipStream_t)stream, info, ags_device);
+  if (e != hipSuccess) return hip_fail(e);
+  if (N == 0) return NVFP4_SUCCESS;
   e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }

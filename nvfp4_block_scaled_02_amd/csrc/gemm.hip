@@ -37,6 +37,7 @@
 //    lane ends up holding 4 consecutive output columns of one row: 8-byte bf16 stores.
 //  * Epilogue: fp32 accumulator * alpha (fp32), round to nearest even bf16.
 #include "gemm_common.hpp"
+#include "quant_common.hpp"
 
 // VALU instructions the scheduler is asked to place after each MFMA of a k-step.
 #ifndef NVFP4_GEMM_VALU_PER_MFMA
@@ -768,10 +769,21 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // both operands below 2^31 bytes (32-bit buffer offsets). In a last chunk that holds only
 // 32 elements, the upper lane half reads past its row; its scale is forced to zero, so
 // those products vanish (E2M1 codes are always finite).
-template <int A, int B, int D>
-__global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
-  constexpr int NW = 4;
+//
+// kFuse: the fused linear for the shortest activations (M * K <= kFuseElems). The
+// workgroup first quantizes the M real activation rows together, two lanes per
+// 16-element block exactly as the quantize kernel does (same functions, so the codes and
+// scales are bit-identical to nvfp4_quantize's), into LDS in the NVFP4 layout; the
+// workgroups of the first weight-row tile also store them to the caller's workspace.
+// The K loop then reads the activation fragments from LDS (zeros for rows past M).
+// Every workgroup along N repeats the quantization, which is why it is limited to a few
+// thousand elements per thread block.
+constexpr int kFuseElems = 16384;
+template <int A, int B, int D, int NW, bool kFuse>
+__global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, FusedQuant fq) {
   __shared__ float red[2][NW][16 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElems / 2 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xqs[kFuse ? kFuseElems / 16 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -805,6 +817,32 @@ __global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
 
   u32x4 wraw[D][A], xraw[D][B];
   uint32_t wsr[D][A], xsr[D][B];
+  if constexpr (kFuse) {
+    // Quantize the M x K activations into LDS: half block hb (8 elements) per lane, the
+    // pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one wave.
+    const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
+    const int nhalves = (int)(p.M * p.K / 8);
+    const u32x4* xv = (const u32x4*)fq.x;
+    for (int hb = threadIdx.x; hb < nhalves; hb += 64 * NW) {
+      float f[8];
+      unpack_bf16x8(xv[hb], f);
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
+      const float o = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
+      const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
+                                                           : encode_half<false>(f, bs);
+      *(uint32_t*)&xq[4 * hb] = word;
+      if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
+      if (tn == 0 && fq.ws_packed != nullptr) {
+        *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
+        if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
+      }
+    }
+    __syncthreads();
+  }
   // chunk number q of this wave (chunk index wave + 4q) into ring slot d
   auto load = [&](int d, int q) {
     const int c = wave + NW * q;
@@ -817,15 +855,26 @@ __global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
     }
 #pragma unroll
     for (int g = 0; g < B; ++g) {
-      xraw[d][g] = __builtin_amdgcn_raw_buffer_load_b128(
-          rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
-      xsr[d][g] = __builtin_amdgcn_raw_buffer_load_b16(
-          rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+      if constexpr (!kFuse) {
+        xraw[d][g] = __builtin_amdgcn_raw_buffer_load_b128(
+            rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
+        xsr[d][g] = __builtin_amdgcn_raw_buffer_load_b16(
+            rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+      }
     }
   };
   auto compute = [&](int d, int q) {
     // upper lane half of a 32-element last chunk: no elements, zero scale
     const bool dead = h == 1 && (int64_t)(wave + NW * q) * 64 + 32 >= p.K;
+    if constexpr (kFuse) {
+      // activation fragment from LDS (rows past M and the dead upper half read as zero)
+      const int c = wave + NW * q;
+      const bool live = r32 < p.M && !dead;
+      xraw[d][0] = live ? *(const u32x4*)&xq[r32 * pitch + (uint32_t)c * 32 + h * 16]
+                        : u32x4{0u, 0u, 0u, 0u};
+      xsr[d][0] = live ? (uint32_t)*(const uint16_t*)&xqs[r32 * spitch + (uint32_t)c * 4 + h * 2]
+                       : 0u;
+    }
     half2_t wsc[A], xsc[B];
 #pragma unroll
     for (int i = 0; i < A; ++i) wsc[i] = scales_to_f16<true>(dead ? 0u : wsr[d][i]);
@@ -885,10 +934,9 @@ __global__ void __launch_bounds__(256) gemm_splitk_kernel(GemmProblem p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int v = 4 * q + e;
-              float s = rb[(0 * 16 + v) * 64 + lane];
-              s += rb[(1 * 16 + v) * 64 + lane];
-              s += rb[(2 * 16 + v) * 64 + lane];
-              s += rb[(3 * 16 + v) * 64 + lane];
+              float s = rb[v * 64 + lane];
+#pragma unroll
+              for (int w = 1; w < NW; ++w) s += rb[(w * 16 + v) * 64 + lane];
               b[e] = bf16_rne(s * alpha);
             }
             if (n_vec && n + 3 < p.N) {
@@ -974,10 +1022,12 @@ SplitShape splitk_shape(int64_t M) {
 hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s) {
   const int64_t wgs = ((p.N + 32 * s.a - 1) / (32 * s.a)) * ((p.M + 32 * s.b - 1) / (32 * s.b));
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)wgs), block(256);
-  if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8>), grid, block, 0, stream, p);
-  else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 6>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 4>), grid, block, 0, stream, p);
+  constexpr int NW = 4;  // 8 or 16 waves per workgroup measured no faster
+  const dim3 grid((unsigned)wgs), block(64 * NW);
+  const FusedQuant none{};
+  if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8, NW, false>), grid, block, 0, stream, p, none);
+  else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 6, NW, false>), grid, block, 0, stream, p, none);
+  else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 4, NW, false>), grid, block, 0, stream, p, none);
   return hipGetLastError();
 }
 
@@ -1006,11 +1056,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   // 256 x 256) for activations too short to fill the chip with the larger tiles
   const int64_t t128 = ((M + 127) / 128) * ((N + 191) / 192);
   const double c128 = fast ? (double)passes(t128, cus) * (nk * 48 * mfma_cycles(5.0 / 6.0) + 20000.0) : 1e300;
-  // Few tiles and at most 512 rows (short activations): the tiled kernels would leave
-  // most compute units idle for a whole K loop; split K inside the workgroup instead
-  // (it reads the activations once per 32 weight rows, which stops paying beyond about
-  // 512 rows).
+  // Split K inside the workgroup (short activations, at most 512 rows: it reads the
+  // activations once per 32 weight rows, which stops paying beyond that). Measured cost:
+  // ~6000 cycles of launch and reduction plus, per pass over the chip, 360 / 740 / 1330
+  // cycles per 128 elements of K for 32-row groups B = 1 / 2 / 4 per workgroup.
   const bool split_ok = aligned && K % 32 == 0 && fits32;
+  const SplitShape sh = splitk_shape(M);
+  const int64_t wsplit = ((N + 31) / 32) * ((M + 32 * sh.b - 1) / (32 * sh.b));
+  const double csplit = 6000.0 + (double)passes(wsplit, cus) * ((double)K / 128.0) *
+                                     (sh.b == 1 ? 360.0 : sh.b == 2 ? 740.0 : 1330.0);
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
 #ifdef NVFP4_GEMM_FORCE_TILE
@@ -1019,12 +1073,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   else if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) plan.kernel = NVFP4_GEMM_FIT;
   return plan;
 #endif
-  if (split_ok && tfit * 4 <= cus && M <= 512) {
-    plan.kernel = NVFP4_GEMM_SPLITK;
-  } else if (fast || fit_ok) {
+  if (fast || fit_ok) {
     double best = c256;
     if (fit_ok && cfit <= best) { plan.kernel = NVFP4_GEMM_FIT; best = cfit; }
-    if (fast && c128 < best) plan.kernel = NVFP4_GEMM_TILE128;
+    if (fast && c128 < best) { plan.kernel = NVFP4_GEMM_TILE128; best = c128; }
+    if (split_ok && M <= 512 && csplit < best) plan.kernel = NVFP4_GEMM_SPLITK;
+  } else if (split_ok && M <= 512 && tfit * 4 <= cus) {
+    // against the register-staged kernel (K % 128 != 0): few tiles only
+    plan.kernel = NVFP4_GEMM_SPLITK;
   }
   return plan;
 }
@@ -1052,6 +1108,21 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
       return launch_tile<kTileBM, kTileBN, kTileKC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(
           p, stream, plan.kernel == NVFP4_GEMM_TILE256);
   }
+}
+
+bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
+  const GemmPlan g = plan_gemm(M, N, K, aligned, cus);
+  // one 32-row activation group, and activations small enough to quantize in every
+  // workgroup (and to sit in its LDS)
+  return g.kernel == NVFP4_GEMM_SPLITK && M <= 32 && M * K <= kFuseElems;
+}
+
+hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream) {
+  const int64_t wgs = (p.N + 31) / 32;
+  if (p.M > 32 || p.M * p.K > kFuseElems || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8, 4, true>), dim3((unsigned)wgs), dim3(256), 0,
+                     stream, p, fq);
+  return hipGetLastError();
 }
 
 hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,

@@ -34,6 +34,20 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);
 
+// The fused linear for short activations: the split-K GEMM quantizes its own bf16
+// activations (bit-identical to launch_quantize) and, when ws_packed is set, the
+// workgroups of the first weight-row tile store the codes and scales there. The GEMM
+// problem's a_packed / a_scales are unused.
+struct FusedQuant {
+  const void* x;          // bf16 activations [M, K]
+  float gs, den, rden;    // host global scale, RN(6 gs), RN(1 / RN(6 gs))
+  const float* gs_dev;    // device-resident global scale instead (then gs/den/rden unused)
+  uint8_t* ws_packed;     // [M, K/2] codes out, or null
+  uint8_t* ws_scales;     // [M, K/16] scales out
+};
+bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus);
+hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream);
+
 // The kernel launch_gemm picks for a shape (values of nvfp4_gemm_kernel in nvfp4.h), and
 // the split-K workgroup shape (32a weight rows x 32b activation rows) when it splits.
 struct SplitShape { int a, b; };

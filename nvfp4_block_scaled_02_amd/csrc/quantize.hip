@@ -21,43 +21,11 @@
 //    IEEE quotient for every bf16 x (see codec.hpp); the E2M1 encode is the gfx950
 //    conversion instruction, whose rounding (to nearest even, saturating) is checked
 //    exhaustively against the software encoder by the self-test entry points.
-#include "codec.hpp"
-#include "kernels.hpp"
+#include "quant_common.hpp"
 
 namespace nvfp4 {
 
 namespace {
-
-__device__ __forceinline__ void unpack_bf16x8(const u32x4 v, float* f) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = u2f(w[i] << 16);
-    f[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
-  }
-}
-
-// Encode 8 values (in f) of one half block into 4 packed bytes (element 2j in the low
-// nibble of byte j), given the block's scale. kClamp selects the quotient form that
-// tolerates an overflowing |x| * r (only needed for blocks whose scale saturated).
-template <bool kClamp>
-__device__ __forceinline__ uint32_t encode_half(const float* f, const BlockScale& bs) {
-  uint32_t out = 0u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float y0 = kClamp ? div_by_scale(f[2 * j], bs.d, bs.r)
-                            : div_by_scale_unclamped(f[2 * j], bs.d, bs.r);
-    const float y1 = kClamp ? div_by_scale(f[2 * j + 1], bs.d, bs.r)
-                            : div_by_scale_unclamped(f[2 * j + 1], bs.d, bs.r);
-    switch (j) {
-      case 0: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 0); break;
-      case 1: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 1); break;
-      case 2: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 2); break;
-      default: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, y0, y1, 1.0f, 3); break;
-    }
-  }
-  return out;
-}
 
 // nhalves = 2 * (number of blocks); half index hi covers x[hi] (16 bytes) and packed
 // word hi. The pair (hi, hi ^ 1) is one block; since nhalves is even and workgroups are
@@ -68,10 +36,11 @@ __global__ void __launch_bounds__(256) quantize_kernel(const u32x4* __restrict__
                                                        uint8_t* __restrict__ scales,
                                                        int64_t nhalves, float gs, float den,
                                                        float rden, const float* gs_dev) {
-  if (gs_dev != nullptr) {  // device-resident global scale: same arithmetic as the host's
-    gs = clamp_global_scale(*gs_dev);
-    den = 6.0f * gs;
-    rden = 1.0f / den;
+  {
+    const QuantScale qs = quant_scale(gs, den, rden, gs_dev);
+    gs = qs.gs;
+    den = qs.den;
+    rden = qs.rden;
   }
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * UNROLL;
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x * UNROLL + threadIdx.x; base < nhalves;

@@ -226,6 +226,14 @@ def gemm_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
     return GEMM_KERNELS[kind.value]
 
 
+def linear_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
+    """"fused" when :func:`linear` runs the shape as one kernel (quantize inside the
+    short-activation GEMM), else "two_kernels". Host only."""
+    fused = ctypes.c_int(-1)
+    check(load_library().nvfp4_linear_plan(M, N, K, num_cus, ctypes.byref(fused)), "nvfp4_linear_plan")
+    return "fused" if fused.value == 1 else "two_kernels"
+
+
 def linear_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().nvfp4_linear_workspace_bytes(M, K))
 

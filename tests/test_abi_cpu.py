@@ -115,6 +115,11 @@ def test_gemm_plan_routes_shapes(lib):
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
     for M in (1, 17, 256, 512):
         assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    # wide weights with few rows: split-K's workgroups still fill the chip
+    for M, N in [(1, 18432), (17, 18432), (64, 18432), (128, 12288)]:
+        assert plan(M, N, 3072) == (L.SUCCESS, SPLIT), (M, N)
+    assert plan(256, 12288, 3072) == (L.SUCCESS, T128)
+    assert plan(512, 12288, 3072) == (L.SUCCESS, T128)
     for M in (600, 1000, 2000):   # a few hundred to a few thousand rows: 128 x 192 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128), M
     assert plan(2600, 1650, 128) == (L.SUCCESS, T128)
@@ -127,6 +132,31 @@ def test_gemm_plan_routes_shapes(lib):
     assert plan(8, 8, 40)[0] == L.INVALID_SHAPE
     assert plan(-1, 8, 64)[0] == L.INVALID_SHAPE
     assert lib.nvfp4_gemm_plan(8, 8, 64, 0, None) == L.INVALID_VALUE
+
+
+def test_linear_plan_fuses_short_activations(lib):
+    """nvfp4_linear runs the shortest activations (at most 32 rows, the split-K GEMM's
+    one-group shape, and at most 16384 elements, which every workgroup quantizes into its
+    LDS) as one kernel; everything else as quantize + GEMM."""
+    def plan(M, N, K, cus=0):
+        f = ctypes.c_int(-1)
+        st = lib.nvfp4_linear_plan(M, N, K, cus, ctypes.byref(f))
+        return st, f.value
+
+    for M in (1, 5):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, 1), M
+    assert plan(1, 64, 32) == (L.SUCCESS, 1)
+    assert plan(1, 3072, 12288) == (L.SUCCESS, 1)
+    assert plan(32, 3072, 512) == (L.SUCCESS, 1)
+    assert plan(32, 3072, 544) == (L.SUCCESS, 0)   # 17408 elements
+    assert plan(2, 96, 12288) == (L.SUCCESS, 0)
+    for M in (6, 17, 32, 33, 64, 256, 1000, 4608):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, 0), M
+    assert plan(8, 60, 208) == (L.SUCCESS, 0)     # K % 32 == 16: no split-K
+    assert plan(0, 3072, 3072) == (L.SUCCESS, 0)
+    assert plan(8, 0, 3072) == (L.SUCCESS, 0)
+    assert plan(8, 8, 40)[0] == L.INVALID_SHAPE
+    assert lib.nvfp4_linear_plan(8, 8, 64, 0, None) == L.INVALID_VALUE
 
 
 def test_gemm_w4a16_validation(lib):

@@ -52,6 +52,8 @@ def _assert_close(got_bits, ap, as_, ags, wp, ws, wgs, label):
     # three workgroup shapes the launcher picks: 32x32, 32x64 and 32x128 outputs
     (5, 200, 96), (100, 70, 224), (3, 5000, 1056), (33, 6144, 96), (256, 12288, 96),
     (640, 3072, 96),
+    # few rows, wide weights: split-K over 576 workgroups (more than one pass)
+    (1, 18432, 256), (17, 18432, 128),
 ])
 def test_gemm_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 131 + N * 7 + K)
