@@ -231,10 +231,17 @@ def context_legs(nv, lib, stream, n):
         y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)
         ms16 = time_launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, stream)
+        # the whole linear (quantize + GEMM, one fused kernel where the plan says so)
+        nb = nv.linear_workspace_bytes(M, K)
+        work = torch.empty(nb, dtype=torch.uint8, device=dev)
+        al = (P(x), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16),
+              P(work), ctypes.c_size_t(nb), sp)
+        msl = time_launches(lambda: lib.nvfp4_linear(*al), n, stream)
         wbytes = N * (K // 2 + K // 16)
         out["short_activations"][f"M={M}"] = {
             "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K), "w4a4_avg_ms": round(ms, 5),
             "w4a4_weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "linear": nv.linear_plan(M, N, K), "linear_avg_ms": round(msl, 5),
             "w4a16_avg_ms": round(ms16, 5),
             "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
     return out
