@@ -770,9 +770,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // 32 elements, the upper lane half reads past its row; its scale is forced to zero, so
 // those products vanish (E2M1 codes are always finite).
 //
-// kFuse: the fused linear for the shortest activations (M * K <= kFuseElems). The
-// workgroup first quantizes the M real activation rows together, two lanes per
-// 16-element block exactly as the quantize kernel does (same functions, so the codes and
+// kFuse: the fused linear for the shortest activations (M * K <= kFuseElems). Once its
+// first weight loads are in flight, the workgroup quantizes the M real activation rows
+// together, two lanes per 16-element block exactly as the quantize kernel does (same functions, so the codes and
 // scales are bit-identical to nvfp4_quantize's), into LDS in the NVFP4 layout; the
 // workgroups of the first weight-row tile also store them to the caller's workspace.
 // The K loop then reads the activation fragments from LDS (zeros for rows past M).
@@ -817,32 +817,6 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
 
   u32x4 wraw[D][A], xraw[D][B];
   uint32_t wsr[D][A], xsr[D][B];
-  if constexpr (kFuse) {
-    // Quantize the M x K activations into LDS: half block hb (8 elements) per lane, the
-    // pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one wave.
-    const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
-    const int nhalves = (int)(p.M * p.K / 8);
-    const u32x4* xv = (const u32x4*)fq.x;
-    for (int hb = threadIdx.x; hb < nhalves; hb += 64 * NW) {
-      float f[8];
-      unpack_bf16x8(xv[hb], f);
-      float a = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
-      const float o = __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
-      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
-      const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
-                                                           : encode_half<false>(f, bs);
-      *(uint32_t*)&xq[4 * hb] = word;
-      if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
-      if (tn == 0 && fq.ws_packed != nullptr) {
-        *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
-        if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
-      }
-    }
-    __syncthreads();
-  }
   // chunk number q of this wave (chunk index wave + 4q) into ring slot d
   auto load = [&](int d, int q) {
     const int c = wave + NW * q;
@@ -897,9 +871,38 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
     }
   };
 
+  // kFuse: quantize the M x K activations into LDS: half block hb (8 elements) per lane,
+  // the pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one wave.
+  auto quantize_to_lds = [&]() {
+    const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
+    const int nhalves = (int)(p.M * p.K / 8);
+    const u32x4* xv = (const u32x4*)fq.x;
+    for (int hb = threadIdx.x; hb < nhalves; hb += 64 * NW) {
+      float f[8];
+      unpack_bf16x8(xv[hb], f);
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
+      const float o = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
+      const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
+                                                           : encode_half<false>(f, bs);
+      *(uint32_t*)&xq[4 * hb] = word;
+      if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
+      if (tn == 0 && fq.ws_packed != nullptr) {
+        *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
+        if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
+      }
+    }
+    __syncthreads();
+  };
+
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < nq) load(d, d);
+  // (after the first weight loads, so their latency overlaps the quantization)
+  if constexpr (kFuse) quantize_to_lds();
   for (int q = 0; q < nq; q += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
