@@ -322,19 +322,200 @@ __global__ void __launch_bounds__(256) gemm_w4a16_tile_kernel(W4A16Problem p) {
                          (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
+
+// ---- 288 x 192 tiles: every FLUX product in whole multiples of 256 tiles -------------
+//
+// The W4A4 fit tile's shape (4608 = 16 x 288; 3072, 9216, 12288 are multiples of 192)
+// on the tiled form's loads and stage pipeline. 2 x 2 waves: wave (m, n) owns weight
+// groups 3n .. 3n+2 and activation groups 0-3 (m = 0) or 5-8 (m = 1); the middle group 4
+// is split by weight group, wave (0, n) taking groups 3n and 3n+1, wave (1, n) group
+// 3n+2. Both read the middle activation fragment straight from LDS (activations need no
+// decode here), and wave (1, n) also issues a second middle MFMA whose result it drops,
+// so every wave issues 14 MFMAs per k-step with no branch in the loop. Loads per stage:
+// 36 activation pieces (8 rows x 128 bytes), 6 weight pieces, 3 scale pieces, spread
+// over the waves (slots past the last piece repeat it: identical data to the same LDS
+// bytes). Three stage buffers (3 x 42.75 KiB).
+template <int BM, int BN>
+struct alignas(16) W4A16FitSmem {
+  uint8_t x[3][BM * 128];
+  uint8_t w[3][BN * 32];
+  uint8_t ws[3][BN * 4];
+};
+
+// Requires K % 64 == 0, 16-byte aligned x, codes and out, 4-byte aligned scales, and
+// (M + BM) * K * 2 and (N + BN) * K / 2 below 2^31 (32-bit buffer offsets).
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
+  constexpr int NW = 4, WN = 2;
+  __shared__ W4A16FitSmem<BM, BN> sm;
+  constexpr int GX = BM / 32, GW = BN / 32;
+  static_assert(GX * 32 == BM && GW * 32 == BN && GX % 2 == 1 && GW % WN == 0, "tile shape");
+  constexpr int GS = GX / 2;      // the middle activation group
+  constexpr int FM = GX / 2;      // own activation groups per wave
+  constexpr int FN = GW / WN;     // weight groups per wave
+  static_assert(FN == 3, "middle split: two weight groups for wave row 0, one for row 1");
+  constexpr int kPx = BM / 8, kPw = GW, kPs = (BN + 63) / 64;  // pieces per stage
+  constexpr int kPxW = (kPx + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW, kPsW = (kPs + NW - 1) / NW;
+  constexpr int kLoads = kPxW + kPwW + kPsW;
+  static_assert(kLoads < 16, "one stage of loads fits the vmcnt immediate");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_n = wave % WN;
+  const int wave_m = wave / WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  int tile_m, tile_n;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int nk = (int)(p.K / 64);
+  const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * xpitch);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
+  const int xr = lane >> 3;  // row (within 8) of an activation load
+  const uint32_t voff_w = r32 * pitch + h * 16;
+  const uint32_t voff_s = lane * spitch;
+
+  // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
+  auto issue = [&](int j, int stage, int buf) {
+    if (j < kPxW) {
+      const int i = min(j * NW + wave, kPx - 1);  // rows 8i .. 8i+7 of the tile
+      const int row = 8 * i + xr;
+      const uint32_t voff = xr * xpitch + 16 * ((lane & 7) ^ x_swz(row & 31));
+      buffer_load_lds16(rx, &sm.x[buf][i * 1024], voff, (uint32_t)(m0 + 8 * i) * xpitch + (uint32_t)stage * 128);
+    } else if (j < kPxW + kPwW) {
+      const int i = min((j - kPxW) * NW + wave, kPw - 1);  // weight group i
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], voff_w, (uint32_t)(n0 + 32 * i) * pitch + (uint32_t)stage * 32);
+    } else {
+      const int i = min((j - kPxW - kPwW) * NW + wave, kPs - 1);  // weight rows 64i .. 64i+63
+      buffer_load_lds4(rs, &sm.ws[buf][i * 256], voff_s, (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)stage * 4);
+    }
+  };
+
+  floatx16 acc[FN][FM], accm[2];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) accm[k][v] = 0.0f;
+
+  const int xg0 = wave_m == 0 ? 0 : GS + 1;  // first own activation group
+  const int xs0 = 16 * ((4 * h) ^ x_swz(r32));  // k-step j: slot offset xs0 ^ (16 j)
+  u32x4 wraw[FN];
+  float wsc_lo[FN], wsc_hi[FN];
+  bf16x8_t wf[2][FN], xf[2][FM + 1];  // xf[.][FM]: the middle group
+  auto read_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      wraw[i] = *(const u32x4*)&sm.w[buf][(wave_n * FN + i) * 1024 + lane * 16];
+      const uint32_t sw = *(const uint16_t*)&sm.ws[buf][(wave_n * FN * 32 + i * 32 + r32) * 4 + 2 * h];
+      wsc_lo[i] = e4m3_decode(sw & 0xFFu);
+      wsc_hi[i] = e4m3_decode(sw >> 8);
+    }
+  };
+  auto read_x = [&](int slot, int buf, int j) {
+#pragma unroll
+    for (int g = 0; g <= FM; ++g) {
+      const int grp = g < FM ? xg0 + g : GS;
+      const u32x4 v = *(const u32x4*)&sm.x[buf][grp * 4096 + r32 * 128 + (xs0 ^ (16 * j))];
+      xf[slot][g] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  auto decode_w = [&](int slot, int j) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wf[slot][i] = decode8_bf16(wraw[i][j], j < 2 ? wsc_lo[i] : wsc_hi[i]);
+  };
+
+  // prologue: stages 0 and 1
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, nk > 1 ? 1 : 0, 1);
+  wait_vmcnt<kLoads>();
+  __builtin_amdgcn_s_barrier();
+
+  int buf = 0;
+  for (int t = 0; t < nk; ++t) {
+    const int lbuf = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
+    const int lstage = t + 2 < nk ? t + 2 : nk - 1;
+    read_w(buf);
+    read_x(0, buf, 0);
+    decode_w(0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cur = j & 1;
+      if (j < 3) {
+        read_x(cur ^ 1, buf, j + 1);
+        decode_w(cur ^ 1, j + 1);
+      }
+#pragma unroll
+      for (int l = 0; l < (kLoads + 3) / 4; ++l)
+        if (j * ((kLoads + 3) / 4) + l < kLoads) issue(j * ((kLoads + 3) / 4) + l, lstage, lbuf);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
+      // middle group: row 0 takes weight groups 0 and 1 of the wave, row 1 group 2 (and
+      // a dropped product with group 1)
+      const bf16x8_t m0w = wave_m == 0 ? wf[cur][0] : wf[cur][2];
+      accm[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0w, xf[cur][FM], accm[0], 0, 0, 0);
+      accm[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][1], xf[cur][FM], accm[1], 0, 0, 0);
+    }
+    wait_vmcnt<kLoads>();
+    __builtin_amdgcn_s_barrier();
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  GemmProblem q{};
+  q.out = p.out;
+  q.M = p.M;
+  q.N = p.N;
+  q.K = p.K;
+  q.alpha = p.alpha;
+  uint16_t* stage_area = (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN);
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
+  const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
+  store_tile_lds<FM, FN>(acc, q, (int64_t)m0 + xg0 * 32, n_base, lane, stage_area);
+  if (wave_m == 0)
+    store_tile_lds<1, 2>(*(const floatx16(*)[2][1])&accm, q, (int64_t)m0 + GS * 32, n_base, lane,
+                         stage_area);
+  else
+    store_tile_lds<1, 1>(*(const floatx16(*)[1][1])&accm[0], q, (int64_t)m0 + GS * 32, n_base + 64,
+                         lane, stage_area);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
-  // long activations: the tiled kernel when its tiles cover at least a quarter of the
-  // compute units (as the W4A4 planner)
+  // long activations: a tiled kernel when its tiles cover at least a quarter of the
+  // compute units (as the W4A4 planner); 288 x 192 unless 256 x 256 tiles need fewer
+  // passes (measured: 4608 x 3072 x 3072 88.7 us vs 90.4 us, x 12288 x 3072 352.5 vs 365.7)
   const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
   const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  const bool fits32 = (p.M + 256) * p.K * 2 < ((int64_t)1 << 31) && (p.N + 256) * (p.K / 2) < ((int64_t)1 << 31);
+  const int64_t tfit = ((p.M + 287) / 288) * ((p.N + 191) / 192);
+  const bool fits32 = (p.M + 288) * p.K * 2 < ((int64_t)1 << 31) && (p.N + 256) * (p.K / 2) < ((int64_t)1 << 31);
   const bool aligned = (uintptr_t)p.x % 16 == 0 && (uintptr_t)p.w_packed % 16 == 0 &&
                        (uintptr_t)p.w_scales % 4 == 0;
   if (p.K % 64 == 0 && fits32 && aligned && tiles * 4 > cus) {
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    if (tiles > 0x7FFFFFFF || tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // passes over the compute units weighted by MFMAs per wave and k-step (14 vs 16)
+    const int64_t pf = (tfit + cus - 1) / cus, p256 = (tiles + cus - 1) / cus;
+    if (pf * 14 <= p256 * 16)
+      hipLaunchKernelGGL((gemm_w4a16_fit_kernel<288, 192>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   // workgroup shape: 32 weight rows x 32B activation rows, B the smallest of 1, 2, 4 that

@@ -36,9 +36,13 @@ def _check(got, x, wp, ws, wgs, label):
 @pytest.mark.parametrize("M,N,K", [
     (1, 64, 64), (17, 72, 128), (33, 100, 96), (64, 3000, 224), (130, 70, 256),
     (5, 5, 32), (300, 200, 1056), (64, 128, 256),
-    # enough 256 x 256 tiles (more than a quarter of the compute units) for the tiled
-    # kernel: ragged by one row and column, one stage (K = 64), several stages
-    (2049, 2081, 64), (2300, 2000, 192), (2304, 2048, 640),
+    # enough tiles (more than a quarter of the compute units) for the tiled kernels. The
+    # 288 x 192 tile, whenever it needs no more passes than 256 x 256: ragged by one row
+    # and column, one stage (K = 64), several stages
+    (2049, 2081, 64), (2300, 2000, 192), (2304, 2048, 640), (2305, 1537, 128),
+    (2017, 3000, 320),
+    # the 256 x 256 tile (one pass; the 288 x 192 tiling would need two)
+    (4096, 4096, 64),
 ])
 def test_w4a16_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
