@@ -57,6 +57,24 @@ def test_w4a16_small_shapes_in_full(M, N, K):
     _check(got, x, wp, ws, wgs, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 256, 1024), (2305, 1537, 128), (4096, 4096, 64)])
+def test_w4a16_every_scale_code(M, N, K):
+    """Weight scales cycling through all 127 finite E4M3 codes (subnormals and 448
+    included) with random codes: pins the scale conversion on every code, in the split-K,
+    288 x 192 and 256 x 256 kernels."""
+    rng = np.random.default_rng(M + N + K)
+    x = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    ws = (np.arange(N * (K // 16)) % 127).astype(np.uint8).reshape(N, K // 16)
+    ws = ws[rng.permutation(N)]
+    wgs = np.float32(2.0**-7)
+    say("w4a16 every scale code", M, N, K)
+    out, ok = _run(x, wp, ws, wgs)
+    got = to_host(out)
+    assert ok(), "write outside out"
+    _check(got, x, wp, ws, wgs, f"scales {M}x{N}x{K}")
+
+
 def test_w4a16_identity_weights():
     """W = 3 I under w_gs = 2^-6: every product and sum is exact, out = bf16(3 x)."""
     rng = np.random.default_rng(41)
