@@ -124,7 +124,10 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
 // instruction writes whole row segments (FN*64 bytes per row) instead of 16-byte pieces
 // of 32 rows. The 16-byte row padding puts the 32 rows a lane group writes at once in
 // different LDS banks. `blk` must not be used by other waves; LDS order within the wave
-// makes the round trip safe without a barrier.
+// makes the round trip safe without a barrier. The 16-byte row pieces are stored
+// nontemporal (the kernel never reads its output back): measured 1-2% faster on the
+// 4608-row FLUX products, while the same hint on store_tile's 8-byte pieces, which two
+// waves fill half a cache line each, was 5% slower.
 constexpr int kStoreRowPad(int fn) { return fn * 32 + 8; }
 
 //
@@ -183,7 +186,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
         if (m < p.M) {
           const u32x4 v = *(const u32x4*)&blk[r * RS + col];
           if (n_vec && n + 7 < p.N) {
-            *(u32x4*)&p.out[m * p.N + n] = v;
+            __builtin_nontemporal_store(v, (u32x4*)&p.out[m * p.N + n]);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
