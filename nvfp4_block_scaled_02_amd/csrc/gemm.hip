@@ -759,11 +759,14 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // the chip idle: M = 1 gives one tile row, so only N / 192 compute units work while the
 // weights (the bulk of the bytes) stream through them. Here a workgroup owns A x B output
 // blocks of 32 x 32 (32A weight rows, 32B activation rows) and its 4 waves split K:
-// wave w takes the 64-element chunks w, w+4, w+8, ..., so together they read whole
-// 128-byte lines of every row. Each lane loads its fragments straight into registers
-// (16 bytes = 32 codes of one row, the same K mapping as the LDS layouts of the tiled
-// kernels, plus its two scale bytes), D chunks ahead of their use; the four partial sums
-// of each block meet in LDS at the end and are added in a fixed order.
+// the 64-element chunks go in groups of four (one 128-byte line of codes per row), wave w
+// taking groups w, w + 4, ..., so the waves move through K together.
+// Each lane loads its fragments straight into registers (16 bytes = 32 codes of one row,
+// the same K mapping as the LDS layouts of the tiled kernels), DG groups ahead of their
+// use; the scales of a group come with one 16-byte load per row when K % 64 == 0
+// (kVecScale: scale loads, which touch one cache line per row for a few bytes, had cost
+// a third of the time at 256 rows), else two bytes per chunk. The four partial sums of
+// each block meet in LDS at the end and are added in a fixed order.
 //
 // Requires K % 32 == 0, 16-byte aligned packed operands and 4-byte aligned scales, and
 // both operands below 2^31 bytes (32-bit buffer offsets). In a last chunk that holds only
@@ -779,7 +782,7 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // Every workgroup along N repeats the quantization, which is why it is limited to a few
 // thousand elements per thread block.
 constexpr int kFuseElems = 16384;
-template <int A, int B, int D, int NW, bool kFuse>
+template <int A, int B, int DG, int NW, bool kFuse, bool kVecScale>
 __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, FusedQuant fq) {
   __shared__ float red[2][NW][16 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElems / 2 : 16];
@@ -798,7 +801,10 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
   const int nchunks = (int)((p.K + 63) / 64);
-  const int nq = (nchunks - wave + NW - 1) / NW;  // this wave's chunks
+  // groups of four consecutive chunks (one 128-byte line of codes per row, and one
+  // 16-byte load per row brings their scales); wave w takes groups w, w + NW, ...
+  const int ngt = (nchunks + 3) / 4;
+  const int ngroups = (ngt - wave + NW - 1) / NW;  // this wave's groups
 
   const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
   const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
@@ -815,52 +821,93 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
 
-  u32x4 wraw[D][A], xraw[D][B];
-  uint32_t wsr[D][A], xsr[D][B];
-  // chunk number q of this wave (chunk index wave + 4q) into ring slot d
-  auto load = [&](int d, int q) {
-    const int c = wave + NW * q;
+  // ring slot s: the codes of a group's four chunks and its scales (kVecScale: the 16
+  // scale bytes of the four chunks for the lane's row, both lane halves; otherwise the
+  // lane's two bytes of chunk k in word k)
+  u32x4 wraw[DG][4][A], xraw[DG][4][B];
+  u32x4 wsv[DG][A], xsv[DG][B];
+  const uint32_t voff_sv = r32 * spitch;
+  // group G of this wave (chunks 4 (NW G + wave) .. + 3) into ring slot s
+  auto load_group = [&](int s, int G) {
+    const int c0 = 4 * (NW * G + wave);
 #pragma unroll
-    for (int i = 0; i < A; ++i) {
-      wraw[d][i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rwp, (int)voff_p, (int)((uint32_t)(n0 + 32 * i) * pitch + (uint32_t)c * 32), 0);
-      wsr[d][i] = __builtin_amdgcn_raw_buffer_load_b16(
-          rws, (int)voff_s, (int)((uint32_t)(n0 + 32 * i) * spitch + (uint32_t)c * 4), 0);
+    for (int k = 0; k < 4; ++k) {
+      if (c0 + k < nchunks) {
+        const int c = c0 + k;
+#pragma unroll
+        for (int i = 0; i < A; ++i) {
+          wraw[s][k][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              rwp, (int)voff_p, (int)((uint32_t)(n0 + 32 * i) * pitch + (uint32_t)c * 32), 0);
+          if constexpr (!kVecScale)
+            wsv[s][i][k] = __builtin_amdgcn_raw_buffer_load_b16(
+                rws, (int)voff_s, (int)((uint32_t)(n0 + 32 * i) * spitch + (uint32_t)c * 4), 0);
+        }
+        if constexpr (!kFuse) {
+#pragma unroll
+          for (int g = 0; g < B; ++g) {
+            xraw[s][k][g] = __builtin_amdgcn_raw_buffer_load_b128(
+                rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
+            if constexpr (!kVecScale)
+              xsv[s][g][k] = __builtin_amdgcn_raw_buffer_load_b16(
+                  rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+          }
+        }
+      }
     }
+    if constexpr (kVecScale) {
+      // a whole group: its 16 scale bytes lie inside the row; a partial last group takes
+      // 4 bytes per chunk instead (same layout), so no load reaches past the row's end
+      auto vec = [&](__amdgpu_buffer_rsrc_t r, int row0) -> u32x4 {
+        const uint32_t base = (uint32_t)row0 * spitch + (uint32_t)c0 * 4;
+        if (c0 + 4 <= nchunks) return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, (int)voff_sv, (int)base, 0);
+        u32x4 v{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int g = 0; g < B; ++g) {
+        for (int k = 0; k < 4; ++k)
+          if (c0 + k < nchunks) v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff_sv, (int)(base + 4 * k), 0);
+        return v;
+      };
+#pragma unroll
+      for (int i = 0; i < A; ++i) wsv[s][i] = vec(rws, n0 + 32 * i);
       if constexpr (!kFuse) {
-        xraw[d][g] = __builtin_amdgcn_raw_buffer_load_b128(
-            rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
-        xsr[d][g] = __builtin_amdgcn_raw_buffer_load_b16(
-            rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+#pragma unroll
+        for (int g = 0; g < B; ++g) xsv[s][g] = vec(rxs, m0 + 32 * g);
       }
     }
   };
-  auto compute = [&](int d, int q) {
+  // chunk k of group G (ring slot s); the lane's two scale bytes sit in the low 16 bits
+  auto compute = [&](int s, int G, int k) {
+    const int c = 4 * (NW * G + wave) + k;
     // upper lane half of a 32-element last chunk: no elements, zero scale
-    const bool dead = h == 1 && (int64_t)(wave + NW * q) * 64 + 32 >= p.K;
+    const bool dead = h == 1 && (int64_t)c * 64 + 32 >= p.K;
+    auto lane_scales = [&](uint32_t v) { return kVecScale ? v >> (16 * h) : v; };
+    u32x4 xr[B];
+    uint32_t xs[B];
     if constexpr (kFuse) {
       // activation fragment from LDS (rows past M and the dead upper half read as zero)
-      const int c = wave + NW * q;
       const bool live = r32 < p.M && !dead;
-      xraw[d][0] = live ? *(const u32x4*)&xq[r32 * pitch + (uint32_t)c * 32 + h * 16]
-                        : u32x4{0u, 0u, 0u, 0u};
-      xsr[d][0] = live ? (uint32_t)*(const uint16_t*)&xqs[r32 * spitch + (uint32_t)c * 4 + h * 2]
-                       : 0u;
+      xr[0] = live ? *(const u32x4*)&xq[r32 * pitch + (uint32_t)c * 32 + h * 16]
+                   : u32x4{0u, 0u, 0u, 0u};
+      xs[0] = live ? (uint32_t)*(const uint16_t*)&xqs[r32 * spitch + (uint32_t)c * 4 + h * 2]
+                   : 0u;
+    } else {
+#pragma unroll
+      for (int g = 0; g < B; ++g) {
+        xr[g] = xraw[s][k][g];
+        xs[g] = lane_scales(xsv[s][g][k]);
+      }
     }
     half2_t wsc[A], xsc[B];
 #pragma unroll
-    for (int i = 0; i < A; ++i) wsc[i] = scales_to_f16<true>(dead ? 0u : wsr[d][i]);
+    for (int i = 0; i < A; ++i) wsc[i] = scales_to_f16<true>(dead ? 0u : lane_scales(wsv[s][i][k]));
 #pragma unroll
-    for (int g = 0; g < B; ++g) xsc[g] = scales_to_f16<true>(dead ? 0u : xsr[d][g]);
+    for (int g = 0; g < B; ++g) xsc[g] = scales_to_f16<true>(dead ? 0u : xs[g]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       half8_t wf[A], xf[B];
 #pragma unroll
-      for (int i = 0; i < A; ++i) wf[i] = decode8<true>(wraw[d][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
+      for (int i = 0; i < A; ++i) wf[i] = decode8<true>(wraw[s][k][i][j], j < 2 ? wsc[i].xx : wsc[i].yy);
 #pragma unroll
-      for (int g = 0; g < B; ++g) xf[g] = decode8<true>(xraw[d][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
+      for (int g = 0; g < B; ++g) xf[g] = decode8<true>(xr[g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
 #pragma unroll
       for (int i = 0; i < A; ++i)
 #pragma unroll
@@ -899,16 +946,18 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
   };
 
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nq) load(d, d);
+  for (int s = 0; s < DG; ++s)
+    if (s < ngroups) load_group(s, s);
   // (after the first weight loads, so their latency overlaps the quantization)
   if constexpr (kFuse) quantize_to_lds();
-  for (int q = 0; q < nq; q += D) {
+  for (int G = 0; G < ngroups; G += DG) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (q + d < nq) {
-        compute(d, q + d);
-        if (q + d + D < nq) load(d, q + d + D);
+    for (int s = 0; s < DG; ++s) {
+      if (G + s < ngroups) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (4 * (NW * (G + s) + wave) + k < nchunks) compute(s, G + s, k);
+        if (G + s + DG < ngroups) load_group(s, G + s + DG);
       }
     }
   }
@@ -1028,9 +1077,18 @@ hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s)
   constexpr int NW = 4;  // 8 or 16 waves per workgroup measured no faster
   const dim3 grid((unsigned)wgs), block(64 * NW);
   const FusedQuant none{};
-  if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8, NW, false>), grid, block, 0, stream, p, none);
-  else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 6, NW, false>), grid, block, 0, stream, p, none);
-  else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 4, NW, false>), grid, block, 0, stream, p, none);
+  // 16-byte scale loads need 4-byte aligned scale rows (K % 64 == 0)
+  // groups in flight per wave by workgroup shape (registers: about 40 VGPRs per group
+  // and activation group); measured: deeper rings gain nothing
+  if (p.K % 64 == 0) {
+    if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, NW, false, true>), grid, block, 0, stream, p, none);
+    else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 3, NW, false, true>), grid, block, 0, stream, p, none);
+    else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 2, NW, false, true>), grid, block, 0, stream, p, none);
+  } else {
+    if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, NW, false, false>), grid, block, 0, stream, p, none);
+    else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 3, NW, false, false>), grid, block, 0, stream, p, none);
+    else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 2, NW, false, false>), grid, block, 0, stream, p, none);
+  }
   return hipGetLastError();
 }
 
@@ -1123,8 +1181,12 @@ bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
 hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream) {
   const int64_t wgs = (p.N + 31) / 32;
   if (p.M > 32 || p.M * p.K > kFuseElems || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 8, 4, true>), dim3((unsigned)wgs), dim3(256), 0,
-                     stream, p, fq);
+  if (p.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, 4, true, true>), dim3((unsigned)wgs), dim3(256), 0,
+                       stream, p, fq);
+  else
+    hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, 4, true, false>), dim3((unsigned)wgs), dim3(256), 0,
+                       stream, p, fq);
   return hipGetLastError();
 }
 
