@@ -419,7 +419,9 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
-  wait_vmcnt<0>();
+  // stages 0 and 1 (stage 0 reads stage 1's first chunk ahead); stage 2's loads may
+  // still be in flight: the wait at the end of stage 0 covers them
+  wait_vmcnt<kPaW + kPwW>();
   __builtin_amdgcn_s_barrier();
   read_chunk(0, 0, 0, 0, 0);
   decode_step(0, 0, wf[0], xf[0]);
@@ -676,7 +678,9 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
-  wait_vmcnt<0>();
+  // stages 0 and 1 (stage 0 reads stage 1's first chunk ahead); stage 2's loads may
+  // still be in flight: the wait at the end of stage 0 covers them
+  wait_vmcnt<kPaW + kPwW>();
   __builtin_amdgcn_s_barrier();
   read_chunk(0, 0, wave_m, 0, 0);
   decode_step(0, 0, 0);
