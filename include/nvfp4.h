@@ -112,8 +112,10 @@ typedef enum {
                              and FLUX widths split into whole multiples of 256 tiles */
   NVFP4_GEMM_SPLITK = 2,  /* K split over a workgroup's waves: short activations */
   NVFP4_GEMM_GENERIC = 3, /* 256 x 256 tiles, register-staged loads: any K % 16 == 0 */
-  NVFP4_GEMM_TILE128 = 4  /* 128 x 192 output tiles (K % 128 == 0): activations of a few
+  NVFP4_GEMM_TILE128 = 4, /* 128 x 192 output tiles (K % 128 == 0): activations of a few
                              hundred to a few thousand rows */
+  NVFP4_GEMM_TILE128X128 = 5 /* 128 x 128 output tiles (K % 128 == 0): the most tiles, where
+                                the larger ones would leave compute units idle */
 } nvfp4_gemm_kernel;
 
 /*

@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
 // across stages ----
 //
 // 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
-// 2 x 3 for 128 x 192 (medium M: four times the tiles, so a few thousand rows still fill
-// the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
+// 2 x 3 for 128 x 192 and 2 x 2 for 128 x 128 (medium M: more tiles, so fewer rows still
+// fill the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
 // are the fit kernel's (below): code loads of 16 rows x the stage's 64 bytes (4 lanes per
 // row) into 1 KiB pieces whose 16-byte chunks are swizzled by chunk_swz, scale loads of
 // 64 rows x 16 bytes (a pair of stages) into three pair buffers, four code buffers filled
@@ -1121,6 +1121,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   // 256 x 256) for activations too short to fill the chip with the larger tiles
   const int64_t t128 = ((M + 127) / 128) * ((N + 191) / 192);
   const double c128 = fast ? (double)passes(t128, cus) * (nk * 48 * mfma_cycles(5.0 / 6.0) + 20000.0) : 1e300;
+  // 128 x 128 tiles (2 x 2 blocks per wave, one fragment decoded per MFMA): the most
+  // tiles, for activations of a few hundred rows or a few hundred x wide weights
+  const int64_t t128sq = ((M + 127) / 128) * ((N + 127) / 128);
+  const double c128sq = fast ? (double)passes(t128sq, cus) * (nk * 32 * mfma_cycles(1.0) + 20000.0) : 1e300;
   // Split K inside the workgroup (short activations, at most 512 rows: it reads the
   // activations once per 32 weight rows, which stops paying beyond that). Measured cost:
   // ~6000 cycles of launch and reduction plus, per pass over the chip, 360 / 740 / 1330
@@ -1142,6 +1146,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
     double best = c256;
     if (fit_ok && cfit <= best) { plan.kernel = NVFP4_GEMM_FIT; best = cfit; }
     if (fast && c128 < best) { plan.kernel = NVFP4_GEMM_TILE128; best = c128; }
+    if (fast && c128sq < best) { plan.kernel = NVFP4_GEMM_TILE128X128; best = c128sq; }
     if (split_ok && M <= 512 && csplit < best) plan.kernel = NVFP4_GEMM_SPLITK;
   } else if (split_ok && M <= 512 && tfit * 4 <= cus) {
     // against the register-staged kernel (K % 128 != 0): few tiles only
@@ -1167,6 +1172,12 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
       const int64_t t = ((p.M + 127) / 128) * ((p.N + 191) / 192);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
       hipLaunchKernelGGL((gemm_dma_kernel<128, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case NVFP4_GEMM_TILE128X128: {
+      const int64_t t = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+      if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_dma_kernel<128, 128>), dim3((unsigned)t), dim3(256), 0, stream, p);
       return hipGetLastError();
     }
     default:
