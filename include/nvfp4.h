@@ -114,8 +114,10 @@ typedef enum {
   NVFP4_GEMM_GENERIC = 3, /* 256 x 256 tiles, register-staged loads: any K % 16 == 0 */
   NVFP4_GEMM_TILE128 = 4, /* 128 x 192 output tiles (K % 128 == 0): activations of a few
                              hundred to a few thousand rows */
-  NVFP4_GEMM_TILE128X128 = 5 /* 128 x 128 output tiles (K % 128 == 0): the most tiles, where
-                                the larger ones would leave compute units idle */
+  NVFP4_GEMM_TILE128X128 = 5, /* 128 x 128 output tiles (K % 128 == 0): more tiles, where
+                                 the larger ones would leave compute units idle */
+  NVFP4_GEMM_TILE128X64 = 6    /* 128 x 64 output tiles (K % 128 == 0): more still, for a few
+                                 hundred rows */
 } nvfp4_gemm_kernel;
 
 /*

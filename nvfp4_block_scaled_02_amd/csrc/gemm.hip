@@ -279,8 +279,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
 // across stages ----
 //
 // 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
-// 2 x 3 for 128 x 192 and 2 x 2 for 128 x 128 (medium M: more tiles, so fewer rows still
-// fill the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
+// 2 x 3 for 128 x 192, 2 x 2 for 128 x 128 and 2 x 1 for 128 x 64 (medium M: more tiles,
+// so fewer rows still fill the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
 // are the fit kernel's (below): code loads of 16 rows x the stage's 64 bytes (4 lanes per
 // row) into 1 KiB pieces whose 16-byte chunks are swizzled by chunk_swz, scale loads of
 // 64 rows x 16 bytes (a pair of stages) into three pair buffers, four code buffers filled
@@ -1041,10 +1041,11 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
   *(u32x4*)&out[i * 8] = __builtin_bit_cast(u32x4, v);
 }
 
-// Rough cost model (core cycles of one launch) used to choose between the tiled
-// kernels; calibrated on the 32x32x16 f16 MFMA, which issues every ~34 cycles back to
-// back and slows down once a wave has more than about 3 VALU instructions per MFMA (the
-// decode costs 8 VALU per fragment of 8 elements per lane).
+// Rough cost model (core cycles of one launch) used to choose between the kernels; the
+// 32x32x16 f16 MFMA issues every ~34 cycles back to back and slows by ~5.5 cycles per
+// VALU instruction beyond about 3 per MFMA (the decode costs 8 VALU per fragment of 8
+// elements per lane), a slope fitted to the 128 x 64 / 128 x 128 / 128 x 192 tiles'
+// measured times; the split-K costs are its own measurements.
 #ifndef NVFP4_GEMM_KC
 #define NVFP4_GEMM_KC 2
 #endif
@@ -1063,7 +1064,7 @@ constexpr int kFitBM = NVFP4_FIT_BM, kFitBN = NVFP4_FIT_BN;
 
 double mfma_cycles(double frags_per_mfma) {
   const double v = 8.0 * frags_per_mfma;
-  return 34.0 + (v > 3.0 ? 3.5 * (v - 3.0) : 0.0);
+  return 34.0 + (v > 3.0 ? 5.5 * (v - 3.0) : 0.0);
 }
 int64_t passes(int64_t wgs, int64_t cus) { return (wgs + cus - 1) / cus; }
 
@@ -1125,15 +1126,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   // tiles, for activations of a few hundred rows or a few hundred x wide weights
   const int64_t t128sq = ((M + 127) / 128) * ((N + 127) / 128);
   const double c128sq = fast ? (double)passes(t128sq, cus) * (nk * 32 * mfma_cycles(1.0) + 20000.0) : 1e300;
+  // 128 x 64 tiles (2 x 1 blocks per wave, 1.5 fragments per MFMA): shorter tiles still
+  const int64_t t12864 = ((M + 127) / 128) * ((N + 63) / 64);
+  const double c12864 = fast ? (double)passes(t12864, cus) * (nk * 16 * mfma_cycles(1.5) + 20000.0) : 1e300;
   // Split K inside the workgroup (short activations, at most 512 rows: it reads the
   // activations once per 32 weight rows, which stops paying beyond that). Measured cost:
-  // ~6000 cycles of launch and reduction plus, per pass over the chip, 360 / 740 / 1330
+  // ~6000 cycles of launch and reduction plus, per pass over the chip, 360 / 740 / 1100
   // cycles per 128 elements of K for 32-row groups B = 1 / 2 / 4 per workgroup.
   const bool split_ok = aligned && K % 32 == 0 && fits32;
   const SplitShape sh = splitk_shape(M);
   const int64_t wsplit = ((N + 31) / 32) * ((M + 32 * sh.b - 1) / (32 * sh.b));
   const double csplit = 6000.0 + (double)passes(wsplit, cus) * ((double)K / 128.0) *
-                                     (sh.b == 1 ? 360.0 : sh.b == 2 ? 740.0 : 1330.0);
+                                     (sh.b == 1 ? 360.0 : sh.b == 2 ? 740.0 : 1100.0);
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
 #ifdef NVFP4_GEMM_FORCE_TILE
@@ -1147,6 +1151,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
     if (fit_ok && cfit <= best) { plan.kernel = NVFP4_GEMM_FIT; best = cfit; }
     if (fast && c128 < best) { plan.kernel = NVFP4_GEMM_TILE128; best = c128; }
     if (fast && c128sq < best) { plan.kernel = NVFP4_GEMM_TILE128X128; best = c128sq; }
+    if (fast && c12864 < best) { plan.kernel = NVFP4_GEMM_TILE128X64; best = c12864; }
     if (split_ok && M <= 512 && csplit < best) plan.kernel = NVFP4_GEMM_SPLITK;
   } else if (split_ok && M <= 512 && tfit * 4 <= cus) {
     // against the register-staged kernel (K % 128 != 0): few tiles only
@@ -1178,6 +1183,12 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
       const int64_t t = ((p.M + 127) / 128) * ((p.N + 127) / 128);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
       hipLaunchKernelGGL((gemm_dma_kernel<128, 128>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case NVFP4_GEMM_TILE128X64: {
+      const int64_t t = ((p.M + 127) / 128) * ((p.N + 63) / 64);
+      if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_dma_kernel<128, 64>), dim3((unsigned)t), dim3(256), 0, stream, p);
       return hipGetLastError();
     }
     default:

@@ -109,7 +109,7 @@ def test_gemm_plan_routes_shapes(lib):
         st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    FIT, TILE, SPLIT, GEN, T128, T128SQ = 1, 0, 2, 3, 4, 5
+    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864 = 1, 0, 2, 3, 4, 5, 6
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
                     (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
@@ -118,13 +118,15 @@ def test_gemm_plan_routes_shapes(lib):
     # wide weights with few rows: split-K's workgroups still fill the chip
     for M, N in [(1, 18432), (17, 18432), (64, 18432)]:
         assert plan(M, N, 3072) == (L.SUCCESS, SPLIT), (M, N)
-    assert plan(128, 12288, 3072) == (L.SUCCESS, T128SQ)
+    assert plan(128, 12288, 3072) == (L.SUCCESS, T12864)
     assert plan(256, 12288, 3072) == (L.SUCCESS, T128SQ)
     assert plan(512, 12288, 3072) == (L.SUCCESS, T128)
     for M in (1500, 2000):   # a few thousand rows: 128 x 192 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128), M
-    for M in (300, 600, 1000):   # a few hundred to a thousand rows: 128 x 128 tiles
+    for M in (800, 1000):   # about a thousand rows: 128 x 128 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128SQ), M
+    for M in (300, 512, 600):   # a few hundred rows: 128 x 64 tiles
+        assert plan(M, 3072, 3072) == (L.SUCCESS, T12864), M
     assert plan(2600, 1650, 128) == (L.SUCCESS, T128)
     assert plan(4096, 4096, 128) == (L.SUCCESS, TILE)
     assert plan(18432, 12288, 3072) == (L.SUCCESS, TILE)

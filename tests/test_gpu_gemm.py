@@ -74,9 +74,11 @@ def test_gemm_small_shapes_in_full(M, N, K):
     (2000, 4000, 1152, "fit"),
     # 128 x 192 tiles: the same kinds of cases at a few thousand rows
     (2600, 1650, 384, "tile128"), (2500, 1900, 256, "tile128"), (2000, 2100, 640, "tile128"),
-    # 128 x 128 tiles: a few hundred to about a thousand rows
-    (1500, 2500, 128, "tile128x128"), (513, 1000, 640, "tile128x128"),
-    (777, 385, 1152, "tile128x128"), (600, 700, 256, "tile128x128"),
+    # 128 x 128 tiles: about a thousand rows
+    (1500, 2500, 128, "tile128x128"), (1100, 2200, 384, "tile128x128"),
+    (1000, 2900, 640, "tile128x128"),
+    # 128 x 64 tiles: a few hundred rows
+    (513, 1000, 640, "tile128x64"), (777, 385, 1152, "tile128x64"), (600, 700, 256, "tile128x64"),
     (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])
