@@ -164,3 +164,41 @@ def test_linear_matches_quantize_then_gemm(name):
     assert np.array_equal(to_host(g2), got)
     rows = _sample_rows(wl.M, np.random.default_rng(12), n=32)
     _assert_close(got[rows], ap[rows], as_[rows], ags, wp, ws, wgs, name)
+
+
+def test_operands_beyond_32bit_offsets():
+    """Largest-size case: 4 194 081 activation rows x K = 1024, so the packed activations
+    (2.1 GB) pass 2^31 bytes and the bf16 input (8.6 GB) passes 2^32; the planner sends
+    the GEMM to the register-staged kernel (64-bit addressing). Generated on the device;
+    rows straddling the 2^31- and 2^32-byte boundaries of either tensor, and the ends, are
+    checked against the oracle: quantization bit-exact, GEMM within the bound."""
+    M, N, K = (1 << 22) + 777, 72, 1024
+    assert nv.gemm_plan(M, N, K) == "generic"
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, M, 1 << 20):   # fp32 draws in slices, rounded to bf16
+        r1 = min(M, r0 + (1 << 20))
+        x[r0:r1] = torch.randn((r1 - r0, K), device="cuda", generator=gen).to(torch.bfloat16)
+    rng = np.random.default_rng(22)
+    w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ags = nv.calibrate(x)
+    wgs = O.global_scale(w)
+    wp, ws = O.quantize(w, wgs)
+    say("gemm beyond 32-bit offsets", M, N, K)
+    ap, as_ = nv.quantize(x, ags)
+    out = nv.gemm(ap, as_, ags, u8_to_dev(wp), u8_to_dev(ws), float(wgs))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, M - 1, M - 2, M // 2,
+                   (1 << 22) - 1, 1 << 22, (1 << 22) + 1,     # packed rows across 2^31 bytes
+                   (1 << 20) - 1, 1 << 20, (1 << 21) - 1, 1 << 21,  # bf16 rows across 2^31, 2^32
+                   *rng.choice(M, 24, replace=False).tolist()})
+    idx = torch.tensor(rows, device="cuda")
+    xs = x.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    want_p, want_s = O.quantize(xs, np.float32(ags))
+    got_p = ap.index_select(0, idx).cpu().numpy()
+    got_s = as_.index_select(0, idx).cpu().numpy()
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_s, want_s)
+    got = out.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    _assert_close(got, want_p, want_s, ags, wp, ws, wgs, "beyond 32-bit offsets")
+    del x, ap, as_, out
+    torch.cuda.empty_cache()
