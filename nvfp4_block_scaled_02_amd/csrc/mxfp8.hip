@@ -262,7 +262,9 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 1 ? 1 : nk - 1, 1);
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 2 ? 2 : nk - 1, 2);
-  wait_vmcnt<0>();
+  // scales and stages 0 and 1 (stage 0 reads stage 1's fragments ahead); stage 2's loads
+  // may still be in flight: the wait at the end of stage 0 covers them
+  wait_vmcnt<kLoads>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int k = 0; k < kReads; ++k) read_one(k, 0, 0, 0);
@@ -449,7 +451,9 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 1 ? 1 : nk - 1, 1);
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 2 ? 2 : nk - 1, 2);
-  wait_vmcnt<0>();
+  // scales and stages 0 and 1 (stage 0 reads stage 1's fragments ahead); stage 2's loads
+  // may still be in flight: the wait at the end of stage 0 covers them
+  wait_vmcnt<kLoads>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int k = 0; k < kReads; ++k) read_one(k, 0, 0, 0);
