@@ -20,8 +20,8 @@
 //    below an f16-staged design.
 //  * LDS layout of a packed tile: a lane reads its operand fragment for a 64-element
 //    chunk (row r, bytes [16h, 16h+16) of the chunk) with one 16-byte LDS load, free of
-//    bank conflicts. The direct-to-LDS kernels (256 x 256 and 288 x 192 tiles) keep each
-//    row's 64 bytes of a stage together in 1 KiB pieces of 16 rows with the 16-byte
+//    bank conflicts. The direct-to-LDS kernels (288 x 192, 256 x 256, 128 x 192, 128 x 128
+//    and 128 x 64 tiles) keep each row's 64 bytes of a stage together in 1 KiB pieces of 16 rows with the 16-byte
 //    chunks swizzled (chunk_swz), because their loads read whole 64-byte row segments;
 //    the register-staged kernel stores 64 slots of 16 bytes per 32-row group and chunk
 //    in MFMA lane order.
@@ -34,8 +34,13 @@
 //    and one packed f16 multiply per pair gives q * s exactly (all values are normal
 //    f16, so no step depends on the denormal mode).
 //  * The weights are the MFMA's A operand and the activations its B operand, so each
-//    lane ends up holding 4 consecutive output columns of one row: 8-byte bf16 stores.
-//  * Epilogue: fp32 accumulator * alpha (fp32), round to nearest even bf16.
+//    lane ends up holding 4 consecutive output columns of one row.
+//  * Epilogue: fp32 accumulator * alpha (fp32), round to nearest even bf16. The
+//    direct-to-LDS kernels pass each 32-row group of a wave's blocks through LDS and
+//    store 16-byte row pieces; the others store each lane's 8 bytes directly.
+//  * Short activations (split-K kernel): K is split over the waves of a workgroup and
+//    the partial sums meet in LDS; nvfp4_linear's fused form quantizes the activations
+//    into LDS first.
 #include "gemm_common.hpp"
 #include "quant_common.hpp"
 
@@ -1140,12 +1145,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
                                      (sh.b == 1 ? 360.0 : sh.b == 2 ? 740.0 : 1100.0);
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
-#ifdef NVFP4_GEMM_FORCE_TILE
-  // development switch: 0 = 256x256, 1 = fit tile, 2 = split-K
-  if (NVFP4_GEMM_FORCE_TILE == 2 && split_ok) plan.kernel = NVFP4_GEMM_SPLITK;
-  else if (NVFP4_GEMM_FORCE_TILE == 1 && fit_ok) plan.kernel = NVFP4_GEMM_FIT;
-  return plan;
-#endif
   if (fast || fit_ok) {
     double best = c256;
     if (fit_ok && cfit <= best) { plan.kernel = NVFP4_GEMM_FIT; best = cfit; }

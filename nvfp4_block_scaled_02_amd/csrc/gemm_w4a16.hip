@@ -13,7 +13,12 @@
 // multiply): the fp4 -> fp32 conversion gives q, one fp32 multiply by s, and a packed
 // conversion to bf16 (exact). 16 VALU per 8 elements per lane; the activations need none.
 //
-// Structure (split K inside the workgroup, as the W4A4 short-activation kernel): a
+// Structure: two forms, chosen by the number of output tiles.
+//  * Long activations (more than a quarter of the compute units' worth of 256 x 256
+//    tiles, K % 64 == 0, aligned operands): tiled kernels with the bf16 activations
+//    staged in LDS and the weights 4-bit in LDS (288 x 192 and 256 x 256 tiles,
+//    described below).
+//  * Otherwise, split K inside the workgroup, as in the W4A4 short-activation kernel: a
 // workgroup owns 32 weight rows x 32B activation rows; its 4 waves take interleaved
 // 64-element chunks of K (wave w: chunks w, w+4, ...), load their fragments straight into
 // registers D chunks ahead, and the four partial sums of each 32x32 block meet in LDS in
