@@ -84,8 +84,9 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(wl, d, ags, wgs, seconds):
-    """The oracle as it stands, on the first R activation rows (R grows until about
-    `seconds` of CPU work), full weights; scaled to TFLOP/s of the same 2*R*N*K count."""
+    """The oracle as it stands on the workload's activation rows, full weights: chunks of
+    rows in order (wrapping round to row 0 after the last) until about `seconds` of CPU
+    work; scaled to TFLOP/s of the same 2*rows*N*K count."""
     import numpy as np
 
     from oracle import nvfp4_oracle as O
@@ -98,14 +99,15 @@ def cpu_baseline(wl, d, ags, wgs, seconds):
     except Exception:  # threadpoolctl missing: report the affinity size
         cores = len(os.sched_getaffinity(0))
     wp, ws = O.quantize(d["w"], wgs)  # offline weight quantization, not timed
-    rows_done, t_total, chunk = 0, 0.0, 64
-    while t_total < seconds and rows_done < wl.M:
-        r1 = min(wl.M, rows_done + chunk)
+    rows_done, t_total, chunk, r0 = 0, 0.0, 64, 0
+    while t_total < seconds:
+        r1 = min(wl.M, r0 + chunk)
         t0 = time.perf_counter()
-        ap, as_ = O.quantize(d["x"][rows_done:r1], ags)
+        ap, as_ = O.quantize(d["x"][r0:r1], ags)
         O.gemm_ref(ap, as_, ags, wp, ws, wgs, with_abs=False)
         t_total += time.perf_counter() - t0
-        rows_done = r1
+        rows_done += r1 - r0
+        r0 = 0 if r1 == wl.M else r1
         chunk = min(chunk * 2, 1024)
     flops = 2.0 * rows_done * wl.N * wl.K
     return {
@@ -113,9 +115,9 @@ def cpu_baseline(wl, d, ags, wgs, seconds):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"first {rows_done} of {wl.M} activation rows x full [{wl.N}x{wl.K}] weights: "
-                  f"NumPy quantize (1 thread) + float64 GEMM reference ({cores} BLAS threads), "
-                  f"{t_total:.1f} s",
+        "sample": f"{rows_done} activation rows ({rows_done / wl.M:.2f} passes over the {wl.M} rows) "
+                  f"x full [{wl.N}x{wl.K}] weights: NumPy quantize (1 thread) + float64 GEMM "
+                  f"reference ({cores} BLAS threads), {t_total:.1f} s",
     }
 
 
