@@ -31,10 +31,14 @@
  *     amax = max|x|; s = E4M3(RN(amax / RN(6 * global))) with ties to the even code and
  *     saturation at 448; d = RN(s * global); code_i = E2M1(RN(|x_i| / d)) with ties to
  *     the even code, saturation at 6 and the sign of x_i copied (d == 0 gives magnitude 0).
- *   - GEMM: out = bf16_RNE(RN(a_global * w_global) * sum_k a_k w_k) with the decoded
- *     (E2M1 x E4M3) operands; the products are exact and accumulate in fp32. Any result
- *     within 2^-10 * sum_k |a_k w_k| (global scales included) + 1 bf16 ulp of the exact
- *     value is correct; the library's result is deterministic for a given shape.
+ *   - GEMM: out = bf16_RNE(RN(alpha * sum_k a_k w_k)) with the decoded (E2M1 x E4M3)
+ *     operands and alpha = RN(a_global * w_global); the products are exact and
+ *     accumulate in fp32. Where that alpha would not be a normal fp32 (valid global
+ *     scales multiply to anything in [2^-180, 2^180]) the product is applied as m * 2^e
+ *     instead (m the rounded product of the two scales' frexp mantissas, 2^e by an exact
+ *     ldexp). Any result within 2^-10 * sum_k |a_k w_k| (global scales included) + 1 bf16
+ *     ulp of the exact value is correct; the library's result is deterministic for a
+ *     given shape.
  *
  * Preconditions that are not checked (checking them would read the data):
  *   inputs are finite; buffers do not overlap; pointers are device memory of the
@@ -275,9 +279,10 @@ float nvfp4_global_scale_from_amax(float amax);
  * when the kernel runs (a value outside [2^-90, 2^90] is clamped into it; NaN and values
  * <= 0 read as 1.0). Bit-exact to nvfp4_quantize with that value.
  *
- * nvfp4_gemm_devgs: nvfp4_gemm with alpha = RN32(a_gs_device[0] * w_gs_device[0]) read
- * when the kernel runs; bit-exact to nvfp4_gemm with the same two values. The values
- * must be finite and > 0.
+ * nvfp4_gemm_devgs: nvfp4_gemm with the two global scales read from a_gs_device[0] and
+ * w_gs_device[0] when the kernel runs, each clamped as nvfp4_quantize_devgs clamps its
+ * scale (into [2^-90, 2^90]; NaN and values <= 0 read as 1.0); bit-exact to nvfp4_gemm
+ * with the two values so read.
  *
  * nvfp4_linear_devgs: nvfp4_linear with both global scales device-resident.
  */

@@ -141,8 +141,9 @@ int nvfp4_gemm(const void* ap, const void* as, float ags, const void* wp, const 
   nvfp4::LaunchInfo info;
   s = current_device(&info);
   if (s) return s;
+  const nvfp4::Alpha al = nvfp4::split_alpha(ags, wgs);
   nvfp4::GemmProblem p{(const uint8_t*)ap, (const uint8_t*)as, (const uint8_t*)wp,
-                       (const uint8_t*)ws, (uint16_t*)out, M, N, K, ags * wgs};
+                       (const uint8_t*)ws, (uint16_t*)out, M, N, K, al.m, nullptr, nullptr, al.e};
   hipError_t e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
@@ -281,8 +282,9 @@ int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float
   nvfp4::LaunchInfo info;
   s = current_device(&info);
   if (s) return s;
+  const nvfp4::Alpha al = nvfp4::split_alpha(ags, wgs);
   nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
-                       M, N, K, ags * wgs};
+                       M, N, K, al.m, nullptr, nullptr, al.e};
   hipError_t e;
   if (N > 0 && nvfp4::linear_fused(M, N, K, true, info.num_cus)) {
     const float den = 6.0f * ags;

@@ -35,9 +35,11 @@
 //    f16, so no step depends on the denormal mode).
 //  * The weights are the MFMA's A operand and the activations its B operand, so each
 //    lane ends up holding 4 consecutive output columns of one row.
-//  * Epilogue: fp32 accumulator * alpha (fp32), round to nearest even bf16. The
-//    direct-to-LDS kernels pass each 32-row group of a wave's blocks through LDS and
-//    store 16-byte row pieces; the others store each lane's 8 bytes directly.
+//  * Epilogue: fp32 accumulator * a_global * w_global (one fp32 multiply; split_alpha
+//    adds an exact power-of-two ldexp for scale pairs whose product leaves the normal
+//    binary32 range), round to nearest even bf16. The direct-to-LDS kernels pass each
+//    32-row group of a wave's blocks through LDS and store 16-byte row pieces; the
+//    others store each lane's 8 bytes directly.
 //  * Short activations (split-K kernel): K is split over the waves of a workgroup and
 //    the partial sums meet in LDS; nvfp4_linear's fused form quantizes the activations
 //    into LDS first.
@@ -152,7 +154,7 @@ __device__ __forceinline__ void store_stage(const StageRegs<ROWS, KC, NT>& r, ui
 
 // WM x WN waves; wave (wave_m, wave_n) owns activation rows [wave_m*WTM, +WTM) and
 // weight rows (output columns) [wave_n*WTN, +WTN) of the BM x BN tile.
-template <int BM, int BN, int KC, int WM, int WN, bool kHw, bool kFast>
+template <int BM, int BN, int KC, int WM, int WN, bool kHw, bool kFast, bool kExp>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
   constexpr int NT = 64 * WM * WN;
   __shared__ GemmSmem<BM, BN, KC> sm;
@@ -277,7 +279,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
     __syncthreads();
   }
 
-  store_tile<FM, FN>(acc, p, m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
+  store_tile<FM, FN, kExp>(acc, p, gemm_alpha(p), m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
 // ---- 256 x 256 and 128 x 192 tiles: direct-to-LDS loads, four code stages, one pipeline
@@ -301,7 +303,7 @@ struct alignas(16) GemmSmem256 {
 
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
 // (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
-template <int BM, int BN>
+template <int BM, int BN, bool kExp>
 __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   constexpr int NW = 4, WM = 2, WN = 2;
   __shared__ GemmSmem256<BM, BN> sm;
@@ -481,8 +483,9 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
-  store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN, lane,
-                         (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+  store_tile_lds<FM, FN, false, kExp>(acc, p, gemm_alpha(p), (int64_t)m0 + wave_m * WTM,
+                                      (int64_t)n0 + wave_n * WTN, lane,
+                                      (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- fit-tile path: 288 x 192 tiles ------------------------------------------------------
@@ -530,7 +533,7 @@ struct alignas(16) GemmSmemFit {
 // buffer u % 3 and are loaded during stages 2u-4 and 2u-3 (one load per wave each), so
 // they are complete before stage 2u-1 first reads them, and their buffer's previous pair
 // was last read in stage 2u-5.
-template <int BM, int BN>
+template <int BM, int BN, bool kExp>
 __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int NW = 4;
   constexpr int GX = BM / 32, GW = BN / 32;
@@ -755,11 +758,12 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.w), "store staging fits");
-  store_tile_lds<FM, FN>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane,
-                         (uint16_t*)&sm.w[0][0] + wave * 32 * kStoreRowPad(FN));
+  const Alpha alpha = gemm_alpha(p);
+  store_tile_lds<FM, FN, false, kExp>(acc, p, alpha, (int64_t)m0 + xg0 * 32, n_base, lane,
+                                      (uint16_t*)&sm.w[0][0] + wave * 32 * kStoreRowPad(FN));
   // group GS: wave m = 0 stores column quads 0-1 of every block, m = 1 quads 2-3
-  store_tile<1, FN>(*(const floatx16(*)[FN][1])&accs, p, (int64_t)m0 + GS * 32, n_base, lane,
-                    wave_m * 2, wave_m * 2 + 2);
+  store_tile<1, FN, kExp>(*(const floatx16(*)[FN][1])&accs, p, alpha, (int64_t)m0 + GS * 32,
+                          n_base, lane, wave_m * 2, wave_m * 2 + 2);
 }
 
 // ---- small-M path: split K inside the workgroup -----------------------------------------
@@ -791,7 +795,7 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // Every workgroup along N repeats the quantization, which is why it is limited to a few
 // thousand elements per thread block.
 constexpr int kFuseElems = 16384;
-template <int A, int B, int DG, int NW, bool kFuse, bool kVecScale>
+template <int A, int B, int DG, int NW, bool kFuse, bool kVecScale, bool kExp>
 __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, FusedQuant fq) {
   __shared__ float red[2][NW][16 * 64];
   __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElems / 2 : 16];
@@ -972,9 +976,9 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
   }
 
   // Partial sums: block by block, every wave writes its part, the owner wave (block
-  // number % 4) adds the four in wave order and stores.
+  // number % 4) adds the four in wave order, scales (apply_alpha) and stores.
   const bool n_vec = (p.N & 3) == 0;
-  const float alpha = gemm_alpha(p);
+  const Alpha alpha = gemm_alpha(p);
 #pragma unroll
   for (int i = 0; i < A; ++i)
 #pragma unroll
@@ -998,7 +1002,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
               float s = rb[v * 64 + lane];
 #pragma unroll
               for (int w = 1; w < NW; ++w) s += rb[(w * 16 + v) * 64 + lane];
-              b[e] = bf16_rne(s * alpha);
+              b[e] = bf16_rne(apply_alpha<kExp>(s, alpha));
             }
             if (n_vec && n + 3 < p.N) {
               *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
@@ -1013,14 +1017,25 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
     }
 }
 
+// Device-resident global scales (whose product the launch cannot see) and host pairs
+// whose product is not a normal fp32 run the tiled kernels' ldexp epilogue (apply_alpha).
+bool alpha_needs_exp(const GemmProblem& p) { return p.a_gs_dev != nullptr || p.alpha_exp != 0; }
+
 template <int BM, int BN, int KC, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool fast) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (fast)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)tiles);
+  const bool ext = alpha_needs_exp(p);
+  if (fast && ext)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, true>), grid, dim3(256), 0, stream, p);
+  else if (fast)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, false>), grid, dim3(256), 0, stream, p);
+  else if (ext)
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, WM, WN, true, false, true>), grid,
+                       dim3(64 * WM * WN), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, WM, WN, true, false>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, KC, WM, WN, true, false, false>), grid,
                        dim3(64 * WM * WN), 0, stream, p);
   return hipGetLastError();
 }
@@ -1081,6 +1096,17 @@ SplitShape splitk_shape(int64_t M) {
   return {1, 4};
 }
 
+template <int A, int B, int DG, int NW, bool kFuse, bool kVecScale>
+void launch_splitk_kernel(dim3 grid, dim3 block, hipStream_t stream, const GemmProblem& p,
+                          const FusedQuant& fq) {
+  if (alpha_needs_exp(p))
+    hipLaunchKernelGGL((gemm_splitk_kernel<A, B, DG, NW, kFuse, kVecScale, true>), grid, block, 0,
+                       stream, p, fq);
+  else
+    hipLaunchKernelGGL((gemm_splitk_kernel<A, B, DG, NW, kFuse, kVecScale, false>), grid, block, 0,
+                       stream, p, fq);
+}
+
 hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s) {
   const int64_t wgs = ((p.N + 32 * s.a - 1) / (32 * s.a)) * ((p.M + 32 * s.b - 1) / (32 * s.b));
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1091,13 +1117,13 @@ hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s)
   // groups in flight per wave by workgroup shape (registers: about 40 VGPRs per group
   // and activation group); measured: deeper rings gain nothing
   if (p.K % 64 == 0) {
-    if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, NW, false, true>), grid, block, 0, stream, p, none);
-    else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 3, NW, false, true>), grid, block, 0, stream, p, none);
-    else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 2, NW, false, true>), grid, block, 0, stream, p, none);
+    if (s.b == 1) launch_splitk_kernel<1, 1, 4, NW, false, true>(grid, block, stream, p, none);
+    else if (s.b == 2) launch_splitk_kernel<1, 2, 3, NW, false, true>(grid, block, stream, p, none);
+    else launch_splitk_kernel<1, 4, 2, NW, false, true>(grid, block, stream, p, none);
   } else {
-    if (s.b == 1) hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, NW, false, false>), grid, block, 0, stream, p, none);
-    else if (s.b == 2) hipLaunchKernelGGL((gemm_splitk_kernel<1, 2, 3, NW, false, false>), grid, block, 0, stream, p, none);
-    else hipLaunchKernelGGL((gemm_splitk_kernel<1, 4, 2, NW, false, false>), grid, block, 0, stream, p, none);
+    if (s.b == 1) launch_splitk_kernel<1, 1, 4, NW, false, false>(grid, block, stream, p, none);
+    else if (s.b == 2) launch_splitk_kernel<1, 2, 3, NW, false, false>(grid, block, stream, p, none);
+    else launch_splitk_kernel<1, 4, 2, NW, false, false>(grid, block, stream, p, none);
   }
   return hipGetLastError();
 }
@@ -1169,25 +1195,45 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
     case NVFP4_GEMM_FIT: {
       const int64_t tfit = ((p.M + kFitBM - 1) / kFitBM) * ((p.N + kFitBN - 1) / kFitBN);
       if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_fit_kernel<kFitBM, kFitBN>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
+      if (alpha_needs_exp(p))
+        hipLaunchKernelGGL((gemm_fit_kernel<kFitBM, kFitBN, true>), dim3((unsigned)tfit), dim3(256),
+                           0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_fit_kernel<kFitBM, kFitBN, false>), dim3((unsigned)tfit), dim3(256),
+                           0, stream, p);
       return hipGetLastError();
     }
     case NVFP4_GEMM_TILE128: {
       const int64_t t = ((p.M + 127) / 128) * ((p.N + 191) / 192);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_dma_kernel<128, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      if (alpha_needs_exp(p))
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 192, true>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 192, false>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
       return hipGetLastError();
     }
     case NVFP4_GEMM_TILE128X128: {
       const int64_t t = ((p.M + 127) / 128) * ((p.N + 127) / 128);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_dma_kernel<128, 128>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      if (alpha_needs_exp(p))
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, true>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, false>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
       return hipGetLastError();
     }
     case NVFP4_GEMM_TILE128X64: {
       const int64_t t = ((p.M + 127) / 128) * ((p.N + 63) / 64);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_dma_kernel<128, 64>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      if (alpha_needs_exp(p))
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 64, true>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 64, false>), dim3((unsigned)t), dim3(256), 0,
+                           stream, p);
       return hipGetLastError();
     }
     default:
@@ -1207,11 +1253,9 @@ hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipSt
   const int64_t wgs = (p.N + 31) / 32;
   if (p.M > 32 || p.M * p.K > kFuseElems || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.K % 64 == 0)
-    hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, 4, true, true>), dim3((unsigned)wgs), dim3(256), 0,
-                       stream, p, fq);
+    launch_splitk_kernel<1, 1, 4, 4, true, true>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
   else
-    hipLaunchKernelGGL((gemm_splitk_kernel<1, 1, 4, 4, true, false>), dim3((unsigned)wgs), dim3(256), 0,
-                       stream, p, fq);
+    launch_splitk_kernel<1, 1, 4, 4, true, false>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
   return hipGetLastError();
 }
 

@@ -73,25 +73,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
 
-// Epilogue shared by the GEMM kernels: lane holds, for weight group i and activation
-// group g, output row m = m_base + 32g + (lane % 32) and columns
-// n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is scaled by
-// alpha in fp32, rounded to nearest even bf16 and stored (8 bytes per lane when the row
-// pitch allows). Only column quads q in [q0, q1) are stored.
-// The epilogue scale: RN(a_global * w_global), from the launch arguments or, when the
-// global scales are device-resident, from device memory.
-__device__ __forceinline__ float gemm_alpha(const GemmProblem& p) {
-  return p.a_gs_dev != nullptr ? (*p.a_gs_dev) * (*p.w_gs_dev) : p.alpha;
+// The epilogue scale a_global * w_global (split as in split_alpha), from the launch
+// arguments or, when the global scales are device-resident, from device memory (each
+// value clamped as the quantizer clamps it, so a linear layer's two kernels agree).
+__device__ __forceinline__ Alpha gemm_alpha(const GemmProblem& p) {
+  if (p.a_gs_dev != nullptr)
+    return split_alpha(clamp_global_scale(*p.a_gs_dev), clamp_global_scale(*p.w_gs_dev));
+  return Alpha{p.alpha, p.alpha_exp};
+}
+// acc * a_global * w_global in fp32. With kExp = false (launches whose host scales
+// multiply to a normal fp32, alpha.e == 0): one multiply and one rounding per element.
+// With kExp = true (other host pairs, and device-resident scales, whose product the
+// launch cannot see): the multiply by m, then 2^e by ldexp, which rounds a second time
+// only where it takes a result below the normal range. The launchers pick the kernel
+// instantiation, so the common epilogue keeps its single multiply (an ldexp per element
+// costs 0.7% on the 4608 x 3072 x 3072 product).
+template <bool kExp>
+__device__ __forceinline__ float apply_alpha(float acc, const Alpha& al) {
+  if constexpr (kExp) return __builtin_ldexpf(acc * al.m, al.e);
+  else return acc * al.m;
 }
 
-template <int FM, int FN>
+// Epilogue shared by the GEMM kernels: lane holds, for weight group i and activation
+// group g, output row m = m_base + 32g + (lane % 32) and columns
+// n_base + 32i + 8q + 4(lane / 32) + {0..3} in acc[i][g][4q..4q+3]; each is multiplied
+// by alpha (apply_alpha) in fp32, rounded to nearest even bf16 and stored (8 bytes per
+// lane when the row pitch allows). Only column quads q in [q0, q1) are stored.
+template <int FM, int FN, bool kExp = false>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
-                                           int64_t m_base, int64_t n_base, int lane, int q0 = 0,
-                                           int q1 = 4) {
+                                           const Alpha alpha, int64_t m_base, int64_t n_base,
+                                           int lane, int q0 = 0, int q1 = 4) {
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 3) == 0;
-  const float alpha = gemm_alpha(p);
 #pragma unroll
   for (int g = 0; g < FM; ++g) {
     const int64_t m = m_base + g * 32 + r32;
@@ -105,7 +119,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
         const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
         uint32_t b[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(acc[i][g][4 * q + e] * alpha);
+        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(apply_alpha<kExp>(acc[i][g][4 * q + e], alpha));
         if (n_vec && n + 3 < p.N) {
           *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
         } else {
@@ -135,17 +149,16 @@ constexpr int kStoreRowPad(int fn) { return fn * 32 + 8; }
 // kRowCol: instead of the scalar alpha, each output (m, n) is scaled by a_scales[m] *
 // w_scales[n], read as fp32 arrays [M] and [N] (rowwise-scaled products); entries past M
 // or N read as zero through range-checked buffer loads.
-template <int FM, int FN, bool kRowCol = false>
+template <int FM, int FN, bool kRowCol = false, bool kExp = false>
 __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], const GemmProblem& p,
-                                               int64_t m_base, int64_t n_base, int lane,
-                                               uint16_t* blk) {
+                                               const Alpha alpha, int64_t m_base, int64_t n_base,
+                                               int lane, uint16_t* blk) {
   constexpr int W = FN * 32;            // columns of the wave's blocks
   constexpr int RS = kStoreRowPad(FN);  // row stride in the staging area
   constexpr int kPieces = 32 * W / 8;   // 16-byte pieces per 32-row group
   const int h = lane >> 5;
   const int r32 = lane & 31;
   const bool n_vec = (p.N & 7) == 0;  // 16-byte aligned row pieces
-  const float alpha = kRowCol ? 1.0f : gemm_alpha(p);
   float sx[FM];
   u32x4 sw[FN][4];
   if constexpr (kRowCol) {
@@ -173,7 +186,7 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (kRowCol) b[e] = bf16_rne(acc[i][g][4 * q + e] * sx[g] * u2f(sw[i][q][e]));
-          else b[e] = bf16_rne(acc[i][g][4 * q + e] * alpha);
+          else b[e] = bf16_rne(apply_alpha<kExp>(acc[i][g][4 * q + e], alpha));
         }
         *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
       }

@@ -331,7 +331,8 @@ __global__ void __launch_bounds__(256) gemm_w4a16_tile_kernel(W4A16Problem p) {
   q.K = p.K;
   q.alpha = p.alpha;
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
-  store_tile_lds<FM, FN>(acc, q, (int64_t)m0 + wave_m * FM * 32, (int64_t)n0 + wave_n * FN * 32, lane,
+  store_tile_lds<FM, FN>(acc, q, Alpha{q.alpha, 0}, (int64_t)m0 + wave_m * FM * 32,
+                         (int64_t)n0 + wave_n * FN * 32, lane,
                          (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
@@ -501,13 +502,14 @@ __global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
   uint16_t* stage_area = (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN);
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
-  store_tile_lds<FM, FN>(acc, q, (int64_t)m0 + xg0 * 32, n_base, lane, stage_area);
-  if (wave_m == 0)
-    store_tile_lds<1, 2>(*(const floatx16(*)[2][1])&accm, q, (int64_t)m0 + GS * 32, n_base, lane,
+  store_tile_lds<FM, FN>(acc, q, Alpha{q.alpha, 0}, (int64_t)m0 + xg0 * 32, n_base, lane,
                          stage_area);
+  if (wave_m == 0)
+    store_tile_lds<1, 2>(*(const floatx16(*)[2][1])&accm, q, Alpha{q.alpha, 0},
+                         (int64_t)m0 + GS * 32, n_base, lane, stage_area);
   else
-    store_tile_lds<1, 1>(*(const floatx16(*)[1][1])&accm[0], q, (int64_t)m0 + GS * 32, n_base + 64,
-                         lane, stage_area);
+    store_tile_lds<1, 1>(*(const floatx16(*)[1][1])&accm[0], q, Alpha{q.alpha, 0},
+                         (int64_t)m0 + GS * 32, n_base + 64, lane, stage_area);
 }
 
 }  // namespace

@@ -18,6 +18,25 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
                            void* scales, hipStream_t stream, const LaunchInfo& dev,
                            const float* gs_dev = nullptr);
 
+// The epilogue scale a_global * w_global as m * 2^e. When RN(a_global * w_global) is a
+// normal binary32 (every realistic pair) m is that product and e = 0. Global scales in
+// [2^-90, 2^90] can also multiply to anything in [2^-180, 2^180], where a single fp32
+// alpha would be subnormal (precision lost) or infinite; then m is the rounded product of
+// the two frexp mantissas, in [0.25, 1), e the sum of their exponents, and the epilogue
+// applies 2^e with ldexp after the multiply by m.
+struct Alpha {
+  float m;
+  int e;
+};
+__host__ __device__ inline Alpha split_alpha(float a, float w) {
+  const float prod = a * w;
+  if (prod >= 0x1p-126f && prod <= 0x1.fffffep127f) return Alpha{prod, 0};
+  int ea = 0, ew = 0;
+  const float ma = frexpf(a, &ea);
+  const float mw = frexpf(w, &ew);
+  return Alpha{ma * mw, ea + ew};
+}
+
 struct GemmProblem {
   const uint8_t* a_packed;
   const uint8_t* a_scales;
@@ -25,11 +44,13 @@ struct GemmProblem {
   const uint8_t* w_scales;
   uint16_t* out;
   int64_t M, N, K;
-  float alpha;  // RN(a_global * w_global)
-  // Device-resident global scales (both set, or both null): alpha is then
-  // RN(*a_gs_dev * *w_gs_dev), read by the kernel.
+  float alpha;  // split_alpha(a_global, w_global): alpha * 2^alpha_exp
+  // Device-resident global scales (both set, or both null): the kernel then reads both,
+  // clamps each as the quantizer clamps a device-resident scale, and splits their product
+  // with split_alpha; alpha and alpha_exp are unused.
   const float* a_gs_dev;
   const float* w_gs_dev;
+  int alpha_exp = 0;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev);

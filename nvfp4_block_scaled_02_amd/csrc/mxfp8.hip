@@ -313,8 +313,9 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
-  store_tile_lds<FM, FN, kRowwise>(acc, p, (int64_t)m0 + wave_m * WTM, (int64_t)n0 + wave_n * WTN,
-                                   lane, (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+  store_tile_lds<FM, FN, kRowwise>(acc, p, Alpha{p.alpha, 0}, (int64_t)m0 + wave_m * WTM,
+                                   (int64_t)n0 + wave_n * WTN, lane,
+                                   (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 // ---- GEMM, 288 x 192 tiles ---------------------------------------------------------------
@@ -503,9 +504,10 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   uint16_t* blk = (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN);
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
   const int64_t n_base = (int64_t)n0 + wave_n * FN * 32;
-  store_tile_lds<FM, FN, kRowwise>(acc, p, (int64_t)m0 + xg0 * 32, n_base, lane, blk);
-  store_tile_lds<1, kS, kRowwise>(*(const floatx16(*)[kS][1])&accs, p, (int64_t)m0 + GS * 32,
-                                  n_base + kI0 * 32, lane, blk);
+  store_tile_lds<FM, FN, kRowwise>(acc, p, Alpha{p.alpha, 0}, (int64_t)m0 + xg0 * 32, n_base,
+                                   lane, blk);
+  store_tile_lds<1, kS, kRowwise>(*(const floatx16(*)[kS][1])&accs, p, Alpha{p.alpha, 0},
+                                  (int64_t)m0 + GS * 32, n_base + kI0 * 32, lane, blk);
 }
 
 template <int BM, int BN, bool kRowwise>

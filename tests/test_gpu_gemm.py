@@ -118,6 +118,50 @@ def test_gemm_exact_cases():
     assert np.all((to_host(out) & 0x7FFF) == 0)
 
 
+# Global-scale pairs whose fp32 product leaves the normal binary32 range (each scale is
+# valid: in [2^-90, 2^90]). A single fp32 alpha would be subnormal (2 significant bits
+# left, 9% off), zero or infinite; the library applies the power of two exactly. Each pair comes
+# with block-scale codes that put the outputs in bf16's range: E4M3 0x70..0x7E (128..448)
+# for the tiny products, 0x01..0x02 (2^-9, 2^-8) for the huge one.
+_EXTREME_PAIRS = [
+    (np.float32(1.37 * 2.0**-80), np.float32(2.0**-68), range(0x70, 0x7F)),  # 1.37 * 2^-148
+    (np.float32(2.0**-90), np.float32(2.0**-60), range(0x70, 0x7F)),         # 2^-150
+    (np.float32(2.0**90), np.float32(1.25 * 2.0**40), range(0x01, 0x03)),    # 1.25 * 2^130
+]
+
+
+@pytest.mark.parametrize("pair", range(len(_EXTREME_PAIRS)))
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (64, 128, 128, "splitk"), (600, 700, 256, "tile128x64"), (1500, 2500, 128, "tile128x128"),
+    (2600, 1650, 384, "tile128"), (2600, 3000, 128, "fit"), (4096, 4096, 128, "tile256"),
+    (600, 700, 208, "generic"),
+])
+def test_gemm_extreme_global_scale_pairs(M, N, K, kernel, pair):
+    """Every kernel's epilogue against the oracle (whose a_gs * w_gs is exact in float64)
+    for scale pairs whose product is not a normal fp32, with random code bytes; the same
+    values passed as device-resident scales give the same bits."""
+    assert nv.gemm_plan(M, N, K) == kernel
+    ags, wgs, codes = _EXTREME_PAIRS[pair]
+    rng = np.random.default_rng(M + N + K + 1000 * pair)
+    codes = np.asarray(list(codes), np.uint8)
+    ap = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    as_ = rng.choice(codes, (M, K // 16))
+    ws = rng.choice(codes, (N, K // 16))
+    say("gemm extreme scales", kernel, M, N, K, float(ags), float(wgs))
+    out, ok = _gemm_dev(ap, as_, ags, wp, ws, wgs)
+    got = to_host(out)
+    assert ok(), "write outside out"
+    ref, absref = O.gemm_ref(ap, as_, ags, wp, ws, wgs)
+    assert np.isfinite(ref).all() and np.abs(ref).max() < 2.0**127
+    assert np.abs(ref).max() > 2.0**-128            # outputs far above bf16's 2^-133 ulp
+    good, worst, nbad = O.check_gemm(got, ref, absref)
+    assert good, f"{kernel} {M}x{N}x{K}: {nbad} out of tolerance (worst err/tol {worst:.3g})"
+    dev = lambda v: torch.tensor([float(v)], dtype=torch.float32, device="cuda")
+    o2 = nv.gemm(u8_to_dev(ap), u8_to_dev(as_), dev(ags), u8_to_dev(wp), u8_to_dev(ws), dev(wgs))
+    assert np.array_equal(to_host(o2), got)
+
+
 def _sample_rows(M, rng, n=48):
     rows = {0, M - 1, M // 2}
     rows |= set(rng.choice(M, size=min(n, M), replace=False).tolist())
