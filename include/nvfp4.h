@@ -197,7 +197,11 @@ int nvfp4_mxfp8_gemm(const void* a_codes, const void* a_scales, const void* w_co
  *   - layouts: codes uint8 [rows, K] row-major, scales fp32 [rows];
  *   - GEMM: out = bf16_RNE(s_a[m] * s_w[n] * sum_k e4m3(a[m,k]) e4m3(w[n,k])); any result
  *     within 2^-10 * sum_k |a_k w_k| + 1 bf16 ulp of the exact value is correct and the
- *     library's result is deterministic for a given shape.
+ *     library's result is deterministic for a given shape. The epilogue evaluates
+ *     RN(RN(sum * s_a[m]) * s_w[n]) in fp32, so the bound assumes the intermediate
+ *     sum * s_a[m] stays inside fp32's normal range: an activation row with amax above
+ *     about 2^99 can overflow it, and a row of bf16 subnormals paired with a weight row
+ *     above about 2^20 can lose precision in it.
  *
  * nvfp4_fp8r_quantize: x_bf16 [M, K] (16-byte aligned) -> codes uint8 [M, K] (16-byte
  * aligned) and scales fp32 [M] (4-byte aligned). K >= 16, K % 16 == 0. Bit-exact to the
