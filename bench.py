@@ -55,7 +55,8 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "quantize.hip", "quant_common.hpp", "codec.hpp"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "kernels.hpp", "quantize.hip", "quant_common.hpp",
+                  "codec.hpp"]
 PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA
 
 
