@@ -210,6 +210,36 @@ def test_linear_matches_quantize_then_gemm(name):
     _assert_close(got[rows], ap[rows], as_[rows], ags, wp, ws, wgs, name)
 
 
+@pytest.mark.parametrize("M,N,K,plan", [(1, 640, 256, "fused"), (17, 3072, 1024, "two_kernels"),
+                                         (600, 700, 256, "two_kernels")])
+def test_linear_calibrated_scales_with_subnormal_product(M, N, K, plan):
+    """nvfp4_linear on tensors of magnitude 2^-70 and 2^-60 (all positive, so the sums do
+    not cancel): their calibrated global scales multiply to about 2^-149, below fp32's
+    normal range, while the outputs (about 2^-122) are normal bf16. Workspace bit-exact,
+    output within tolerance, and equal to quantize-then-GEMM."""
+    assert nv.linear_plan(M, N, K) == plan
+    rng = np.random.default_rng(M + N + K)
+    x = to_bf16_bits((np.abs(rng.standard_normal((M, K))) * 2.0**-70).astype(np.float32))
+    w = to_bf16_bits((np.abs(rng.standard_normal((N, K))) * 2.0**-60).astype(np.float32))
+    ags, wgs = O.global_scale(x), O.global_scale(w)
+    assert float(np.float32(ags) * np.float32(wgs)) < 2.0**-126
+    wp, ws = O.quantize(w, wgs)
+    work = torch.empty(nv.linear_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    say("linear subnormal scale product", M, N, K)
+    out = nv.linear(bf16_to_dev(x), float(ags), u8_to_dev(wp), u8_to_dev(ws), float(wgs),
+                    workspace=work)
+    got = to_host(out)
+    qp, qs = nv.workspace_views(work, M, K)
+    ap, as_ = O.quantize(x, ags)
+    assert np.array_equal(to_host(qp), ap) and np.array_equal(to_host(qs), as_)
+    ref, absref = O.gemm_ref(ap, as_, ags, wp, ws, wgs)
+    assert np.abs(ref).min() > 2.0**-126
+    good, worst, nbad = O.check_gemm(got, ref, absref)
+    assert good, f"{nbad} out of tolerance (worst err/tol {worst:.3g})"
+    g2, _ = _gemm_dev(ap, as_, ags, wp, ws, wgs, guard=False)
+    assert np.array_equal(to_host(g2), got)
+
+
 def test_operands_beyond_32bit_offsets():
     """Largest-size case: 4 194 081 activation rows x K = 1024, so the packed activations
     (2.1 GB) pass 2^31 bytes and the bf16 input (8.6 GB) passes 2^32; the planner sends
