@@ -98,6 +98,12 @@ def test_gemm_validation(lib):
     assert call({1: ctypes.c_void_p(0x20001)}) == L.MISALIGNED
     assert call({6: 0}) == L.SUCCESS
     assert call({7: 0}) == L.SUCCESS
+    # every pair of valid global scales is accepted, also where their fp32 product is
+    # subnormal, zero or infinite (the epilogue applies it as m * 2^e); validation runs
+    # before the empty-problem return
+    for a_gs, w_gs in ((2.0**-90, 2.0**-90), (2.0**90, 2.0**90), (2.0**-80, 2.0**-70)):
+        assert call({2: a_gs, 5: w_gs, 6: 0}) == L.SUCCESS
+    assert call({2: 2.0**-91, 6: 0}) == L.INVALID_VALUE
 
 
 def test_gemm_plan_routes_shapes(lib):
