@@ -88,6 +88,29 @@ def test_gemm_devgs_equals_gemm(M, N, K):
     assert np.array_equal(to_host(o1), to_host(o2))
 
 
+@pytest.mark.parametrize("a_dev,w_dev,a_host,w_host", [
+    (2.0**100, 2.0**-100, 2.0**90, 2.0**-90),      # clamped into [2^-90, 2^90]
+    (float("nan"), 0.5, 1.0, 0.5), (-3.0, 0.0, 1.0, 1.0),
+])
+@pytest.mark.parametrize("M,N,K", [(2600, 1650, 128), (17, 3072, 256)])
+def test_gemm_devgs_reads_scales_as_the_quantizer_does(M, N, K, a_dev, w_dev, a_host, w_host):
+    """Device-resident GEMM scales outside [2^-90, 2^90] are clamped into it, NaN and
+    values <= 0 read as 1.0 (as nvfp4_quantize_devgs reads its scale): the output equals
+    nvfp4_gemm with the values so read, bit for bit."""
+    rng = np.random.default_rng(M + K)
+    codes = np.arange(0x30, 0x48, dtype=np.uint8)
+    ap = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    as_ = rng.choice(codes, (M, K // 16))
+    ws = rng.choice(codes, (N, K // 16))
+    say("gemm_devgs clamp", nv.gemm_plan(M, N, K), M, N, K, a_dev, w_dev)
+    args = (u8_to_dev(ap), u8_to_dev(as_))
+    wargs = (u8_to_dev(wp), u8_to_dev(ws))
+    o1 = nv.gemm(*args, _dev_scalar(a_dev), *wargs, _dev_scalar(w_dev))
+    o2 = nv.gemm(*args, a_host, *wargs, w_host)
+    assert np.array_equal(to_host(o1), to_host(o2))
+
+
 def test_linear_devgs_end_to_end():
     """Calibrate on the device, then the fused linear with both scales device-resident:
     identical to the host-scale linear, and within the GEMM bound of the oracle."""
