@@ -63,7 +63,12 @@ extern "C" {
 typedef enum nvfp4_status {
   NVFP4_SUCCESS = 0,                  /* also returned for an empty problem (M == 0 or N == 0) */
   NVFP4_ERROR_INVALID_VALUE = 1,      /* null pointer; global scale not finite, <= 0, or
-                                         outside [2^-90, 2^90] */
+                                         outside [2^-90, 2^90]. The range is a restriction
+                                         of this library beyond "finite and > 0": inside it
+                                         the quantizer's reciprocal-plus-correction
+                                         divisions are exact (their residuals never
+                                         underflow); any bf16 tensor with amax in
+                                         [2^-78, 2^101] calibrates into it */
   NVFP4_ERROR_INVALID_SHAPE = 2,      /* negative size, K < 16, K % 16 != 0, size overflow */
   NVFP4_ERROR_MISALIGNED = 3,         /* x, packed, out or workspace not 16-byte aligned;
                                          scales not 4-byte aligned */
@@ -72,7 +77,13 @@ typedef enum nvfp4_status {
   NVFP4_ERROR_HIP = 6                 /* a HIP call failed; see nvfp4_last_hip_error() */
 } nvfp4_status;
 
-/* Version of this ABI (NVFP4_ABI_VERSION). A binding must refuse a mismatch. */
+/*
+ * Version of this ABI (NVFP4_ABI_VERSION). A binding must refuse a mismatch, as the pages'
+ * FP4 kernel package refuses to import when its two parts differ in version ("BFL (fp8r /
+ * nvfp4)", paragraph under the Kernels table: the Python and the prebuilt-kernel packages
+ * have to be installed at the same version). The Python binding of this library checks it
+ * on load and raises on a mismatch.
+ */
 int nvfp4_abi_version(void);
 
 /* Static string naming a status code (never NULL). */
@@ -101,7 +112,7 @@ int nvfp4_quantize(const void* x_bf16, int64_t M, int64_t K, float global_scale,
  * Kernels table, nvfp4 row): out[M, N] = a_global * w_global * A_hat[M, K] W_hat[N, K]^T.
  *   a_packed, a_scales  device, activations in NVFP4 layout [M, K/2], [M, K/16]
  *   w_packed, w_scales  device, weights in NVFP4 layout [N, K/2], [N, K/16]
- *   a_global_scale, w_global_scale  fp32, finite, > 0
+ *   a_global_scale, w_global_scale  fp32, finite, in [2^-90, 2^90]
  *   out_bf16            device, bf16 [M, N], 16-byte aligned, written
  * Packed operands must be 16-byte aligned, scales 4-byte aligned.
  */

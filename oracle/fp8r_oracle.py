@@ -106,8 +106,3 @@ def gemm_ref(a_codes, a_scales, w_codes, w_scales, *, with_abs: bool = True):
         absref = (np.abs(qa) @ np.abs(qw).T) * np.abs(sa)[:, None] * np.abs(sw)[None, :]
     return ref, absref
 
-
-def bytes_per_element(K: int) -> float:
-    """Stored bytes per element of a rowwise FP8 tensor: one code byte plus a 4-byte
-    scale per row of K elements."""
-    return 1.0 + 4.0 / K

@@ -118,7 +118,3 @@ def gemm_ref(a_codes, a_scales, w_codes, w_scales, *, with_abs: bool = True):
     absref = np.abs(A) @ np.abs(W).T if with_abs else None
     return ref, absref
 
-
-def bytes_per_element() -> float:
-    """Stored bytes per element of an MXFP8 tensor: one code byte plus 1/32 scale byte."""
-    return 1.0 + 1.0 / BLOCK

@@ -318,13 +318,6 @@ def check_gemm(out_bf16_bits: np.ndarray, ref: np.ndarray, absref: np.ndarray):
     return (not bool(bad.any())), worst, int(bad.sum())
 
 
-def linear_ref(x_bits, a_gs, w_packed, w_scales, w_gs):
-    """Fused path reference: quantize x under ``a_gs`` (R1), then :func:`gemm_ref`."""
-    ap, as_ = quantize(x_bits, a_gs)
-    ref, absref = gemm_ref(ap, as_, a_gs, w_packed, w_scales, w_gs)
-    return (ap, as_), ref, absref
-
-
 def w4a16_ref(x_bits, w_packed, w_scales, w_gs, *, with_abs: bool = True):
     """Dequantise-only product (bf16 activations kept unquantised), float64.
 
