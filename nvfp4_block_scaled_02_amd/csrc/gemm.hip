@@ -287,13 +287,14 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
 //
 // 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
 // 2 x 3 for 128 x 192, 2 x 2 for 128 x 128 and 2 x 1 for 128 x 64 (medium M: more tiles,
-// so fewer rows still fill the chip, at a higher decode cost per MFMA). Loads, LDS image and stage pipeline
-// are the fit kernel's (below): code loads of 16 rows x the stage's 64 bytes (4 lanes per
-// row) into 1 KiB pieces whose 16-byte chunks are swizzled by chunk_swz, scale loads of
-// 64 rows x 16 bytes (a pair of stages) into three pair buffers, four code buffers filled
-// three stages ahead, one wait and barrier per stage; range-checked buffer loads, so a
-// ragged tile needs no clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS at 256 x 256,
-// 4 x 20 KiB + 3 x 5 KiB = 95 KiB at 128 x 192.
+// so fewer rows still fill the chip, at a higher decode cost per MFMA). Loads, LDS image
+// and stage pipeline are the fit kernel's (below): code loads of 16 rows x the stage's
+// 64 bytes (4 lanes per row) into 1 KiB pieces whose 16-byte chunks are swizzled by
+// chunk_swz, scale loads of 64 rows x 16 bytes (a pair of stages) into three pair
+// buffers, four code buffers filled three stages ahead, one wait and barrier per stage;
+// range-checked buffer loads over row windows (window_rsrc), so a ragged tile needs no
+// clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS at 256 x 256, 4 x 20 KiB + 3 x 5 KiB
+// = 95 KiB at 128 x 192.
 template <int BM, int BN>
 struct alignas(16) GemmSmem256 {
   uint8_t x[4][BM * 64];
@@ -338,31 +339,30 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
-  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
-  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int lr = lane >> 2;
-  const uint32_t voff_p = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
-  const uint32_t voff_s = lane * spitch;
+  // row windows [m0, M) and [n0, N) (see window_rsrc)
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   // scale piece half * NW + wave of a pair (slots past the last piece repeat it, writing
   // the same bytes to the same place)
   auto issue_scale = [&](int pair, int half, int sb) {
     const int i = min(half * NW + wave, kSp - 1);
     const bool isx = i < kSx;
-    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
-    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024], voff_s, row * spitch + (uint32_t)pair * 16);
+    const int prow = isx ? 64 * i : 64 * (i - kSx);
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024],
+                      scale_piece_voff(lane, prow, spitch, (uint32_t)pair * 16), 0);
   };
   auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
     if (j < kPaW) {
       const int i = j * NW + wave;
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_p,
-                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else if (j < kPaW + kPwW) {
       const int i = (j - kPaW) * NW + wave;
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_p,
-                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else {
       issue_scale(spair, t & 1, sb);
     }
@@ -577,35 +577,33 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
-  // Buffer resources: the range check returns zeros for rows past M (or N), so a ragged
-  // last tile needs no clamping.
-  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
-  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int lr = lane >> 2;  // row of a code piece this lane loads
-  const uint32_t voff_p = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
-  const uint32_t voff_s = lane * spitch;
+  // Buffer resources over the row windows [m0, M) and [n0, N): rows past M (or N) are
+  // out of range and read as zero, so a ragged last tile needs no clamping.
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   // Scale piece `half` * NW + wave of stage pair `pair` into pair buffer `sb`; pieces below
   // kSx hold activation rows, the rest weight rows (selects, no branch).
   auto issue_scale = [&](int pair, int half, int sb) {
     const int i = half * NW + wave;
     const bool isx = i < kSx;
-    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
-    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024], voff_s, row * spitch + (uint32_t)pair * 16);
+    const int prow = isx ? 64 * i : 64 * (i - kSx);
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024],
+                      scale_piece_voff(lane, prow, spitch, (uint32_t)pair * 16), 0);
   };
   // Load j of this wave in stage t: code pieces of stage `stage` into buffer `buf`, the
   // last one the stage's scale piece (pair `spair` into pair buffer `sb`).
   auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
     if (j < kPaW) {
       const int i = min(j * NW + wave, kPa - 1);
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_p,
-                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else if (j < kPaW + kPwW) {
       const int i = min((j - kPaW) * NW + wave, kPw - 1);
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_p,
-                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else {
       issue_scale(spair, t & 1, sb);
     }
@@ -819,12 +817,19 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
   const int ngt = (nchunks + 3) / 4;
   const int ngroups = (ngt - wave + NW - 1) / NW;  // this wave's groups
 
-  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
-  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const uint32_t voff_p = r32 * pitch + h * 16;
-  const uint32_t voff_s = r32 * spitch + h * 2;
+  // Row windows [m0, M) and [n0, N) (see window_rsrc). Every load's per-lane offset holds
+  // its row and its whole position along K: the upper lane half of a 32-element last
+  // chunk reads past its row, which for the operand's last row is past its end, so that
+  // position must be range-checked too. (The kFuse form reads no activations from memory
+  // and never uses rxp or rxs.)
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
+  // lane's row r32 of 32-row group i of a window, its half h of a chunk: codes at
+  // splitk_code_voff(i) + 32 c, two scale bytes at splitk_scale_voff(i) + 4 c
+  auto splitk_code_voff = [&](int i) { return (uint32_t)(32 * i + r32) * pitch + (uint32_t)h * 16; };
+  auto splitk_scale_voff = [&](int i) { return (uint32_t)(32 * i + r32) * spitch + (uint32_t)h * 2; };
 
   floatx16 acc[A][B];
 #pragma unroll
@@ -839,7 +844,6 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
   // lane's two bytes of chunk k in word k)
   u32x4 wraw[DG][4][A], xraw[DG][4][B];
   u32x4 wsv[DG][A], xsv[DG][B];
-  const uint32_t voff_sv = r32 * spitch;
   // group G of this wave (chunks 4 (NW G + wave) .. + 3) into ring slot s
   auto load_group = [&](int s, int G) {
     const int c0 = 4 * (NW * G + wave);
@@ -850,19 +854,19 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
 #pragma unroll
         for (int i = 0; i < A; ++i) {
           wraw[s][k][i] = __builtin_amdgcn_raw_buffer_load_b128(
-              rwp, (int)voff_p, (int)((uint32_t)(n0 + 32 * i) * pitch + (uint32_t)c * 32), 0);
+              rwp, (int)(splitk_code_voff(i) + (uint32_t)c * 32), 0, 0);
           if constexpr (!kVecScale)
             wsv[s][i][k] = __builtin_amdgcn_raw_buffer_load_b16(
-                rws, (int)voff_s, (int)((uint32_t)(n0 + 32 * i) * spitch + (uint32_t)c * 4), 0);
+                rws, (int)(splitk_scale_voff(i) + (uint32_t)c * 4), 0, 0);
         }
         if constexpr (!kFuse) {
 #pragma unroll
           for (int g = 0; g < B; ++g) {
             xraw[s][k][g] = __builtin_amdgcn_raw_buffer_load_b128(
-                rxp, (int)voff_p, (int)((uint32_t)(m0 + 32 * g) * pitch + (uint32_t)c * 32), 0);
+                rxp, (int)(splitk_code_voff(g) + (uint32_t)c * 32), 0, 0);
             if constexpr (!kVecScale)
               xsv[s][g][k] = __builtin_amdgcn_raw_buffer_load_b16(
-                  rxs, (int)voff_s, (int)((uint32_t)(m0 + 32 * g) * spitch + (uint32_t)c * 4), 0);
+                  rxs, (int)(splitk_scale_voff(g) + (uint32_t)c * 4), 0, 0);
           }
         }
       }
@@ -870,20 +874,20 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
     if constexpr (kVecScale) {
       // a whole group: its 16 scale bytes lie inside the row; a partial last group takes
       // 4 bytes per chunk instead (same layout), so no load reaches past the row's end
-      auto vec = [&](__amdgpu_buffer_rsrc_t r, int row0) -> u32x4 {
-        const uint32_t base = (uint32_t)row0 * spitch + (uint32_t)c0 * 4;
-        if (c0 + 4 <= nchunks) return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, (int)voff_sv, (int)base, 0);
+      auto vec = [&](__amdgpu_buffer_rsrc_t r, int grp) -> u32x4 {
+        const uint32_t voff = (uint32_t)(32 * grp + r32) * spitch + (uint32_t)c0 * 4;
+        if (c0 + 4 <= nchunks) return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
         u32x4 v{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (c0 + k < nchunks) v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff_sv, (int)(base + 4 * k), 0);
+          if (c0 + k < nchunks) v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * k), 0, 0);
         return v;
       };
 #pragma unroll
-      for (int i = 0; i < A; ++i) wsv[s][i] = vec(rws, n0 + 32 * i);
+      for (int i = 0; i < A; ++i) wsv[s][i] = vec(rws, i);
       if constexpr (!kFuse) {
 #pragma unroll
-        for (int g = 0; g < B; ++g) xsv[s][g] = vec(rxs, m0 + 32 * g);
+        for (int g = 0; g < B; ++g) xsv[s][g] = vec(rxs, g);
       }
     }
   };

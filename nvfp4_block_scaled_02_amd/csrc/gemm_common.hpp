@@ -68,9 +68,70 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // Raw buffer resource over n bytes at p (gfx9-family descriptor word 3: 32-bit data
-// format, no swizzle); loads at offsets >= n return zero.
+// format, no swizzle). The hardware range check compares only the per-lane offset
+// (voffset plus the instruction's immediate) with n, dword by dword for multi-dword
+// loads; the scalar offset (soffset) is added to the address but is NOT checked. A
+// dword whose per-lane offset is >= n reads as zero and touches no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t n) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// ---- row windows: how every range-checked operand load finds its row ---------------------
+//
+// A kernel that reads rows past the end of an operand (the ragged last tile of a GEMM)
+// relies on the range check to turn those reads into zeros. Since only the per-lane
+// offset is checked, the row of every load must be in that offset: each operand gets a
+// resource based at the tile's first row row0 and covering rows [row0, rows), and a
+// load's per-lane offset is (row - row0) * pitch plus whatever part of its position
+// along K could leave the row; the scalar offset carries only a position along K that
+// keeps the whole load inside its row. Then a row past the operand's end is out of range
+// as a whole, and no in-range dword lies outside the operand.
+
+// Bytes of the window of rows [row0, rows) (row0 < rows); the shape checks of the entry
+// points keep (rows + one tile) * pitch below 2^31.
+NVFP4_HD uint32_t window_bytes(int64_t row0, int64_t rows, uint32_t pitch) {
+  return (uint32_t)((rows - row0) * (int64_t)pitch);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const void* base, int64_t row0,
+                                                              int64_t rows, uint32_t pitch) {
+  return make_rsrc((const uint8_t*)base + row0 * (int64_t)pitch, window_bytes(row0, rows, pitch));
+}
+
+// Chunk swizzle of a 64-byte LDS row by its index r (0..15) within a 1 KiB piece of 16
+// rows: the row's 16-byte chunk q is stored at slot q ^ chunk_swz(r). A lane (h, r) of an
+// MFMA fragment reads chunk h or h + 2 of row r; with this swizzle the 16-byte reads of
+// any 8 or 16 consecutive lanes fall in distinct LDS banks (32- or 64-bank view), and a
+// direct-to-LDS load whose lane l fetches chunk (l % 4) ^ chunk_swz(l / 4) of row l / 4
+// writes the piece in this order.
+NVFP4_HD int chunk_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
+
+// Per-lane offset of a 16-row code piece load (16 rows x 64 bytes, four lanes per row):
+// lane l reads row prow + l / 4 of the window, chunk (l % 4) ^ chunk_swz(l / 4) of the
+// 64-byte segment that the scalar offset selects (a stage's position along K, inside
+// the row).
+NVFP4_HD uint32_t code_piece_voff(int lane, int prow, uint32_t pitch) {
+  const int lr = lane >> 2;
+  return (uint32_t)(prow + lr) * pitch + 16u * (uint32_t)((lane & 3) ^ chunk_swz(lr));
+}
+
+// Per-lane offset of a 64-row scale piece load (16 bytes of each of 64 rows): lane l reads
+// row prow + l of the window at byte kbyte of the row. kbyte is part of the checked
+// offset because the last piece of a row can extend past the row's end (a partial last
+// group of stages): its dwords past the operand's end then read as zero.
+NVFP4_HD uint32_t scale_piece_voff(int lane, int prow, uint32_t spitch, uint32_t kbyte) {
+  return (uint32_t)(prow + lane) * spitch + kbyte;
+}
+
+// Swizzle of the W4A16 kernels' bf16 activation rows (128 bytes of a stage, eight 16-byte
+// chunks): chunk c of row r (r = row within its 32-row group) sits at slot c ^ x_swz(r).
+NVFP4_HD int x_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// Per-lane offset of a W4A16 activation piece load (8 rows x 128 bytes, eight lanes per
+// row): lane l reads row prow + l / 8 of the window, chunk (l % 8) ^ x_swz(row % 32) of
+// the stage's 128-byte segment (selected by the scalar offset).
+NVFP4_HD uint32_t x_piece_voff(int lane, int prow, uint32_t xpitch) {
+  const int xr = lane >> 3;
+  return (uint32_t)(prow + xr) * xpitch + 16u * (uint32_t)((lane & 7) ^ x_swz((prow + xr) & 31));
 }
 
 // The epilogue scale a_global * w_global (split as in split_alpha), from the launch
@@ -240,14 +301,6 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, void*
 // own L2, so workgroup b takes tile (b % 8) * (T / 8) + b / 8 of an order in which each
 // XCD's share is contiguous; that order walks groups of G tile rows column by column, so
 // an XCD's tiles share few activation and weight rows. (T % 8 != 0: plain order.)
-// Chunk swizzle of a 64-byte LDS row by its index r (0..15) within a 1 KiB piece of 16
-// rows: the row's 16-byte chunk q is stored at slot q ^ chunk_swz(r). A lane (h, r) of an
-// MFMA fragment reads chunk h or h + 2 of row r; with this swizzle the 16-byte reads of
-// any 8 or 16 consecutive lanes fall in distinct LDS banks (32- or 64-bank view), and a
-// direct-to-LDS load whose lane l fetches chunk (l % 4) ^ chunk_swz(l / 4) of row l / 4
-// writes the piece in this order.
-__device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
-
 __device__ __forceinline__ void tile_order(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int kXcd = 8, G = NVFP4_GEMM_XCD_GROUP;
   const int T = tiles_m * tiles_n;

@@ -85,6 +85,9 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x + m0 * p.K, clamp31((p.M - m0) * (int64_t)xpitch));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed + n0 * pitch, clamp31((p.N - n0) * (int64_t)pitch));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales + n0 * spitch, clamp31((p.N - n0) * (int64_t)spitch));
+  // Every load's per-lane offset holds its row within the window and its whole position
+  // along K (the upper lane half of a 32-element last chunk reads past its row, past the
+  // operand's end for the last row), so the range check covers both.
   const uint32_t voff_x = r32 * xpitch + h * 64;
   const uint32_t voff_w = r32 * pitch + h * 16;
   const uint32_t voff_s = r32 * spitch + h * 2;
@@ -99,14 +102,14 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
   uint32_t wsr[D];
   auto load = [&](int d, int q) {
     const uint32_t c = (uint32_t)(wave + NW * q);
-    wraw[d] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)voff_w, (int)(c * 32), 0);
-    wsr[d] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)voff_s, (int)(c * 4), 0);
+    wraw[d] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(voff_w + c * 32), 0, 0);
+    wsr[d] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(voff_s + c * 4), 0, 0);
 #pragma unroll
     for (int g = 0; g < B; ++g)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         xraw[d][g][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rx, (int)(voff_x + 16 * j), (int)((uint32_t)g * 32 * xpitch + c * 128), 0);
+            rx, (int)(voff_x + (uint32_t)g * 32 * xpitch + c * 128 + 16 * j), 0, 0);
   };
   auto compute = [&](int d, int q) {
     // upper lane half of a 32-element last chunk: no elements (its loads read the next
@@ -193,7 +196,6 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
 // end of stage t each wave waits for the loads it issued before stage t and the
 // workgroup meets at a barrier, so stage t+1 is complete when it starts. A stage reads
 // its fragments k-step by k-step, one k-step ahead of its MFMAs.
-__device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 template <int BM, int BN>
 struct alignas(16) W4A16Smem {
@@ -229,26 +231,23 @@ __global__ void __launch_bounds__(256) gemm_w4a16_tile_kernel(W4A16Problem p) {
   const int nk = (int)(p.K / 64);
   const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
 
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * xpitch);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int xr = lane >> 3;  // row (within 8) of an activation load
-  const uint32_t voff_w = r32 * pitch + h * 16;
-  const uint32_t voff_s = lane * spitch;
+  // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
+  const __amdgpu_buffer_rsrc_t rx = window_rsrc(p.x, m0, p.M, xpitch);
+  const __amdgpu_buffer_rsrc_t rw = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rs = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
   auto issue = [&](int j, int stage, int buf) {
     if (j < kPxW) {
       const int i = j * NW + wave;  // rows 8i .. 8i+7 of the tile
-      const int row = 8 * i + xr;
-      const uint32_t voff = xr * xpitch + 16 * ((lane & 7) ^ x_swz(row & 31));
-      buffer_load_lds16(rx, &sm.x[buf][i * 1024], voff, (uint32_t)(m0 + 8 * i) * xpitch + (uint32_t)stage * 128);
+      buffer_load_lds16(rx, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, xpitch), (uint32_t)stage * 128);
     } else if (j < kPxW + kPwW) {
-      const int i = (j - kPxW) * NW + wave;  // weight group i
-      buffer_load_lds16(rw, &sm.w[buf][i * 1024], voff_w, (uint32_t)(n0 + 32 * i) * pitch + (uint32_t)stage * 32);
+      const int i = (j - kPxW) * NW + wave;  // weight group i: lane (h, r) row 32i + r, half h
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], (uint32_t)(32 * i + r32) * pitch + h * 16u,
+                        (uint32_t)stage * 32);
     } else {
       const int i = (j - kPxW - kPwW) * NW + wave;  // weight rows 64i .. 64i+63
-      buffer_load_lds4(rs, &sm.ws[buf][i * 256], voff_s, (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)stage * 4);
+      buffer_load_lds4(rs, &sm.ws[buf][i * 256], (uint32_t)(64 * i + lane) * spitch, (uint32_t)stage * 4);
     }
   };
 
@@ -387,26 +386,23 @@ __global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
   const int nk = (int)(p.K / 64);
   const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
 
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)p.M * xpitch);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int xr = lane >> 3;  // row (within 8) of an activation load
-  const uint32_t voff_w = r32 * pitch + h * 16;
-  const uint32_t voff_s = lane * spitch;
+  // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
+  const __amdgpu_buffer_rsrc_t rx = window_rsrc(p.x, m0, p.M, xpitch);
+  const __amdgpu_buffer_rsrc_t rw = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rs = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
   auto issue = [&](int j, int stage, int buf) {
     if (j < kPxW) {
       const int i = min(j * NW + wave, kPx - 1);  // rows 8i .. 8i+7 of the tile
-      const int row = 8 * i + xr;
-      const uint32_t voff = xr * xpitch + 16 * ((lane & 7) ^ x_swz(row & 31));
-      buffer_load_lds16(rx, &sm.x[buf][i * 1024], voff, (uint32_t)(m0 + 8 * i) * xpitch + (uint32_t)stage * 128);
+      buffer_load_lds16(rx, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, xpitch), (uint32_t)stage * 128);
     } else if (j < kPxW + kPwW) {
       const int i = min((j - kPxW) * NW + wave, kPw - 1);  // weight group i
-      buffer_load_lds16(rw, &sm.w[buf][i * 1024], voff_w, (uint32_t)(n0 + 32 * i) * pitch + (uint32_t)stage * 32);
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], (uint32_t)(32 * i + r32) * pitch + h * 16u,
+                        (uint32_t)stage * 32);
     } else {
       const int i = min((j - kPxW - kPwW) * NW + wave, kPs - 1);  // weight rows 64i .. 64i+63
-      buffer_load_lds4(rs, &sm.ws[buf][i * 256], voff_s, (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)stage * 4);
+      buffer_load_lds4(rs, &sm.ws[buf][i * 256], (uint32_t)(64 * i + lane) * spitch, (uint32_t)stage * 4);
     }
   };
 

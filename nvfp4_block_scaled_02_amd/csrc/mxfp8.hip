@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
 // than by its bytes, so every load reads whole 64-byte row segments: a code load takes
 // 16 rows x the stage's 64 bytes (4 lanes per row), a scale load 64 rows x 16 bytes (the
 // scales of 512 elements, 8 stages), issued once every 8 stages. Rows past M or N read as
-// zero (buffer range checks).
+// zero (buffer range checks over row windows, window_rsrc).
 //
 // Stage (64 elements of K) layout in LDS: each 16-row piece is 1 KiB, row r's 64 bytes at
 // 64 r, its 16-byte chunk c stored at slot c ^ chunk_swz(r) so that the fragment reads (two
@@ -171,37 +171,36 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   const uint32_t pitch = (uint32_t)p.K;          // code bytes per row
   const uint32_t spitch = (uint32_t)(p.K >> 5);  // scale bytes per row
 
-  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
-  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int lr = lane >> 2;  // row of a code piece this lane loads
-  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
-  const uint32_t voff_s = lane * spitch;
+  // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   // Code load j of this wave for `stage` into buffer `buf`: piece j * NW + wave of the
   // list (x pieces, then w pieces).
   auto issue_codes = [&](int j, int stage, int buf) {
     if (j < kPaW) {
       const int i = j * NW + wave;
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_c,
-                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else {
       const int i = (j - kPaW) * NW + wave;
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_c,
-                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     }
   };
-  // Scale load j of this wave for stage group `grp` into scale buffer `sbuf`.
+  // Scale load j of this wave for stage group `grp` into scale buffer `sbuf` (a partial
+  // last group reads past the row's end: that position is range-checked too).
   auto issue_scales = [&](int j, int grp, int sbuf) {
     if (j < kSa / NW) {
       const int i = j * NW + wave;
-      buffer_load_lds16(rxs, &sm.xs[sbuf][i * 1024], voff_s,
-                        (uint32_t)(m0 + 64 * i) * spitch + (uint32_t)grp * 16);
+      buffer_load_lds16(rxs, &sm.xs[sbuf][i * 1024],
+                        scale_piece_voff(lane, 64 * i, spitch, (uint32_t)grp * 16), 0);
     } else {
       const int i = (j - kSa / NW) * NW + wave;
-      buffer_load_lds16(rws, &sm.ws[sbuf][i * 1024], voff_s,
-                        (uint32_t)(n0 + 64 * i) * spitch + (uint32_t)grp * 16);
+      buffer_load_lds16(rws, &sm.ws[sbuf][i * 1024],
+                        scale_piece_voff(lane, 64 * i, spitch, (uint32_t)grp * 16), 0);
     }
   };
 
@@ -368,23 +367,21 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   const uint32_t pitch = (uint32_t)p.K;
   const uint32_t spitch = (uint32_t)(p.K >> 5);
 
-  const __amdgpu_buffer_rsrc_t rxp = make_rsrc(p.a_packed, (uint32_t)p.M * pitch);
-  const __amdgpu_buffer_rsrc_t rwp = make_rsrc(p.w_packed, (uint32_t)p.N * pitch);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scales, (uint32_t)p.M * spitch);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales, (uint32_t)p.N * spitch);
-  const int lr = lane >> 2;
-  const uint32_t voff_c = lr * pitch + 16 * ((lane & 3) ^ chunk_swz(lr));
-  const uint32_t voff_s = lane * spitch;
+  // row windows [m0, M) and [n0, N) (see window_rsrc)
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
   auto issue_codes = [&](int j, int stage, int buf) {
     if (j < kPaW) {
       const int i = min(j * NW + wave, kPa - 1);
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], voff_c,
-                        (uint32_t)(m0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     } else {
       const int i = min((j - kPaW) * NW + wave, kPw - 1);
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], voff_c,
-                        (uint32_t)(n0 + 16 * i) * pitch + (uint32_t)stage * 64);
+      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
+                        (uint32_t)stage * 64);
     }
   };
   // scale piece j * NW + wave (64 rows x 16 bytes): activation rows first, then weight
@@ -392,8 +389,9 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   auto issue_scales = [&](int j, int grp, int sbuf) {
     const int i = j * NW + wave;
     const bool isx = i < kSx;
-    const uint32_t row = isx ? (uint32_t)(m0 + 64 * i) : (uint32_t)(n0 + 64 * (i - kSx));
-    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sbuf][i * 1024], voff_s, row * spitch + (uint32_t)grp * 16);
+    const int prow = isx ? 64 * i : 64 * (i - kSx);
+    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sbuf][i * 1024],
+                      scale_piece_voff(lane, prow, spitch, (uint32_t)grp * 16), 0);
   };
 
   floatx16 acc[FN][FM], accs[kS];
