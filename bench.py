@@ -2,16 +2,28 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input: run-time
 NVFP4 quantization of the bf16 activations under the calibrated input scale, then the
-block-scaled W4A4 GEMM with bf16 output (the fused linear). Weights are quantized
-offline and the global scales calibrated before the timed region, as a deployed layer
-does. Inputs are resident in HBM when timing starts.
+block-scaled W4A4 GEMM with bf16 output. Weights are quantized offline and the global
+scales calibrated before the timed region, as a deployed layer does. Inputs are resident
+in HBM when timing starts.
 
-Prints one JSON line (rank 0) with the step throughput in TFLOP/s (2*M*N*K per step),
-the dominant kernel's roofline (GEMM vs the f16 dense MFMA peak), the quantize kernel's
-HBM bandwidth on rotated buffers (for the workload's activation and for a large
-4608 x 12288 activation), context rows (the GEMM at every M = 4608 FLUX shape and a
-4-image batch, short activations, hipBLASLt bf16 at the same shape, the MXFP8, rowwise
-FP8 and W4A16 paths) and the CPU oracle timed on a bounded sample.
+Phases, in order (the GPU clock takes tens of milliseconds to rise after idle, so the
+settle phase runs by wall time, whatever --warmup says):
+
+1. settle: whole steps until at least --settle-seconds and --settle-min-steps have
+   passed (reported as its own field, with the step time of its last chunk);
+2. warm-up: --warmup untimed steps;
+3. timed: --steps whole steps between two HIP events on the launch stream -> `value`;
+4. roofline leg: the GEMM alone, back-to-back launches on the same stream (its average
+   launch duration, for the roofline against the f16 dense MFMA peak);
+5. quantize bandwidth on rotated buffers (beyond the 256 MB Infinity Cache) for the three
+   large activations [4608, 3072], [4608, 12288] and [18432, 3072], each beside a rotated
+   device-to-device copy moving the same bytes (the copy ceiling);
+6. context rows: the fused linear (quantize + GEMM) and the GEMM alone for every
+   M = 4608 FLUX linear and the 4-image batch, hipBLASLt bf16 at the metric's shape, the
+   MXFP8, rowwise FP8 and W4A16 paths, and short activations;
+7. the CPU oracle timed on a bounded sample.
+
+The GFX clock is sampled (amdsmi, its own thread) throughout and reported per leg.
 
     python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
                     [--no-context] [--no-cpu-baseline]
@@ -23,6 +35,7 @@ import ctypes
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -30,25 +43,30 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 GEMM TFLOP/s + % MFMA peak at FLUX shapes; quantize GB/s % HBM peak"
 PEAK_F16_TFLOPS = 2516.6  # MI355X dense f16/bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 QUANT_BYTES_PER_ELEM = 2.5625  # 2 B bf16 in + 0.5 B codes + 1/16 B scale out
+QUANT_SHAPES = [(4608, 3072), (4608, 12288), (18432, 3072)]  # the large FLUX activations
+LINEAR_WORKLOADS = ["attn_out", "mlp_up_static", "qkv", "mlp_down", "batch4_up"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU clock ramps for tens of milliseconds after idle: the first 50 attn_out steps
-    # average ~45% longer than the steady state reached after ~500 steps, so the default
-    # warm-up runs well past that before the timed steps.
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="wall time of whole steps run before the warm-up (clock ramp)")
+    ap.add_argument("--settle-min-steps", type=int, default=500)
+    ap.add_argument("--roofline-launches", type=int, default=1000,
+                    help="back-to-back GEMM launches of the roofline leg (at least --steps)")
     ap.add_argument("--workload", default="attn_out")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context rows (other shapes, hipBLASLt, MXFP8, fp8r, W4A16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rotate-mb", type=int, default=1024,
-                    help="bytes of rotated activation buffers for the quantize bandwidth leg")
+                    help="bytes of rotated buffers for the quantize and copy bandwidth legs")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -57,7 +75,6 @@ def parse():
 
 KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "kernels.hpp", "quantize.hip", "quant_common.hpp",
                   "codec.hpp"]
-PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA
 
 
 def kernel_source_hash() -> str:
@@ -84,12 +101,104 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's GFX clock (MHz) from amdsmi every `interval` seconds on its own
+    thread; `window(t0, t1)` summarises the samples taken between two host times. The
+    GPU is matched to amdsmi's device list by PCI bus; without amdsmi (or a readable
+    clock) every summary is None."""
+
+    def __init__(self, interval: float = 0.004):
+        self.interval = interval
+        self.samples: list[tuple[float, float]] = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            self._setup()
+        except Exception as e:  # no amdsmi, no permission, no device: report, never fail
+            self.source = f"unavailable ({type(e).__name__})"
+            self._read = None
+
+    def _setup(self):
+        import amdsmi
+        import torch
+
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            raise RuntimeError("no amdsmi devices")
+        props = torch.cuda.get_device_properties(0)
+        handle, matched = handles[0], False
+        for hd in handles:
+            try:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(hd)  # "dddd:bb:dd.f"
+                dom, bus = bdf.split(":")[0], bdf.split(":")[1]
+                if int(bus, 16) == props.pci_bus_id and int(dom, 16) == props.pci_domain_id:
+                    handle, matched = hd, True
+                    break
+            except Exception:
+                continue
+
+        def from_metrics():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            v = m.get("current_gfxclks")
+            vals = [float(c) for c in (v if isinstance(v, (list, tuple)) else [])
+                    if isinstance(c, (int, float)) and 0 < c < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+            c = m.get("current_gfxclk")
+            return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+
+        def from_clock_info():
+            c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX).get("clk")
+            return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+
+        for name, fn in (("amdsmi gpu_metrics current_gfxclk(s)", from_metrics),
+                         ("amdsmi clock_info GFX", from_clock_info)):
+            try:
+                if fn() is not None:
+                    self._read, self.source = fn, name + ("" if matched else " (device not matched by PCI bus)")
+                    return
+            except Exception:
+                continue
+        raise RuntimeError("no readable GFX clock")
+
+    def start(self):
+        if self._read is None:
+            return self
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    v = self._read()
+                    if v is not None:
+                        self.samples.append((time.perf_counter(), v))
+                except Exception:
+                    pass
+                self._stop.wait(self.interval)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=1.0)
+
+    def window(self, t0: float, t1: float):
+        v = [c for t, c in self.samples if t0 <= t <= t1]
+        if not v:
+            return None
+        return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1),
+                "max_mhz": round(max(v), 1), "samples": len(v)}
+
+
 def cpu_baseline(wl, d, ags, wgs, seconds):
     """The oracle as it stands on the workload's activation rows, full weights: chunks of
     rows in order (wrapping round to row 0 after the last) until about `seconds` of CPU
     work; scaled to TFLOP/s of the same 2*rows*N*K count."""
-    import numpy as np
-
     from oracle import nvfp4_oracle as O
 
     try:
@@ -122,29 +231,120 @@ def cpu_baseline(wl, d, ags, wgs, seconds):
     }
 
 
-def time_launches(fn, n, stream):
-    """Average ms of n back-to-back launches of fn on `stream` (HIP events on that
-    stream), after 3 untimed ones."""
+class Timer:
+    """HIP events on one stream around back-to-back launches, with the host times of the
+    region for the clock sampler."""
+
+    def __init__(self, stream, clock: ClockSampler):
+        import torch
+
+        self.torch, self.stream, self.clock = torch, stream, clock
+
+    def launches(self, fn, n: int, warm: int):
+        """Average ms of n back-to-back launches of fn on the stream, after `warm` untimed
+        ones; returns (ms, clock summary of the timed launches)."""
+        torch = self.torch
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(self.stream)
+        for _ in range(n):
+            fn()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return a.elapsed_time(b) / n, self.clock.window(t0, t1)
+
+
+def settle(step, stream, seconds: float, min_steps: int, chunk: int = 50):
+    """Whole steps in chunks of `chunk` until `seconds` of wall time and `min_steps` steps
+    have passed; returns the settle record (the last chunk's ms per step)."""
     import torch
 
-    for _ in range(3):
-        fn()
+    t_start = time.perf_counter()
+    steps, last_ms = 0, None
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(n):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+    while True:
+        a.record(stream)
+        for _ in range(chunk):
+            step()
+        b.record(stream)
+        b.synchronize()
+        steps += chunk
+        last_ms = a.elapsed_time(b) / chunk
+        if steps >= min_steps and time.perf_counter() - t_start >= seconds:
+            break
+    return {"seconds": round(time.perf_counter() - t_start, 3), "steps": steps,
+            "last_chunk_steps": chunk, "last_chunk_ms_per_step": round(last_ms, 5)}
 
 
-def context_legs(nv, lib, stream, n):
-    """Context rows (not the metric): every M = 4608 FLUX linear of the workload set, short
-    activations, hipBLASLt bf16 at the metric's shape, and the MXFP8, rowwise FP8 and W4A16
-    paths.
-    Operands are device-generated N(0, 1) activations and N(0, 0.02) weights, quantized
-    by the library; GEMM times are warm (operands resident)."""
+def bandwidth_legs(nv, lib, timer, sp, rotate_mb, n_min, gen):
+    """Quantize on rotated buffers for each large activation, and a rotated device copy
+    moving the same bytes (1.28125 B per element each way = the quantize's 2.5625 B of
+    traffic per element)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = []
+    for (M, K) in QUANT_SHAPES:
+        n_rot = max(2, int(rotate_mb * 2**20 // (M * K * 2)))
+        xs = [torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16) for _ in range(n_rot)]
+        f_gs = ctypes.c_float(nv.calibrate(xs[0]))
+        ob = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, K // 16), dtype=torch.uint8, device=dev)) for _ in range(n_rot)]
+        ptrs = [(P(a), P(b), P(c)) for a, (b, c) in zip(xs, ob)]
+        it = [0]
+
+        def q():
+            a, b, c = ptrs[it[0] % n_rot]
+            it[0] += 1
+            if lib.nvfp4_quantize(a, M, K, f_gs, b, c, sp):
+                raise RuntimeError("quantize failed")
+
+        n = max(n_min, 4 * n_rot)
+        ms, clk = timer.launches(q, n, warm=2 * n_rot)
+        nbytes = QUANT_BYTES_PER_ELEM * M * K
+        del xs, ob, ptrs
+        # copy of the same traffic, rotated the same way
+        cbytes = M * K * 41 // 32
+        n_crot = max(2, int(rotate_mb * 2**20 // (2 * cbytes)))
+        srcs = [torch.empty(cbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(n_crot)]
+        dsts = [torch.empty(cbytes, dtype=torch.uint8, device=dev) for _ in range(n_crot)]
+        jt = [0]
+
+        def cp():
+            i = jt[0] % n_crot
+            jt[0] += 1
+            dsts[i].copy_(srcs[i])
+
+        nc = max(n_min, 4 * n_crot)
+        cms, cclk = timer.launches(cp, nc, warm=2 * n_crot)
+        del srcs, dsts
+        torch.cuda.empty_cache()
+        out.append({
+            "shape": [M, K], "rotated_buffers": n_rot, "launches": n,
+            "avg_ms": round(ms, 5), "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": int(nbytes), "clock": clk,
+            "copy_same_bytes": {"bytes_each_way": cbytes, "rotated_buffers": n_crot,
+                                "avg_ms": round(cms, 5),
+                                "GB/s": round(2 * cbytes / (cms * 1e-3) / 1e9, 1),
+                                "frac": round(2 * cbytes / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "clock": cclk},
+        })
+    return out
+
+
+def context_legs(nv, lib, timer, stream, n):
+    """Context rows (not the metric). The fused linear (quantize + GEMM: nvfp4_linear) and
+    the GEMM alone on every M = 4608 FLUX linear and the 4-image batch, on the seeded
+    workload tensors (the static-scale MLP up-projection keeps its offline scale);
+    hipBLASLt bf16, MXFP8, rowwise FP8 and W4A16 at the metric's shape; short activations
+    (weights dominate the bytes). All operands resident (warm)."""
+    import numpy as np
     import torch
 
     from workloads import make
@@ -153,74 +353,79 @@ def context_legs(nv, lib, stream, n):
     gen = torch.Generator(device=dev).manual_seed(7)
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    out = {"gemm": {}, "short_activations": {}}
+    warm = max(20, n // 4)
+    out = {"linear": {}, "short_activations": {}}
 
-    def operands(M, N, K):
-        x = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
-        w = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
-        ags, wgs = nv.calibrate(x), nv.calibrate(w)
-        ap, as_ = nv.quantize(x, ags)
-        wp, ws = nv.quantize(w, wgs)
-        return x, w, ags, wgs, ap, as_, wp, ws
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def nvfp4_gemm_ms(M, N, K, ops):
-        _, _, ags, wgs, ap, as_, wp, ws = ops
-        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        args = (P(ap), P(as_), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(o), sp)
-        return time_launches(lambda: lib.nvfp4_gemm(*args), n, stream)
-
-    for name in ["attn_out", "mlp_up_static", "qkv", "mlp_down", "batch4_up"]:
+    for name in LINEAR_WORKLOADS:
         wl = make(name)
         M, N, K = wl.M, wl.N, wl.K
-        ops = operands(M, N, K)
-        ms = nvfp4_gemm_ms(M, N, K, ops)
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        out["gemm"][name] = {"M": M, "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K),
-                             "avg_ms": round(ms, 5), "TFLOP/s": round(tf, 1),
-                             "frac_f16_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+        d = wl.generate()
+        x, w = to_dev(d["x"]), to_dev(d["w"])
+        wgs = nv.calibrate(w)
+        wp, ws = nv.quantize(w, wgs)
+        ags = nv.calibrate(to_dev(d["calib"])) if "calib" in d else nv.calibrate(x)
+        del d
+        nb = nv.linear_workspace_bytes(M, K)
+        work = torch.empty(nb, dtype=torch.uint8, device=dev)
+        ap, as_ = nv.workspace_views(work, M, K)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        al = (P(x), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y),
+              P(work), ctypes.c_size_t(nb), sp)
+        ms_l, clk_l = timer.launches(lambda: lib.nvfp4_linear(*al), n, warm)
+        ag = (P(ap), P(as_), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
+        ms_g, clk_g = timer.launches(lambda: lib.nvfp4_gemm(*ag), n, warm)
+        fl = 2.0 * M * N * K
+        out["linear"][name] = {
+            "M": M, "N": N, "K": K, "gemm_kernel": nv.gemm_plan(M, N, K),
+            "static_activation_scale": bool(wl.static_scale),
+            "linear_avg_ms": round(ms_l, 5), "linear_TFLOP/s": round(fl / (ms_l * 1e-3) / 1e12, 1),
+            "linear_frac_f16_peak": round(fl / (ms_l * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+            "gemm_avg_ms": round(ms_g, 5), "gemm_TFLOP/s": round(fl / (ms_g * 1e-3) / 1e12, 1),
+            "gemm_frac_f16_peak": round(fl / (ms_g * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+            "gemm_share_of_linear": round(ms_g / ms_l, 4), "clock_linear": clk_l, "clock_gemm": clk_g}
         if name == "attn_out":
-            x, w, ags, wgs, ap, as_, wp, ws = ops
             # hipBLASLt bf16 GEMM of the unquantized operands at the same shape
             wt = w.t().contiguous()
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ms_b = time_launches(lambda: torch.matmul(x, wt, out=y), n, stream)
+            ms_b, _ = timer.launches(lambda: torch.matmul(x, wt, out=y), n, warm)
             out["hipblaslt_bf16_matmul"] = {"shape": [M, N, K], "avg_ms": round(ms_b, 5),
-                                            "TFLOP/s": round(2.0 * M * N * K / (ms_b * 1e-3) / 1e12, 1)}
+                                            "TFLOP/s": round(fl / (ms_b * 1e-3) / 1e12, 1)}
+            del wt
             # MXFP8 path (E4M3 elements, E8M0 scales per 32) on the same operands
             ac, asx = nv.mxfp8_quantize(x)
             wc, wsx = nv.mxfp8_quantize(w)
-            y8 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            a8 = (P(ac), P(asx), P(wc), P(wsx), M, N, K, P(y8), sp)
-            ms8 = time_launches(lambda: lib.nvfp4_mxfp8_gemm(*a8), n, stream)
+            a8 = (P(ac), P(asx), P(wc), P(wsx), M, N, K, P(y), sp)
+            ms8, _ = timer.launches(lambda: lib.nvfp4_mxfp8_gemm(*a8), n, warm)
             q8 = (P(x), M, K, P(ac), P(asx), sp)
-            msq8 = time_launches(lambda: lib.nvfp4_mxfp8_quantize(*q8), n, stream)
-            tf8 = 2.0 * M * N * K / (ms8 * 1e-3) / 1e12
-            out["mxfp8"] = {"shape": [M, N, K], "gemm_avg_ms": round(ms8, 5), "gemm_TFLOP/s": round(tf8, 1),
-                            "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+            msq8, _ = timer.launches(lambda: lib.nvfp4_mxfp8_quantize(*q8), n, warm)
+            out["mxfp8"] = {"shape": [M, N, K], "gemm_avg_ms": round(ms8, 5),
+                            "gemm_TFLOP/s": round(fl / (ms8 * 1e-3) / 1e12, 1),
+                            "frac_fp8_peak": round(fl / (ms8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                             "quantize_avg_ms_warm": round(msq8, 5),
                             "quantize_GB/s_warm": round((2 + 1 + 1 / 32) * M * K / (msq8 * 1e-3) / 1e9, 1)}
+            del ac, asx, wc, wsx
             # rowwise FP8 (fp8r): E4M3 with one fp32 scale per row, unit-scaled fp8 MFMA
             rc, rs = nv.fp8r_quantize(x)
             wrc, wrs = nv.fp8r_quantize(w)
-            yr = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ar = (P(rc), P(rs), P(wrc), P(wrs), M, N, K, P(yr), sp)
-            msr = time_launches(lambda: lib.nvfp4_fp8r_gemm(*ar), n, stream)
+            ar = (P(rc), P(rs), P(wrc), P(wrs), M, N, K, P(y), sp)
+            msr, _ = timer.launches(lambda: lib.nvfp4_fp8r_gemm(*ar), n, warm)
             qr = (P(x), M, K, P(rc), P(rs), sp)
-            msqr = time_launches(lambda: lib.nvfp4_fp8r_quantize(*qr), n, stream)
-            tfr = 2.0 * M * N * K / (msr * 1e-3) / 1e12
-            out["fp8r"] = {"shape": [M, N, K], "gemm_avg_ms": round(msr, 5), "gemm_TFLOP/s": round(tfr, 1),
-                           "frac_fp8_peak": round(tfr / PEAK_FP8_TFLOPS, 4),
+            msqr, _ = timer.launches(lambda: lib.nvfp4_fp8r_quantize(*qr), n, warm)
+            out["fp8r"] = {"shape": [M, N, K], "gemm_avg_ms": round(msr, 5),
+                           "gemm_TFLOP/s": round(fl / (msr * 1e-3) / 1e12, 1),
+                           "frac_fp8_peak": round(fl / (msr * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                            "quantize_avg_ms_warm": round(msqr, 5),
                            "quantize_GB/s_warm": round((3 * M * K + 4 * M) / (msqr * 1e-3) / 1e9, 1)}
-            del rc, rs, wrc, wrs, yr
+            del rc, rs, wrc, wrs
             # W4A16: NVFP4 weights, bf16 activations
-            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)
-            ms16 = time_launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, stream)
+            a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
+            ms16, _ = timer.launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, warm)
             out["w4a16"] = {"shape": [M, N, K], "avg_ms": round(ms16, 5),
-                            "TFLOP/s": round(2.0 * M * N * K / (ms16 * 1e-3) / 1e12, 1)}
-            del x, w, wt, y, ac, asx, wc, wsx, y8, y16
-        del ops
+                            "TFLOP/s": round(fl / (ms16 * 1e-3) / 1e12, 1)}
+        del x, w, wp, ws, work, ap, as_, y
+        torch.cuda.empty_cache()
     # short activations: the weights dominate the bytes (K/2 + K/16 bytes per weight row)
     N, K = 3072, 3072
     w = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
@@ -230,16 +435,16 @@ def context_legs(nv, lib, stream, n):
         x = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
         ags = nv.calibrate(x)
         ap, as_ = nv.quantize(x, ags)
-        ms = nvfp4_gemm_ms(M, N, K, (x, w, ags, wgs, ap, as_, wp, ws))
-        y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16), sp)
-        ms16 = time_launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, stream)
-        # the whole linear (quantize + GEMM, one fused kernel where the plan says so)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ag = (P(ap), P(as_), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
+        ms, _ = timer.launches(lambda: lib.nvfp4_gemm(*ag), n, warm)
+        a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
+        ms16, _ = timer.launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, warm)
         nb = nv.linear_workspace_bytes(M, K)
         work = torch.empty(nb, dtype=torch.uint8, device=dev)
-        al = (P(x), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y16),
+        al = (P(x), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y),
               P(work), ctypes.c_size_t(nb), sp)
-        msl = time_launches(lambda: lib.nvfp4_linear(*al), n, stream)
+        msl, _ = timer.launches(lambda: lib.nvfp4_linear(*al), n, warm)
         wbytes = N * (K // 2 + K // 16)
         out["short_activations"][f"M={M}"] = {
             "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K), "w4a4_avg_ms": round(ms, 5),
@@ -254,7 +459,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   f"--gpus {args.gpus} is not supported"}))
+                                   f"--gpus {args.gpus} is not supported (the hot path is "
+                                   "measured on one GPU's share; see DESIGN.md for sharding)"}))
         sys.exit(2)
 
     import numpy as np
@@ -299,88 +505,46 @@ def main():
         if s1 or s2:
             raise RuntimeError(f"status {s1} {s2}")
 
-    # untimed warm-up; its first 50 steps are timed separately to show the clock ramp
-    n_first = min(50, args.warmup)
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
-    for i in range(args.warmup):
-        step()
-        if i + 1 == n_first:
-            w1.record(stream)
-    torch.cuda.synchronize()
-    first_ms = w0.elapsed_time(w1) / n_first if n_first else None
+    def gemm_only():
+        if lib.nvfp4_gemm(qpa, qsa, f_ags, wqa, wsa, f_wgs, M, N, K, oa, sp):
+            raise RuntimeError("gemm failed")
 
-    # Timed region 1: K whole steps (quantize + GEMM), events only at its two ends.
+    clock = ClockSampler().start()
+    timer = Timer(stream, clock)
+
+    # 1. clock settle (wall time, independent of --warmup), 2. warm-up
+    t_s0 = time.perf_counter()
+    settle_rec = settle(step, stream, args.settle_seconds, args.settle_min_steps)
+    settle_rec["clock"] = clock.window(t_s0, time.perf_counter())
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # 3. Timed region: K whole steps (quantize + GEMM), events only at its two ends.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    h0 = time.perf_counter()
     t_start.record(stream)
     for _ in range(args.steps):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
+    h1 = time.perf_counter()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    # Timed region 2: the dominant kernel alone, K back-to-back launches on the same
-    # stream (its average launch duration, for the roofline).
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for _ in range(args.steps):
-        if lib.nvfp4_gemm(qpa, qsa, f_ags, wqa, wsa, f_wgs, M, N, K, oa, sp):
-            raise RuntimeError("gemm failed")
-    g1.record(stream)
-    torch.cuda.synchronize()
-    g_ms = g0.elapsed_time(g1) / args.steps
+    # 4. The dominant kernel alone, back-to-back launches on the same stream (its average
+    # launch duration, for the roofline).
+    n_roof = max(args.steps, args.roofline_launches)
+    g_ms, g_clk = timer.launches(gemm_only, n_roof, warm=0)
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
 
-    # quantize bandwidth on rotated buffers (beyond the 256 MB Infinity Cache)
-    n_rot = max(2, int(args.rotate_mb * 2**20 // (M * K * 2)))
-    xs = [x] + [x.clone() for _ in range(n_rot - 1)]
-    outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
-             torch.empty((M, K // 16), dtype=torch.uint8, device=dev)) for _ in range(n_rot)]
-    ptrs = [(P(a), P(b), P(c)) for a, (b, c) in zip(xs, outs)]
-    for i in range(n_rot):
-        lib.nvfp4_quantize(ptrs[i][0], M, K, f_ags, ptrs[i][1], ptrs[i][2], sp)
-    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_q = max(args.steps, 4 * n_rot)
-    torch.cuda.synchronize()
-    qa.record(stream)
-    for i in range(n_q):
-        a, b, c = ptrs[i % n_rot]
-        lib.nvfp4_quantize(a, M, K, f_ags, b, c, sp)
-    qb.record(stream)
-    torch.cuda.synchronize()
-    q_rot_ms = qa.elapsed_time(qb) / n_q
-    q_gbs = QUANT_BYTES_PER_ELEM * M * K / (q_rot_ms * 1e-3) / 1e9
-    del xs, outs
-
-    # quantize bandwidth on a large activation (the 4608 x 12288 input of a FLUX MLP down
-    # projection), rotated the same way
-    LM, LK = 4608, 12288
-    n_rot_l = max(2, int(args.rotate_mb * 2**20 // (LM * LK * 2)))
+    # 5. quantize bandwidth (and the copy ceiling) on rotated buffers
     gen = torch.Generator(device=dev).manual_seed(5)
-    xl = [torch.randn((LM, LK), device=dev, generator=gen).to(torch.bfloat16) for _ in range(n_rot_l)]
-    ol = [(torch.empty((LM, LK // 2), dtype=torch.uint8, device=dev),
-           torch.empty((LM, LK // 16), dtype=torch.uint8, device=dev)) for _ in range(n_rot_l)]
-    f_lgs = ctypes.c_float(nv.calibrate(xl[0]))
-    pl = [(P(a), P(b), P(c)) for a, (b, c) in zip(xl, ol)]
-    for i in range(n_rot_l):
-        lib.nvfp4_quantize(pl[i][0], LM, LK, f_lgs, pl[i][1], pl[i][2], sp)
-    n_ql = max(args.steps, 4 * n_rot_l)
-    torch.cuda.synchronize()
-    qa.record(stream)
-    for i in range(n_ql):
-        a, b, c = pl[i % n_rot_l]
-        lib.nvfp4_quantize(a, LM, LK, f_lgs, b, c, sp)
-    qb.record(stream)
-    torch.cuda.synchronize()
-    ql_ms = qa.elapsed_time(qb) / n_ql
-    ql_gbs = QUANT_BYTES_PER_ELEM * LM * LK / (ql_ms * 1e-3) / 1e9
-    del xl, ol
+    del x, qp, qs, work, out
+    torch.cuda.empty_cache()
+    bw = bandwidth_legs(nv, lib, timer, sp, args.rotate_mb, max(args.steps, 200), gen)
 
     if args.copy_calibration_mb:
         # Known-size reference for the hardware byte counters: a plain device copy of
@@ -395,6 +559,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst, evict
 
+    q0 = bw[0]
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -403,7 +568,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "warmup_first_steps_ms_per_step": round(first_ms, 5) if first_ms else None,
+        "settle": settle_rec,
+        "clock_timed_steps": clock.window(h0, h1),
+        "clock_source": clock.source,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -427,30 +594,24 @@ def main():
             "traffic": measured_traffic(wl.name),
             "kernel_source_hash": kernel_source_hash(),
             "avg_ms": round(g_ms, 5),
+            "launches": n_roof,
+            "clock": g_clk,
         },
         "quantize": {
-            "rotated_avg_ms": round(q_rot_ms, 5),
-            "achieved": round(q_gbs, 1),
+            "rotated_avg_ms": q0["avg_ms"],
+            "achieved": q0["achieved"],
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-            "bytes_per_launch": int(QUANT_BYTES_PER_ELEM * M * K),
-            "rotated_buffers": n_rot,
-            "large": {
-                "shape": [LM, LK],
-                "rotated_avg_ms": round(ql_ms, 5),
-                "achieved": round(ql_gbs, 1),
-                "frac": round(ql_gbs / PEAK_HBM_GBS, 4),
-                "rotated_buffers": n_rot_l,
-            },
+            "frac": q0["frac"],
+            "bytes_per_launch": q0["bytes_per_launch"],
+            "shapes": bw,
         },
         "precision": "E2M1 x E4M3 operands decoded exactly to f16, f16 MFMA, fp32 accumulate, "
                      "bf16 output",
     }
     if not args.no_context:
-        del x, qp, qs, work, out
-        torch.cuda.empty_cache()
-        result["context"] = context_legs(nv, lib, stream, max(10, args.steps // 2))
+        result["context"] = context_legs(nv, lib, timer, stream, max(50, args.steps // 2))
+    clock.stop()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, ags, wgs, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -263,16 +263,19 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, gs: float) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def gemm_ref(a_packed, a_scales, a_gs, w_packed, w_scales, w_gs, *, with_abs: bool = True):
+def gemm_ref(a_packed, a_scales, a_gs, w_packed, w_scales, w_gs, *, with_abs: bool = True,
+             w_decoded=None):
     """Reference W4A4 product out = (A_hat @ W_hat^T) * a_gs * w_gs in float64.
 
     A is [M, K] activations, W is [N, K] weights (PyTorch Linear layout), both NVFP4.
     Each decoded product is exact in float64; the float64 sum differs from the exact
     sum by far less than the acceptance bound. Returns ``(ref, absref)`` where
     ``absref = (|A_hat| @ |W_hat|^T) * a_gs * w_gs`` feeds the tolerance (or ``None``).
+    ``w_decoded``, if given, is ``decode_blocks(w_packed, w_scales)`` computed once by
+    the caller for many calls over row chunks of A (a cache; nothing else changes).
     """
     A = decode_blocks(a_packed, a_scales)
-    W = decode_blocks(w_packed, w_scales)
+    W = decode_blocks(w_packed, w_scales) if w_decoded is None else w_decoded
     g = np.float64(np.float32(a_gs)) * np.float64(np.float32(w_gs))
     ref = (A @ W.T) * g
     absref = (np.abs(A) @ np.abs(W).T) * g if with_abs else None
