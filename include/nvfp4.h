@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 /* Status codes. All argument validation happens before any HIP call. */
 typedef enum nvfp4_status {
@@ -74,7 +74,9 @@ typedef enum nvfp4_status {
                                          scales not 4-byte aligned */
   NVFP4_ERROR_WORKSPACE = 4,          /* workspace smaller than nvfp4_linear_workspace_bytes */
   NVFP4_ERROR_UNSUPPORTED_DEVICE = 5, /* no HIP device, or the current device is not gfx950 */
-  NVFP4_ERROR_HIP = 6                 /* a HIP call failed; see nvfp4_last_hip_error() */
+  NVFP4_ERROR_HIP = 6,                /* a HIP call failed; see nvfp4_last_hip_error() */
+  NVFP4_ERROR_TOO_LARGE = 7           /* nvfp4_linear_noalloc: the problem's workspace exceeds
+                                         the library's static scratch (32 MiB) */
 } nvfp4_status;
 
 /*
@@ -264,6 +266,27 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
 int nvfp4_linear(const void* x_bf16, float a_global_scale, const void* w_packed,
                  const void* w_scales, float w_global_scale, int64_t M, int64_t N, int64_t K,
                  void* out_bf16, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_linear without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). It runs the same kernels as nvfp4_linear, with their workspace in a static
+ * device array of 32 MiB that the library holds on each device it is loaded on, for the
+ * life of the process; it calls no allocator. Arguments as in nvfp4_linear, without
+ * workspace and workspace_bytes; out is bit-identical to nvfp4_linear's for the same
+ * inputs.
+ *   - Limit: nvfp4_linear_workspace_bytes(M, K) <= 32 MiB (M * K up to about 59.6 million,
+ *     e.g. [4608, 12288] or [18432, 3072] activations); larger problems return
+ *     NVFP4_ERROR_TOO_LARGE before any HIP call.
+ *   - Every call on a device shares that device's array, which keeps the last call's
+ *     quantized activations. Calls that overlap in time on one device (on different
+ *     streams, or from different threads without ordering) race on it and may produce
+ *     wrong results; calls ordered on one stream are safe.
+ *   - The first call on a device looks up the array's device address (once per device).
+ */
+int nvfp4_linear_noalloc(const void* x_bf16, float a_global_scale, const void* w_packed,
+                         const void* w_scales, float w_global_scale, int64_t M, int64_t N,
+                         int64_t K, void* out_bf16, void* stream);
 
 /*
  * Calibration of a global scale (the pages' calibrated fp32 input_scale and the stored

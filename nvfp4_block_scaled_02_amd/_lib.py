@@ -11,7 +11,7 @@ import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnvfp4.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {
     0: "NVFP4_SUCCESS",
@@ -21,8 +21,9 @@ STATUS = {
     4: "NVFP4_ERROR_WORKSPACE",
     5: "NVFP4_ERROR_UNSUPPORTED_DEVICE",
     6: "NVFP4_ERROR_HIP",
+    7: "NVFP4_ERROR_TOO_LARGE",
 }
-SUCCESS, INVALID_VALUE, INVALID_SHAPE, MISALIGNED, WORKSPACE, UNSUPPORTED_DEVICE, HIP = range(7)
+SUCCESS, INVALID_VALUE, INVALID_SHAPE, MISALIGNED, WORKSPACE, UNSUPPORTED_DEVICE, HIP, TOO_LARGE = range(8)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -46,6 +47,7 @@ SIGNATURES = {
     "nvfp4_linear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "nvfp4_linear": (_int, [_vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp,
                             ctypes.c_size_t, _vp]),
+    "nvfp4_linear_noalloc": (_int, [_vp, _f32, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_amax": (_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_global_scale_from_amax": (_f32, [_f32]),
     "nvfp4_calibrate_device": (_int, [_vp, _i64, _vp, _vp]),

@@ -20,7 +20,7 @@ struct DeviceEntry {
   std::once_flag once;
   int status = NVFP4_ERROR_UNSUPPORTED_DEVICE;
   hipError_t err = hipSuccess;
-  nvfp4::LaunchInfo info{0};
+  nvfp4::LaunchInfo info{0, 0};
 };
 DeviceEntry g_devices[kMaxDevices];
 
@@ -51,6 +51,7 @@ int current_device(nvfp4::LaunchInfo* info) {
       return;
     }
     d.info.num_cus = prop.multiProcessorCount;
+    d.info.device = dev;
     d.status = NVFP4_SUCCESS;
   });
   if (d.status == NVFP4_ERROR_HIP) g_last_hip_error = (int)d.err;
@@ -59,6 +60,37 @@ int current_device(nvfp4::LaunchInfo* info) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Static device scratch of nvfp4_linear_noalloc: the workspace of nvfp4_linear (quantized
+// activations), for callers that cannot allocate. Every device the library is loaded on
+// holds its own copy until the process ends. In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchEntry {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+};
+ScratchEntry g_scratch[kMaxDevices];
+
+// Device address of this device's scratch (info.device is current).
+int scratch_pointer(const nvfp4::LaunchInfo& info, void** out) {
+  ScratchEntry& e = g_scratch[info.device];
+  std::call_once(e.once, [&]() {
+    void* p = nullptr;
+    e.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e.ptr = e.err == hipSuccess ? p : nullptr;
+  });
+  if (e.err != hipSuccess || e.ptr == nullptr) {
+    g_last_hip_error = (int)(e.err != hipSuccess ? e.err : hipErrorInvalidSymbol);
+    return NVFP4_ERROR_HIP;
+  }
+  *out = e.ptr;
+  return NVFP4_SUCCESS;
+}
 
 // Global scales: finite, in [2^-90, 2^90]. In this range every per-block divisor
 // d = s * gs (s >= 2^-9) and 6 * gs stay far enough from the fp32 subnormal range that
@@ -105,6 +137,8 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERROR_WORKSPACE: return "workspace too small";
     case NVFP4_ERROR_UNSUPPORTED_DEVICE: return "no gfx950 device";
     case NVFP4_ERROR_HIP: return "HIP runtime error";
+    case NVFP4_ERROR_TOO_LARGE:
+      return "problem needs more than the static scratch of nvfp4_linear_noalloc (32 MiB)";
     default: return "unknown status";
   }
 }
@@ -265,23 +299,18 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
   return round_up((size_t)(M * K / 2), 256) + round_up((size_t)(M * K / 16), 256);
 }
 
-int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float wgs, int64_t M,
-                 int64_t N, int64_t K, void* out, void* workspace, size_t workspace_bytes,
-                 void* stream) {
-  if (!x || !workspace) return NVFP4_ERROR_INVALID_VALUE;
-  int s = check_shape(M, K);
-  if (s) return s;
+}  // extern "C"
+
+namespace {
+
+// The launches of nvfp4_linear once its arguments are valid and M > 0: quantize into the
+// workspace, then the GEMM (or the one fused kernel for the shortest activations).
+int linear_launch(const void* x, float ags, const void* wp, const void* ws, float wgs, int64_t M,
+                  int64_t N, int64_t K, void* out, void* workspace, void* stream,
+                  const nvfp4::LaunchInfo& info) {
   const size_t packed_bytes = round_up((size_t)(M * K / 2), 256);
   uint8_t* ap = (uint8_t*)workspace;
   uint8_t* as = ap + packed_bytes;
-  s = validate_gemm(ap, as, ags, wp, ws, wgs, M, N, K, out);
-  if (s) return s;
-  if (!aligned(x, 16)) return NVFP4_ERROR_MISALIGNED;
-  if (workspace_bytes < nvfp4_linear_workspace_bytes(M, K)) return NVFP4_ERROR_WORKSPACE;
-  if (M == 0) return NVFP4_SUCCESS;
-  nvfp4::LaunchInfo info;
-  s = current_device(&info);
-  if (s) return s;
   const nvfp4::Alpha al = nvfp4::split_alpha(ags, wgs);
   nvfp4::GemmProblem p{ap, as, (const uint8_t*)wp, (const uint8_t*)ws, (uint16_t*)out,
                        M, N, K, al.m, nullptr, nullptr, al.e};
@@ -297,6 +326,54 @@ int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float
   if (N == 0) return NVFP4_SUCCESS;
   e = nvfp4::launch_gemm(p, (hipStream_t)stream, info);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+// Argument checks shared by nvfp4_linear and nvfp4_linear_noalloc (the workspace address
+// only enters through its alignment).
+int validate_linear(const void* x, float ags, const void* wp, const void* ws, float wgs, int64_t M,
+                    int64_t N, int64_t K, const void* out, const void* workspace) {
+  if (!x || !workspace) return NVFP4_ERROR_INVALID_VALUE;
+  int s = check_shape(M, K);
+  if (s) return s;
+  const uint8_t* ap = (const uint8_t*)workspace;
+  s = validate_gemm(ap, ap + round_up((size_t)(M * K / 2), 256), ags, wp, ws, wgs, M, N, K, out);
+  if (s) return s;
+  if (!aligned(x, 16)) return NVFP4_ERROR_MISALIGNED;
+  return NVFP4_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_linear(const void* x, float ags, const void* wp, const void* ws, float wgs, int64_t M,
+                 int64_t N, int64_t K, void* out, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int s = validate_linear(x, ags, wp, ws, wgs, M, N, K, out, workspace);
+  if (s) return s;
+  if (workspace_bytes < nvfp4_linear_workspace_bytes(M, K)) return NVFP4_ERROR_WORKSPACE;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  return linear_launch(x, ags, wp, ws, wgs, M, N, K, out, workspace, stream, info);
+}
+
+int nvfp4_linear_noalloc(const void* x, float ags, const void* wp, const void* ws, float wgs,
+                         int64_t M, int64_t N, int64_t K, void* out, void* stream) {
+  // a stand-in workspace address for the checks (the scratch is 256-byte aligned)
+  static const uint8_t kAligned[256] __attribute__((aligned(256))) = {0};
+  int s = validate_linear(x, ags, wp, ws, wgs, M, N, K, out, kAligned);
+  if (s) return s;
+  if (nvfp4_linear_workspace_bytes(M, K) > kScratchBytes) return NVFP4_ERROR_TOO_LARGE;
+  if (M == 0) return NVFP4_SUCCESS;
+  nvfp4::LaunchInfo info;
+  s = current_device(&info);
+  if (s) return s;
+  void* work = nullptr;
+  s = scratch_pointer(info, &work);
+  if (s) return s;
+  return linear_launch(x, ags, wp, ws, wgs, M, N, K, out, work, stream, info);
 }
 
 int nvfp4_linear_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* fused) {

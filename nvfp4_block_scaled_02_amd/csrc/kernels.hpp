@@ -10,6 +10,7 @@ namespace nvfp4 {
 
 struct LaunchInfo {
   int num_cus;  // compute units of the current device
+  int device;   // its index
 };
 
 // gs_dev non-null: the global scale is read on the device from *gs_dev (clamped into

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.nvfp4_abi_version() == L.ABI_VERSION
-    for s in range(7):
+    for s in range(8):
         assert lib.nvfp4_status_string(s)
     assert lib.nvfp4_status_string(99) == b"unknown status"
 
@@ -315,6 +315,36 @@ def test_linear_validation_and_workspace(lib):
     assert lin(*b) == L.SUCCESS
 
 
+def test_linear_noalloc_validation(lib):
+    """The allocation-free linear checks its arguments like nvfp4_linear and refuses a
+    problem whose workspace exceeds its 32 MiB static scratch, before any HIP call."""
+    lin = lib.nvfp4_linear_noalloc
+    ws = lib.nvfp4_linear_workspace_bytes
+    base = [P16, 1.0, P16b, P16b, 1.0, 8, 8, 64, P16, NULL]
+    b = list(base)
+    b[0] = NULL
+    assert lin(*b) == L.INVALID_VALUE
+    b = list(base)
+    b[1] = 0.0
+    assert lin(*b) == L.INVALID_VALUE
+    b = list(base)
+    b[0] = ODD
+    assert lin(*b) == L.MISALIGNED
+    b = list(base)
+    b[7] = 72
+    assert lin(*b) == L.INVALID_SHAPE
+    b = list(base)
+    b[5] = 0
+    assert lin(*b) == L.SUCCESS
+    # the largest FLUX activations fit; one more row of 12288 does not
+    assert ws(4608, 12288) <= 32 << 20 and ws(18432, 3072) <= 32 << 20
+    assert ws(4854, 12288) <= 32 << 20 < ws(4855, 12288)
+    b = list(base)
+    b[5], b[7] = 4855, 12288
+    assert lin(*b) == L.TOO_LARGE
+    assert lib.nvfp4_status_string(L.TOO_LARGE).startswith(b"problem needs more")
+
+
 def test_amax_validation(lib):
     out = ctypes.c_void_p(0x30000)
     assert lib.nvfp4_amax(NULL, 16, out, NULL) == L.INVALID_VALUE
@@ -327,6 +357,8 @@ def test_no_device_is_reported(lib, gpu_available):
         pytest.skip("a GPU is present")
     assert lib.nvfp4_quantize(P16, 4, 32, 1.0, P16, P16b, NULL) == L.UNSUPPORTED_DEVICE
     assert lib.nvfp4_gemm(P16, P16b, 1.0, P16, P16b, 1.0, 8, 8, 64, P16, NULL) == \
+        L.UNSUPPORTED_DEVICE
+    assert lib.nvfp4_linear_noalloc(P16, 1.0, P16b, P16b, 1.0, 8, 8, 64, P16, NULL) == \
         L.UNSUPPORTED_DEVICE
 
 
