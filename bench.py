@@ -191,8 +191,10 @@ class ClockSampler:
         v = [c for t, c in self.samples if t0 <= t <= t1]
         if not v:
             return None
+        # (amdsmi refreshes its metrics every few ms to tens of ms, so consecutive samples
+        # often repeat a value: "distinct" counts the different readings)
         return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1),
-                "max_mhz": round(max(v), 1), "samples": len(v)}
+                "max_mhz": round(max(v), 1), "samples": len(v), "distinct": len(set(v))}
 
 
 def cpu_baseline(wl, d, ags, wgs, seconds):

@@ -171,12 +171,15 @@ int nvfp4_gemm_w4a16(const void* x_bf16, const void* w_packed, const void* w_sca
  * (paragraph 1: Open Compute Project standard, 8-bit E4M3/E5M2 elements, 32-element
  * blocks sharing one scale). Conventions of this library (the page names the OCP
  * standard; these follow its format definition):
- *   - elements are OCP E4M3 ("FN", max 448), one byte each, row-major [rows, K];
+ *   - elements are one byte each, row-major [rows, K], of either OCP type:
+ *     E4M3 ("FN": bias 7, no Inf, largest 448 = 1.75 * 2^8) or E5M2 (bias 15, Inf/NaN at
+ *     exponent field 31, largest finite 57344 = 1.75 * 2^15);
  *   - each 32-element block along K shares an E8M0 scale byte (value 2^(byte - 127),
  *     0xFF never produced), row-major [rows, K/32];
- *   - quantization: e = floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block:
- *     e = -127, byte 0); element = E4M3 nearest to x / 2^e, ties to even, saturating at
- *     448, sign copied (-0 -> 0x80);
+ *   - quantization: e = floor(log2(amax)) - emax clamped to [-127, 127], emax = 8 for
+ *     E4M3 and 15 for E5M2 (all-zero block: e = -127, byte 0); element = the value of the
+ *     element type nearest to x / 2^e, ties to even, saturating at its largest finite
+ *     value (never Inf or NaN), sign copied (-0 -> 0x80);
  *   - GEMM: out = bf16_RNE(sum_k a_k w_k) with a_k, w_k the decoded values, no tensor
  *     scale; any result within 2^-10 * sum_k |a_k w_k| + 1 bf16 ulp of the exact value is
  *     correct and the library's result is deterministic for a given shape.
@@ -197,6 +200,26 @@ int nvfp4_mxfp8_quantize(const void* x_bf16, int64_t M, int64_t K, void* codes, 
 int nvfp4_mxfp8_gemm(const void* a_codes, const void* a_scales, const void* w_codes,
                      const void* w_scales, int64_t M, int64_t N, int64_t K, void* out_bf16,
                      void* stream);
+
+/* MXFP8 element types (the `element` arguments below). */
+typedef enum { NVFP4_MX_E4M3 = 0, NVFP4_MX_E5M2 = 1 } nvfp4_mx_element;
+
+/*
+ * nvfp4_mxfp8_quantize with the element type chosen (NVFP4_MX_E4M3 is
+ * nvfp4_mxfp8_quantize); any other value returns NVFP4_ERROR_INVALID_VALUE.
+ */
+int nvfp4_mxfp8_quantize_elem(const void* x_bf16, int64_t M, int64_t K, int element,
+                              void* codes, void* scales, void* stream);
+
+/*
+ * nvfp4_mxfp8_gemm with each operand's element type chosen (E4M3 x E4M3 is
+ * nvfp4_mxfp8_gemm): the block-scaled MFMA takes the two operand formats separately, so
+ * E4M3 and E5M2 operands mix freely. Other requirements as nvfp4_mxfp8_gemm; an unknown
+ * element type returns NVFP4_ERROR_INVALID_VALUE.
+ */
+int nvfp4_mxfp8_gemm_elem(const void* a_codes, const void* a_scales, int a_element,
+                          const void* w_codes, const void* w_scales, int w_element, int64_t M,
+                          int64_t N, int64_t K, void* out_bf16, void* stream);
 
 /*
  * Rowwise FP8 ("fp8r") path: the other scheme of the "BFL (fp8r / nvfp4)" page (scheme

@@ -48,6 +48,12 @@ int nvfp4_selftest_block_scale(const float* amax, float global_scale, uint8_t* c
 int nvfp4_selftest_mxfp8_e4m3_exhaustive(unsigned long long* mismatches, uint32_t* first16,
                                          void* stream);
 
+/* The same for the bf8 (E5M2) conversion of the MXFP8 quantizer: every non-NaN, non-Inf
+ * binary32 pattern clamped to [-57344, 57344], converted by the hardware and by the
+ * software E5M2 encoder (nearest, ties to even, saturating, sign copied). */
+int nvfp4_selftest_mxfp8_e5m2_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                         void* stream);
+
 /* The GEMM's operand decode: packed[nbytes] holds 2*nbytes E2M1 codes (low nibble
  * first); scales[nbytes / 4] holds one E4M3 code per 4 packed bytes. Writes 2*nbytes
  * f16 bit patterns of code value * scale to hw_f16 (conversion-instruction decode) and

@@ -42,6 +42,8 @@ SIGNATURES = {
     "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_mxfp8_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_mxfp8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_mxfp8_quantize_elem": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp]),
+    "nvfp4_mxfp8_gemm_elem": (_int, [_vp, _vp, _int, _vp, _vp, _int, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_fp8r_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_fp8r_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_linear_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
@@ -59,6 +61,7 @@ SIGNATURES = {
     "nvfp4_selftest_e2m1_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_division": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_mxfp8_e4m3_exhaustive": (_int, [_vp, _vp, _vp]),
+    "nvfp4_selftest_mxfp8_e5m2_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_block_scale": (_int, [_vp, _f32, _vp, _vp, _i64, _vp]),
     "nvfp4_selftest_decode": (_int, [_vp, _vp, _vp, _vp, _i64, _vp]),
 }

@@ -217,7 +217,13 @@ int nvfp4_gemm_w4a16(const void* x, const void* wp, const void* ws, float wgs, i
 
 int nvfp4_mxfp8_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
                          void* stream) {
+  return nvfp4_mxfp8_quantize_elem(x, M, K, NVFP4_MX_E4M3, codes, scales, stream);
+}
+
+int nvfp4_mxfp8_quantize_elem(const void* x, int64_t M, int64_t K, int element, void* codes,
+                              void* scales, void* stream) {
   if (!x || !codes || !scales) return NVFP4_ERROR_INVALID_VALUE;
+  if (element != NVFP4_MX_E4M3 && element != NVFP4_MX_E5M2) return NVFP4_ERROR_INVALID_VALUE;
   int s = check_shape(M, K);
   if (s) return s;
   if (K % 32 != 0) return NVFP4_ERROR_INVALID_SHAPE;
@@ -226,13 +232,23 @@ int nvfp4_mxfp8_quantize(const void* x, int64_t M, int64_t K, void* codes, void*
   nvfp4::LaunchInfo info;
   s = current_device(&info);
   if (s) return s;
-  hipError_t e = nvfp4::launch_mx_quantize(x, M, K, codes, scales, (hipStream_t)stream, info);
+  hipError_t e = nvfp4::launch_mx_quantize(x, M, K, codes, scales, (hipStream_t)stream, info,
+                                           (nvfp4::MxElement)element);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
 int nvfp4_mxfp8_gemm(const void* ac, const void* as, const void* wc, const void* ws, int64_t M,
                      int64_t N, int64_t K, void* out, void* stream) {
+  return nvfp4_mxfp8_gemm_elem(ac, as, NVFP4_MX_E4M3, wc, ws, NVFP4_MX_E4M3, M, N, K, out, stream);
+}
+
+int nvfp4_mxfp8_gemm_elem(const void* ac, const void* as, int a_element, const void* wc,
+                          const void* ws, int w_element, int64_t M, int64_t N, int64_t K,
+                          void* out, void* stream) {
   if (!ac || !as || !wc || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;
+  if ((a_element != NVFP4_MX_E4M3 && a_element != NVFP4_MX_E5M2) ||
+      (w_element != NVFP4_MX_E4M3 && w_element != NVFP4_MX_E5M2))
+    return NVFP4_ERROR_INVALID_VALUE;
   int s = check_shape(M, K);
   if (s) return s;
   s = check_shape(N, K);
@@ -251,7 +267,8 @@ int nvfp4_mxfp8_gemm(const void* ac, const void* as, const void* wc, const void*
   if (s) return s;
   nvfp4::GemmProblem p{(const uint8_t*)ac, (const uint8_t*)as, (const uint8_t*)wc,
                        (const uint8_t*)ws, (uint16_t*)out, M, N, K, 1.0f};
-  hipError_t e = nvfp4::launch_mx_gemm(p, (hipStream_t)stream, info);
+  hipError_t e = nvfp4::launch_mx_gemm(p, (hipStream_t)stream, info, (nvfp4::MxElement)a_element,
+                                       (nvfp4::MxElement)w_element);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
@@ -508,6 +525,17 @@ int nvfp4_selftest_mxfp8_e4m3_exhaustive(unsigned long long* mismatches, uint32_
   if (s) return s;
   hipError_t e =
       nvfp4::launch_mx_selftest_e4m3_exhaustive(mismatches, first16, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
+int nvfp4_selftest_mxfp8_e5m2_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                         void* stream) {
+  if (!mismatches || !first16) return NVFP4_ERROR_INVALID_VALUE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e =
+      nvfp4::launch_mx_selftest_e5m2_exhaustive(mismatches, first16, (hipStream_t)stream);
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 

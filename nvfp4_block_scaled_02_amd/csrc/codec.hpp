@@ -49,6 +49,26 @@ NVFP4_HD uint32_t e4m3_encode_sat(float s) {
   return (b >> 20) - (120u << 3);
 }
 
+// Largest finite E5M2 value (1.75 * 2^15) and its code.
+constexpr float kE5M2Max = 57344.0f;
+constexpr uint32_t kE5M2MaxCode = 0x7B;
+
+// E5M2 code of the E5M2 value nearest to s (s >= 0, not NaN; +inf allowed), ties to
+// the even code, saturating at 57344 (0x7B).
+//  * s >= 57344: saturate.
+//  * s < 2^-14 (E5M2 subnormal range, spacing 2^-16): code = round-half-even(s * 2^16);
+//    the product is exact and code 4 is the smallest normal, so the rounding carries
+//    into the normal range seamlessly.
+//  * otherwise round the binary32 significand to 2 bits (half to even, at bit 21) and
+//    rebias the exponent from 127 to 15.
+NVFP4_HD uint32_t e5m2_encode_sat(float s) {
+  if (!(s < kE5M2Max)) return kE5M2MaxCode;
+  if (s < 0x1p-14f) return (uint32_t)__builtin_rintf(s * 65536.0f);
+  uint32_t b = f2u(s);
+  b += 0xFFFFFu + ((b >> 21) & 1u);
+  return (b >> 21) - (112u << 2);
+}
+
 // Exact value of a finite non-negative E4M3 code (0..0x7E), without relying on
 // denormal arithmetic: subnormal codes are m * 2^-9, normal codes shift into a
 // binary32 pattern with the exponent rebiased by +120.

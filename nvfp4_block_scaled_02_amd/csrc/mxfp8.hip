@@ -1,13 +1,15 @@
-// MXFP8 path for gfx950: quantize (bf16 -> E4M3 codes with one E8M0 scale per 32
-// elements) and a GEMM on gfx950's block-scaled MFMA.
+// MXFP8 path for gfx950: quantize (bf16 -> E4M3 or E5M2 codes with one E8M0 scale per
+// 32 elements) and a GEMM on gfx950's block-scaled MFMA.
 //
 // MXFP8 is the second microscaling format the zubnet.ai page measures (paragraph 1): the
 // Open Compute Project standard, 8-bit E4M3/E5M2 elements in 32-element blocks sharing
-// one scale. This library takes E4M3 elements and the OCP E8M0 scale (a power of two,
-// 2^(byte - 127)); the shared exponent of a block is floor(log2(amax)) - 8 (8 being the
-// exponent of E4M3's largest normal, 448), clamped to [-127, 127], an all-zero block
-// taking byte 0; elements are the E4M3 value nearest to x / 2^e, ties to even,
-// saturating at 448, sign copied.
+// one scale. This library takes either element type with the OCP E8M0 scale (a power of
+// two, 2^(byte - 127)); the shared exponent of a block is floor(log2(amax)) - emax (emax
+// the exponent of the element type's largest normal: 8 for E4M3's 448, 15 for E5M2's
+// 57344), clamped to [-127, 127], an all-zero block taking byte 0; elements are the
+// value of the element type nearest to x / 2^e, ties to even, saturating at its largest
+// finite value, sign copied. The GEMM takes each operand's element type separately (the
+// MFMA's operand format fields).
 //
 // Unlike NVFP4's E4M3-per-16 scales, these power-of-two per-32 scales are exactly what
 // v_mfma_scale_f32_32x32x64_f8f6f4 applies, so the GEMM needs no decode: the fp8 codes go
@@ -30,18 +32,35 @@ __device__ __forceinline__ void mx_unpack_bf16x8(const u32x4 v, float* f) {
   }
 }
 
-// x / 2^e clamped to [-448, 448] (sign of zero kept): the conversion below then never
-// overflows, and the clamp is the format's saturation.
+// x / 2^e clamped to the element type's finite range, [-448, 448] or [-57344, 57344]
+// (sign of zero kept): the conversion below then never overflows, and the clamp is the
+// format's saturation.
+template <bool kE5M2>
 __device__ __forceinline__ float mx_scaled(float x, int e) {
-  return __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(x, -e), -kE4M3Max), kE4M3Max);
+  constexpr float lim = kE5M2 ? kE5M2Max : kE4M3Max;
+  return __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(x, -e), -lim), lim);
 }
 
-// Shared exponent of a block from its amax (>= 0): floor(log2(amax)) - 8 from the
-// binary32 exponent field, clamped to [-127, 127]; zero and binary32-subnormal maxima
-// (floor(log2) <= -127) give -127.
+// Shared exponent of a block from its amax (>= 0): floor(log2(amax)) - emax (8 for E4M3,
+// 15 for E5M2) from the binary32 exponent field, clamped to [-127, 127]; zero and
+// binary32-subnormal maxima (floor(log2) <= -127) give -127.
+template <bool kE5M2>
 __device__ __forceinline__ int mx_shared_exponent(float amax) {
   const int eb = (int)(f2u(amax) >> 23);
-  return eb == 0 ? -127 : max(eb - 135, -127);
+  return eb == 0 ? -127 : max(eb - (kE5M2 ? 142 : 135), -127);
+}
+
+// Four elements y0..y3 (already scaled and clamped) into the element type's bytes
+// 0..3 of a word (round to nearest even).
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t mx_convert4(float y0, float y1, float y2, float y3) {
+  if constexpr (kE5M2) {
+    const uint32_t w = __builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
+    return __builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, w, true);
+  } else {
+    const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+  }
 }
 
 // ---- quantize ----------------------------------------------------------------------
@@ -52,7 +71,7 @@ __device__ __forceinline__ int mx_shared_exponent(float amax) {
 // quad (two DPP lane swaps), each lane converts its 8 elements with the gfx950 fp8
 // conversion (round to nearest even; checked exhaustively against a software encoder by
 // the self-test) and stores 8 code bytes; lane 4i writes the scale byte.
-template <int UNROLL>
+template <int UNROLL, bool kE5M2>
 __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restrict__ x,
                                                           u32x2* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
@@ -77,11 +96,11 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
       // quad maximum: lanes 4i..4i+3 (DPP quad_perm [1,0,3,2], then [2,3,0,1])
       a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));
       a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false)));
-      const int e = mx_shared_exponent(a);
-      uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(f[0], e), mx_scaled(f[1], e), 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(f[2], e), mx_scaled(f[3], e), w0, true);
-      uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(f[4], e), mx_scaled(f[5], e), 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(f[6], e), mx_scaled(f[7], e), w1, true);
+      const int e = mx_shared_exponent<kE5M2>(a);
+      const uint32_t w0 = mx_convert4<kE5M2>(mx_scaled<kE5M2>(f[0], e), mx_scaled<kE5M2>(f[1], e),
+                                             mx_scaled<kE5M2>(f[2], e), mx_scaled<kE5M2>(f[3], e));
+      const uint32_t w1 = mx_convert4<kE5M2>(mx_scaled<kE5M2>(f[4], e), mx_scaled<kE5M2>(f[5], e),
+                                             mx_scaled<kE5M2>(f[6], e), mx_scaled<kE5M2>(f[7], e));
       if (li < nlanes) {
         __builtin_nontemporal_store(u32x2{w0, w1}, &codes[li]);
         if ((li & 3) == 0) scales[li >> 2] = (uint8_t)(e + 127);
@@ -94,7 +113,9 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const u32x4* __restric
 //
 // out[M, N] (bf16) = A_hat[M, K] W_hat[N, K]^T, A and W MXFP8. 256 x 256 tiles, 2 x 2
 // waves of 128 x 128 (4 x 4 blocks of 32 x 32), v_mfma_scale_f32_32x32x64_f8f6f4 with
-// weights as the A operand.
+// weights as the A operand. kFw and kFx are that MFMA's operand format codes for the
+// weights (its A operand) and the activations (its B operand): 0 for E4M3, 1 for E5M2;
+// both 8-bit types share the operand layout below.
 //
 // Operand layout of that MFMA (measured on the device): over a 64-element K step, lane
 // (h, r) = (lane / 32, lane % 32) of an operand fragment holds row r's elements
@@ -136,7 +157,7 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 // Kernels table row: E4M3 operands with one fp32 scale per row). The per-row scales leave
 // the K-sum, so the MFMA runs with unit block scales (E8M0 127, no scale loads) and the
 // epilogue multiplies each output by a_scales[m] * w_scales[n] (fp32 arrays).
-template <int BM, int BN, bool kRowwise>
+template <int BM, int BN, bool kRowwise, int kFw, int kFx>
 __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
   constexpr int NW = 4, WM = 2, WN = 2;
   __shared__ MxSmem<BM, BN> sm;
@@ -282,7 +303,7 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
     for (int q = 0; q < kMfma; ++q) {
       const int i = q / FM, g = q % FM;
       acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+          wf[cur][i], xf[cur][g], acc[i][g], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
           kRowwise ? 127 : xsc[cur][g]);
       if (q < kLoads) issue_codes(q, lstage, lbuf);
       else if (q < kLoads + kSLoads && sload) issue_scales(q - kLoads, sgrp, ((t >> 3) + 1) & 1);
@@ -338,7 +359,7 @@ struct alignas(16) MxFitSmem {
 };
 
 // One wave's program; kS = number of middle-group blocks this wave owns (2 or 1).
-template <int BM, int BN, bool kRowwise, int kS>
+template <int BM, int BN, bool kRowwise, int kS, int kFw, int kFx>
 __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, BN>& sm, int lane,
                                             int wave, int m0, int n0) {
   constexpr int NW = 4;
@@ -468,12 +489,12 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
       if (q < FN * FM) {
         const int i = q / FM, g = q % FM;
         acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+            wf[cur][i], xf[cur][g], acc[i][g], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
             kRowwise ? 127 : xsc[cur][g]);
       } else {
         const int sidx = q - FN * FM, i = kI0 + sidx;
         accs[sidx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[cur][i], xf[cur][FM], accs[sidx], 0, 0, 0, kRowwise ? 127 : wsc[cur][i], 0,
+            wf[cur][i], xf[cur][FM], accs[sidx], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
             kRowwise ? 127 : xsc[cur][FM]);
       }
       if (q < kLoads) issue_codes(q, lstage, lbuf);
@@ -508,7 +529,7 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
                                   (int64_t)m0 + GS * 32, n_base + kI0 * 32, lane, blk);
 }
 
-template <int BM, int BN, bool kRowwise>
+template <int BM, int BN, bool kRowwise, int kFw, int kFx>
 __global__ void __launch_bounds__(256) gemm_mx_fit_kernel(GemmProblem p) {
   __shared__ MxFitSmem<BM, BN> sm;
   const int lane = threadIdx.x & 63;
@@ -518,8 +539,10 @@ __global__ void __launch_bounds__(256) gemm_mx_fit_kernel(GemmProblem p) {
   int tile_m, tile_n;
   tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   constexpr int FN = BN / 64;
-  if ((wave >> 1) == 0) mx_fit_wave<BM, BN, kRowwise, FN - 1>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
-  else mx_fit_wave<BM, BN, kRowwise, 1>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
+  if ((wave >> 1) == 0)
+    mx_fit_wave<BM, BN, kRowwise, FN - 1, kFw, kFx>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
+  else
+    mx_fit_wave<BM, BN, kRowwise, 1, kFw, kFx>(p, sm, lane, wave, tile_m * BM, tile_n * BN);
 }
 
 // ---- self-test: the fp8 conversion against the software E4M3 encoder ----------------
@@ -544,18 +567,41 @@ __global__ void mx_selftest_e4m3_exhaustive_kernel(unsigned long long* __restric
   }
 }
 
+// The same for the bf8 conversion against the software E5M2 encoder (clamp to
+// [-57344, 57344], nearest, ties to even, saturating at 57344).
+__global__ void mx_selftest_e5m2_exhaustive_kernel(unsigned long long* __restrict__ count,
+                                                   uint32_t* __restrict__ first) {
+  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t nthreads = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t u = tid; u < (1ull << 32); u += nthreads) {
+    const uint32_t bits = (uint32_t)u;
+    if (((bits >> 23) & 0xFFu) == 0xFFu) continue;
+    const float y = __builtin_fminf(__builtin_fmaxf(u2f(bits), -kE5M2Max), kE5M2Max);
+    const uint32_t hw = __builtin_amdgcn_cvt_pk_bf8_f32(y, 0.0f, 0, false) & 0xFFu;
+    const uint32_t sw = ((bits >> 31) << 7) | e5m2_encode_sat(__builtin_fabsf(y));
+    if (hw != sw) {
+      const unsigned long long k = atomicAdd(count, 1ull);
+      if (k < 16) first[k] = bits;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* codes, void* scales,
-                              hipStream_t stream, const LaunchInfo& dev) {
+                              hipStream_t stream, const LaunchInfo& dev, MxElement elem) {
   const int64_t nlanes = M * K / 8;
   if (nlanes == 0) return hipSuccess;
   constexpr int kThreads = 256, kUnroll = 2;
   const int64_t want = (nlanes + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   const int64_t cap = (int64_t)dev.num_cus * 32;
   const int grid = (int)(want < cap ? want : cap);
-  hipLaunchKernelGGL((mx_quantize_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const u32x4*)x, (u32x2*)codes, (uint8_t*)scales, nlanes);
+  if (elem == MxElement::kE5M2)
+    hipLaunchKernelGGL((mx_quantize_kernel<kUnroll, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       (const u32x4*)x, (u32x2*)codes, (uint8_t*)scales, nlanes);
+  else
+    hipLaunchKernelGGL((mx_quantize_kernel<kUnroll, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       (const u32x4*)x, (u32x2*)codes, (uint8_t*)scales, nlanes);
   return hipGetLastError();
 }
 
@@ -563,7 +609,7 @@ namespace {
 
 // 288 x 192 or 256 x 256 tiles: the fit tile issues 14 MFMAs per wave and stage (the
 // other 16), so it wins unless it needs more passes over the compute units.
-template <bool kRowwise>
+template <bool kRowwise, int kFw, int kFx>
 hipError_t launch_fp8_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
   const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
   const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
@@ -572,11 +618,11 @@ hipError_t launch_fp8_gemm(const GemmProblem& p, hipStream_t stream, const Launc
   const int64_t pass256 = (t256 + cus - 1) / cus, passfit = (tfit + cus - 1) / cus;
   if (fit32 && passfit * 14 <= pass256 * 16) {
     if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_mx_fit_kernel<288, 192, kRowwise>), dim3((unsigned)tfit), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_mx_fit_kernel<288, 192, kRowwise, kFw, kFx>), dim3((unsigned)tfit), dim3(256), 0,
                        stream, p);
   } else {
     if (t256 > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_mx_kernel<256, 256, kRowwise>), dim3((unsigned)t256), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_mx_kernel<256, 256, kRowwise, kFw, kFx>), dim3((unsigned)t256), dim3(256), 0,
                        stream, p);
   }
   return hipGetLastError();
@@ -584,17 +630,29 @@ hipError_t launch_fp8_gemm(const GemmProblem& p, hipStream_t stream, const Launc
 
 }  // namespace
 
-hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  return launch_fp8_gemm<false>(p, stream, dev);
+hipError_t launch_mx_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev,
+                          MxElement a_elem, MxElement w_elem) {
+  const bool a5 = a_elem == MxElement::kE5M2, w5 = w_elem == MxElement::kE5M2;
+  if (w5 && a5) return launch_fp8_gemm<false, 1, 1>(p, stream, dev);
+  if (w5) return launch_fp8_gemm<false, 1, 0>(p, stream, dev);
+  if (a5) return launch_fp8_gemm<false, 0, 1>(p, stream, dev);
+  return launch_fp8_gemm<false, 0, 0>(p, stream, dev);
 }
 
 hipError_t launch_fp8r_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInfo& dev) {
-  return launch_fp8_gemm<true>(p, stream, dev);
+  return launch_fp8_gemm<true, 0, 0>(p, stream, dev);
 }
 
 hipError_t launch_mx_selftest_e4m3_exhaustive(unsigned long long* count, uint32_t* first,
                                               hipStream_t stream) {
   hipLaunchKernelGGL(mx_selftest_e4m3_exhaustive_kernel, dim3(8192), dim3(256), 0, stream, count,
+                     first);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_selftest_e5m2_exhaustive(unsigned long long* count, uint32_t* first,
+                                              hipStream_t stream) {
+  hipLaunchKernelGGL(mx_selftest_e5m2_exhaustive_kernel, dim3(8192), dim3(256), 0, stream, count,
                      first);
   return hipGetLastError();
 }

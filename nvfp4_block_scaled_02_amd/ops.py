@@ -132,9 +132,19 @@ def gemm_w4a16(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
     return out
 
 
+_MX_ELEMENTS = {"e4m3": 0, "e5m2": 1}
+
+
+def _mx_element(elem: str) -> int:
+    if elem not in _MX_ELEMENTS:
+        raise ValueError(f"MXFP8 element type must be one of {sorted(_MX_ELEMENTS)}, not {elem!r}")
+    return _MX_ELEMENTS[elem]
+
+
 def mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor | None = None,
-                   scales: torch.Tensor | None = None, stream=None):
-    """MXFP8 quantization: bf16 [M, K] -> E4M3 codes uint8 [M, K] + E8M0 scales [M, K/32]."""
+                   scales: torch.Tensor | None = None, stream=None, elem: str = "e4m3"):
+    """MXFP8 quantization: bf16 [M, K] -> E4M3 or E5M2 codes uint8 [M, K] + E8M0 scales
+    [M, K/32]."""
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
     if codes is None:
@@ -146,14 +156,16 @@ def mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor | None = None,
     if tuple(codes.shape) != (M, K) or tuple(scales.shape) != (M, K // 32):
         raise ValueError("codes must be [M, K] and scales [M, K/32]")
     lib = load_library()
-    check(lib.nvfp4_mxfp8_quantize(_ptr(x), M, K, _ptr(codes), _ptr(scales), _stream(stream)),
-          "nvfp4_mxfp8_quantize")
+    check(lib.nvfp4_mxfp8_quantize_elem(_ptr(x), M, K, _mx_element(elem), _ptr(codes), _ptr(scales),
+                                        _stream(stream)), "nvfp4_mxfp8_quantize_elem")
     return codes, scales
 
 
 def mxfp8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
-               w_scales: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """MXFP8 GEMM: bf16 [M, N] = A_hat @ W_hat^T on the block-scaled fp8 MFMA."""
+               w_scales: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+               a_elem: str = "e4m3", w_elem: str = "e4m3") -> torch.Tensor:
+    """MXFP8 GEMM: bf16 [M, N] = A_hat @ W_hat^T on the block-scaled fp8 MFMA (each operand
+    E4M3 or E5M2)."""
     for t, n in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"),
                  (w_scales, "w_scales")):
         _need(t, n, torch.uint8, 2)
@@ -168,8 +180,9 @@ def mxfp8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Ten
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape must be [M, N]")
     lib = load_library()
-    check(lib.nvfp4_mxfp8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
-                               M, N, K, _ptr(out), _stream(stream)), "nvfp4_mxfp8_gemm")
+    check(lib.nvfp4_mxfp8_gemm_elem(_ptr(a_codes), _ptr(a_scales), _mx_element(a_elem), _ptr(w_codes),
+                                    _ptr(w_scales), _mx_element(w_elem), M, N, K, _ptr(out),
+                                    _stream(stream)), "nvfp4_mxfp8_gemm_elem")
     return out
 
 

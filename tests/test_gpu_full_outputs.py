@@ -112,17 +112,18 @@ def test_w4a16_flagship_every_output_element():
 
 
 @pytest.mark.timeout(600)
-def test_mxfp8_flagship_every_output_element():
+@pytest.mark.parametrize("a_elem,w_elem", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e5m2", "e4m3")])
+def test_mxfp8_flagship_every_output_element(a_elem, w_elem):
     wl, d = _flagship()
-    ac, as_ = MX.quantize(d["x"])
-    wc, ws = MX.quantize(d["w"])
-    say("full-output mxfp8 attn_out")
-    acd, asd = nv.mxfp8_quantize(bf16_to_dev(d["x"]))
+    ac, as_ = MX.quantize(d["x"], elem=a_elem)
+    wc, ws = MX.quantize(d["w"], elem=w_elem)
+    say("full-output mxfp8 attn_out", a_elem, w_elem)
+    acd, asd = nv.mxfp8_quantize(bf16_to_dev(d["x"]), elem=a_elem)
     assert np.array_equal(to_host(acd), ac) and np.array_equal(to_host(asd), as_)
-    got = to_host(nv.mxfp8_gemm(acd, asd, u8_to_dev(wc), u8_to_dev(ws)))
+    got = to_host(nv.mxfp8_gemm(acd, asd, u8_to_dev(wc), u8_to_dev(ws), a_elem=a_elem, w_elem=w_elem))
     for r0 in range(0, wl.M, CHUNK):
         r1 = min(wl.M, r0 + CHUNK)
-        ref, absref = MX.gemm_ref(ac[r0:r1], as_[r0:r1], wc, ws)
+        ref, absref = MX.gemm_ref(ac[r0:r1], as_[r0:r1], wc, ws, a_elem=a_elem, w_elem=w_elem)
         ok, worst, nbad = O.check_gemm(got[r0:r1], ref, absref)
         assert ok, f"rows {r0}:{r1}: {nbad} out of tolerance (worst {worst:.3g})"
 

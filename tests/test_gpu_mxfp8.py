@@ -141,3 +141,96 @@ def test_gemm_workloads_sampled_rows(name):
     assert good, f"{name}: {nbad} out of tolerance (worst {worst:.3g})"
     out2, _ = _gemm_dev(ac, as_, wc, ws, guard=False)
     assert np.array_equal(to_host(out2), got)
+
+
+# ---- E5M2 elements ------------------------------------------------------------------
+
+
+def test_e5m2_conversion_exhaustive():
+    """gfx950's bf8 conversion equals the software E5M2 encoder on every binary32 pattern
+    (clamped to +-57344 as the quantizer does)."""
+    import ctypes
+
+    lib = nv.load_library()
+    count = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.zeros(16, dtype=torch.int32, device="cuda")
+    say("mxfp8 e5m2 exhaustive")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.nvfp4_selftest_mxfp8_e5m2_exhaustive(
+        ctypes.c_void_p(count.data_ptr()), ctypes.c_void_p(first.data_ptr()), st) == 0
+    n = int(to_host(count)[0])
+    assert n == 0, f"{n} mismatches, first {[hex(int(v) & 0xFFFFFFFF) for v in to_host(first)[:min(n, 16)]]}"
+
+
+def _check_quantize_e5m2(x_bits, label):
+    codes, scales = nv.mxfp8_quantize(bf16_to_dev(x_bits), elem="e5m2")
+    wc, ws = MX.quantize(x_bits, elem="e5m2")
+    gc, gs = to_host(codes), to_host(scales)
+    assert np.array_equal(gs, ws), f"{label}: {np.count_nonzero(gs != ws)} scale bytes differ"
+    assert np.array_equal(gc, wc), f"{label}: {np.count_nonzero(gc != wc)} code bytes differ"
+
+
+@pytest.mark.parametrize("name", ["tiny", "attn_out", "qkv", "mlp_down", "odd_m1", "odd_m1000"])
+def test_quantize_e5m2_workloads_bit_exact(name):
+    wl = make(name)
+    d = wl.generate()
+    say("mxfp8 e5m2 quantize", name)
+    _check_quantize_e5m2(d["x"], name + "/x")
+    _check_quantize_e5m2(d["w"], name + "/w")
+
+
+def test_quantize_e5m2_adversarial():
+    rng = np.random.default_rng(61)
+    M, K = 37, 544
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp(rng.uniform(-20, 20, (M, 1))).astype(np.float32)
+    x[0, :64] = 0.0
+    x[1, :32] = -0.0
+    x[2, :32] = np.float32(2.0**-133)     # bf16 subnormal amax -> clamped exponent
+    x[3, :32] = np.float32(3.3e38)
+    x[4, :32] = np.float32(-3.3e38)
+    # ties at e = 0 (block max 57344): 1.125, 1.375, 3 * 2^-17, 30720
+    x[5, :32] = 0.0
+    x[5, 0] = 57344.0
+    x[5, 1:5] = [1.125, 1.375, 3 * 2.0**-17, 30720.0]
+    x[6, :32] = rng.standard_normal(32).astype(np.float32) * 2.0**-130
+    x[7, :32] = 0.0
+    x[7, 0] = 61000.0                     # e = 0, saturates to 57344
+    x[7, 1] = -60000.0
+    xb = to_bf16_bits(x)
+    say("mxfp8 e5m2 quantize adversarial")
+    _check_quantize_e5m2(xb, "adversarial")
+
+
+@pytest.mark.parametrize("a_elem,w_elem", [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
+@pytest.mark.parametrize("M,N,K", [(64, 128, 256), (17, 72, 128), (300, 520, 384), (600, 400, 1152),
+                                   (289, 193, 640), (4096, 4096, 128)])
+def test_gemm_mixed_elements_in_full(a_elem, w_elem, M, N, K):
+    """Each operand's element type reaches the MFMA's operand format: every output within
+    the bound, on the 288 x 192 and 256 x 256 kernels (4096 x 4096 takes the latter)."""
+    rng = np.random.default_rng(M * 13 + N * 3 + K)
+    x = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    ac, as_ = MX.quantize(x, elem=a_elem)
+    wc, ws = MX.quantize(w, elem=w_elem)
+    say("mxfp8 gemm", a_elem, w_elem, M, N, K)
+    out, ok = guarded((M, N), torch.bfloat16)
+    nv.mxfp8_gemm(u8_to_dev(ac), u8_to_dev(as_), u8_to_dev(wc), u8_to_dev(ws), out=out,
+                  a_elem=a_elem, w_elem=w_elem)
+    got = to_host(out)
+    assert ok(), "write outside out"
+    ref, absref = MX.gemm_ref(ac, as_, wc, ws, a_elem=a_elem, w_elem=w_elem)
+    good, worst, nbad = O.check_gemm(got, ref, absref)
+    assert good, f"{nbad} out of tolerance (worst {worst:.3g})"
+
+
+def test_element_type_is_validated():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        nv.mxfp8_quantize(x, elem="e3m4")
+    import ctypes
+
+    lib = nv.load_library()
+    c = torch.zeros((4, 64), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    assert lib.nvfp4_mxfp8_quantize_elem(P(x), 4, 64, 2, P(c), P(s), None) == 1
