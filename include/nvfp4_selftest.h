@@ -54,6 +54,13 @@ int nvfp4_selftest_mxfp8_e4m3_exhaustive(unsigned long long* mismatches, uint32_
 int nvfp4_selftest_mxfp8_e5m2_exhaustive(unsigned long long* mismatches, uint32_t* first16,
                                          void* stream);
 
+/* The GEMM epilogues' packed fp32 -> bf16 conversion (gfx950 v_cvt_pk_bf16_f32) against
+ * round-to-nearest-even on the bit pattern, for every binary32 pattern except NaN (each in
+ * both halves of the instruction): adds the mismatch count to *mismatches (device,
+ * starts at 0); up to 16 offending patterns land in first16 (device, 16 entries). */
+int nvfp4_selftest_bf16_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                   void* stream);
+
 /* The GEMM's operand decode: packed[nbytes] holds 2*nbytes E2M1 codes (low nibble
  * first); scales[nbytes / 4] holds one E4M3 code per 4 packed bytes. Writes 2*nbytes
  * f16 bit patterns of code value * scale to hw_f16 (conversion-instruction decode) and

@@ -60,6 +60,7 @@ SIGNATURES = {
     "nvfp4_selftest_e2m1_encode": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "nvfp4_selftest_e2m1_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_division": (_int, [_vp, _vp, _vp]),
+    "nvfp4_selftest_bf16_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_mxfp8_e4m3_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_mxfp8_e5m2_exhaustive": (_int, [_vp, _vp, _vp]),
     "nvfp4_selftest_block_scale": (_int, [_vp, _f32, _vp, _vp, _i64, _vp]),

@@ -539,6 +539,16 @@ int nvfp4_selftest_mxfp8_e5m2_exhaustive(unsigned long long* mismatches, uint32_
   return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
 }
 
+int nvfp4_selftest_bf16_exhaustive(unsigned long long* mismatches, uint32_t* first16,
+                                   void* stream) {
+  if (!mismatches || !first16) return NVFP4_ERROR_INVALID_VALUE;
+  nvfp4::LaunchInfo info;
+  int s = current_device(&info);
+  if (s) return s;
+  hipError_t e = nvfp4::launch_selftest_bf16_exhaustive(mismatches, first16, (hipStream_t)stream);
+  return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
+}
+
 int nvfp4_selftest_division(unsigned long long* mismatches, uint32_t* first16, void* stream) {
   if (!mismatches || !first16) return NVFP4_ERROR_INVALID_VALUE;
   nvfp4::LaunchInfo info;

@@ -999,21 +999,22 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int64_t n = (int64_t)n0 + i * 32 + 8 * q + 4 * h;
-            uint32_t b[4];
+            float sv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int v = 4 * q + e;
               float s = rb[v * 64 + lane];
 #pragma unroll
               for (int w = 1; w < NW; ++w) s += rb[(w * 16 + v) * 64 + lane];
-              b[e] = bf16_rne(apply_alpha<kExp>(s, alpha));
+              sv[e] = apply_alpha<kExp>(s, alpha);
             }
+            const u32x2 b = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
             if (n_vec && n + 3 < p.N) {
-              *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+              *(u32x2*)&orow[n] = b;
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+                if (n + e < p.N) orow[n + e] = (uint16_t)(b[e >> 1] >> (16 * (e & 1)));
             }
           }
         }
@@ -1063,6 +1064,27 @@ __global__ void selftest_decode_kernel(const uint8_t* __restrict__ packed,
   // version folds per-element reads of the fp4->f16 conversion result to its low
   // element, so no element is extracted here. nbytes is a multiple of 4.
   *(u32x4*)&out[i * 8] = __builtin_bit_cast(u32x4, v);
+}
+
+// The epilogues' packed fp32 -> bf16 conversion against the bit-pattern rounding on
+// every binary32 pattern except NaN: pattern u in the low half, u ^ 0x00010000 (its
+// neighbour two bf16 ulps away in the other rounding direction's parity) in the high
+// half, so both halves of the instruction see every pattern.
+__global__ void selftest_bf16_exhaustive_kernel(unsigned long long* __restrict__ count,
+                                                uint32_t* __restrict__ first) {
+  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t nthreads = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t u = tid; u < (1ull << 32); u += nthreads) {
+    const uint32_t lo = (uint32_t)u, hi = lo ^ 0x00010000u;
+    const float a = u2f(lo), b = u2f(hi);
+    if (a != a || b != b) continue;
+    const uint32_t hw = bf16x2_rne(a, b);
+    const uint32_t sw = bf16_rne(a) | (bf16_rne(b) << 16);
+    if (hw != sw) {
+      const unsigned long long k = atomicAdd(count, 1ull);
+      if (k < 16) first[k] = lo;
+    }
+  }
 }
 
 // Rough cost model (core cycles of one launch) used to choose between the kernels; the
@@ -1260,6 +1282,13 @@ hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipSt
     launch_splitk_kernel<1, 1, 4, 4, true, true>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
   else
     launch_splitk_kernel<1, 1, 4, 4, true, false>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_bf16_exhaustive(unsigned long long* count, uint32_t* first,
+                                           hipStream_t stream) {
+  hipLaunchKernelGGL(selftest_bf16_exhaustive_kernel, dim3(8192), dim3(256), 0, stream, count,
+                     first);
   return hipGetLastError();
 }
 

@@ -62,9 +62,25 @@ __device__ __forceinline__ half8_t decode8(uint32_t p, half2_t s2) {
   return r;
 }
 
+// fp32 -> bf16, round to nearest even, on the bit pattern (the reference the hardware
+// conversion below is checked against).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t b = f2u(f);
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even bf16 by gfx950's packed conversion
+// (v_cvt_pk_bf16_f32; a in the low half): one instruction where bf16_rne takes four
+// integer operations per value. Equal to bf16_rne on every non-NaN binary32 pattern
+// (nvfp4_selftest_bf16_exhaustive).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ u32x2 bf16x4_rne(float a, float b, float c, float d) {
+  return u32x2{bf16x2_rne(a, b), bf16x2_rne(c, d)};
 }
 
 // Raw buffer resource over n bytes at p (gfx9-family descriptor word 3: 32-bit data
@@ -178,15 +194,16 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FN][FM], const 
       for (int q = 0; q < 4; ++q) {
         if (q < q0 || q >= q1) continue;
         const int64_t n = n_base + i * 32 + 8 * q + 4 * h;
-        uint32_t b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = bf16_rne(apply_alpha<kExp>(acc[i][g][4 * q + e], alpha));
+        const u32x2 w = bf16x4_rne(apply_alpha<kExp>(acc[i][g][4 * q], alpha),
+                                   apply_alpha<kExp>(acc[i][g][4 * q + 1], alpha),
+                                   apply_alpha<kExp>(acc[i][g][4 * q + 2], alpha),
+                                   apply_alpha<kExp>(acc[i][g][4 * q + 3], alpha));
         if (n_vec && n + 3 < p.N) {
-          *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+          *(u32x2*)&orow[n] = w;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+            if (n + e < p.N) orow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
@@ -243,13 +260,13 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[FN][FM], co
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
+        float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if constexpr (kRowCol) b[e] = bf16_rne(acc[i][g][4 * q + e] * sx[g] * u2f(sw[i][q][e]));
-          else b[e] = bf16_rne(apply_alpha<kExp>(acc[i][g][4 * q + e], alpha));
+          if constexpr (kRowCol) v[e] = acc[i][g][4 * q + e] * sx[g] * u2f(sw[i][q][e]);
+          else v[e] = apply_alpha<kExp>(acc[i][g][4 * q + e], alpha);
         }
-        *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        *(u32x2*)&blk[r32 * RS + i * 32 + 8 * q + 4 * h] = bf16x4_rne(v[0], v[1], v[2], v[3]);
       }
     const int64_t m_row = m_base + g * 32;
 #pragma unroll

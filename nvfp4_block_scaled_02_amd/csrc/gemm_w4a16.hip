@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int64_t n = n0 + 8 * qd + 4 * h;
-          uint32_t b[4];
+          float sv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * qd + e;
@@ -167,14 +167,15 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
             s += rb[(1 * 16 + v) * 64 + lane];
             s += rb[(2 * 16 + v) * 64 + lane];
             s += rb[(3 * 16 + v) * 64 + lane];
-            b[e] = bf16_rne(s * p.alpha);
+            sv[e] = s * p.alpha;
           }
+          const u32x2 b = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
           if (n_vec && n + 3 < p.N) {
-            *(u32x2*)&orow[n] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            *(u32x2*)&orow[n] = b;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) orow[n + e] = (uint16_t)b[e];
+              if (n + e < p.N) orow[n + e] = (uint16_t)(b[e >> 1] >> (16 * (e & 1)));
           }
         }
       }

@@ -124,6 +124,8 @@ hipError_t launch_selftest_division(unsigned long long* count, uint32_t* first,
                                     hipStream_t stream);
 hipError_t launch_selftest_scale(const float* amax, float gs, uint8_t* code, float* d, int64_t n,
                                  hipStream_t stream);
+hipError_t launch_selftest_bf16_exhaustive(unsigned long long* count, uint32_t* first,
+                                           hipStream_t stream);
 hipError_t launch_selftest_decode(const uint8_t* packed, const uint8_t* scales, uint16_t* hw,
                                   uint16_t* sw, int64_t nbytes, hipStream_t stream);
 

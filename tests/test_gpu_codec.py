@@ -134,3 +134,16 @@ def test_gemm_operand_decode_is_exact(lib, path):
             f"{path}: {bad.size} mismatches; {int(value_equal.sum())} differ only in the sign "
             f"of zero; by scale code (nonzero) {[(k, int(v)) for k, v in enumerate(by_scale) if v][:40]}; "
             f"by element code {by_code.tolist()}; first {detail}")
+
+
+def test_bf16_epilogue_conversion_exhaustive(lib):
+    """The GEMM epilogues round fp32 to bf16 with gfx950's packed conversion; it must
+    equal round-to-nearest-even on the bit pattern for every non-NaN binary32 value
+    (subnormals, overflow to infinity and ties included), in both halves."""
+    say("bf16 packed conversion exhaustive 2^32")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.zeros(16, dtype=torch.int32, device="cuda")
+    assert lib.nvfp4_selftest_bf16_exhaustive(_p(cnt), _p(first), _s()) == 0
+    n = int(to_host(cnt)[0])
+    bad = [hex(v & 0xFFFFFFFF) for v in to_host(first)[: min(n, 16)]]
+    assert n == 0, (n, bad)
