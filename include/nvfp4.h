@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 /* Status codes. All argument validation happens before any HIP call. */
 typedef enum nvfp4_status {
@@ -165,6 +165,23 @@ int nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel);
 int nvfp4_gemm_w4a16(const void* x_bf16, const void* w_packed, const void* w_scales,
                      float w_global_scale, int64_t M, int64_t N, int64_t K, void* out_bf16,
                      void* stream);
+
+/* Kernels nvfp4_gemm_w4a16 chooses among (reported by nvfp4_gemm_w4a16_plan). */
+typedef enum {
+  NVFP4_W4A16_SPLITK = 0,  /* K split over a workgroup's waves: short activations */
+  NVFP4_W4A16_FIT = 1,     /* 288 x 192 output tiles (K % 64 == 0) */
+  NVFP4_W4A16_TILE256 = 2, /* 256 x 256 output tiles (K % 64 == 0) */
+  NVFP4_W4A16_WIDE = 3     /* 224 x 256 output tiles with the waves side by side along N
+                              (K % 64 == 0): each weight group decoded once per tile */
+} nvfp4_w4a16_kernel;
+
+/*
+ * The kernel nvfp4_gemm_w4a16 launches for an M x N x K product on a device with num_cus
+ * compute units (<= 0: 256, an MI355X). Host only: no device call. Writes an
+ * nvfp4_w4a16_kernel value to *kernel; returns NVFP4_ERROR_INVALID_VALUE for a null
+ * kernel pointer and NVFP4_ERROR_INVALID_SHAPE for shapes nvfp4_gemm_w4a16 rejects.
+ */
+int nvfp4_gemm_w4a16_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel);
 
 /*
  * MXFP8 (OCP microscaling) path: the second microscaling format of the zubnet.ai page

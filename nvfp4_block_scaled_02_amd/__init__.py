@@ -6,6 +6,7 @@ Python entry points (thin wrappers over the C ABI in include/nvfp4.h):
 * :func:`gemm`      -- block-scaled W4A4 GEMM, bf16 output
 * :func:`linear`    -- fused quantize + GEMM through a workspace
 * :func:`gemm_plan` -- which GEMM kernel a shape runs on (host only)
+* :func:`gemm_w4a16_plan` -- the same for :func:`gemm_w4a16`
 * :func:`linear_plan` -- whether :func:`linear` runs a shape as one fused kernel
 * :func:`gemm_w4a16` -- NVFP4 weights x bf16 activations (not quantized), bf16 output
 * :func:`mxfp8_quantize`, :func:`mxfp8_gemm` -- the MXFP8 (OCP microscaling) path
@@ -24,6 +25,7 @@ from .ops import (  # noqa: F401
     gemm,
     gemm_plan,
     gemm_w4a16,
+    gemm_w4a16_plan,
     global_scale_from_amax,
     linear,
     linear_plan,

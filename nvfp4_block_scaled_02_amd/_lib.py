@@ -11,7 +11,7 @@ import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnvfp4.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {
     0: "NVFP4_SUCCESS",
@@ -40,6 +40,7 @@ SIGNATURES = {
     "nvfp4_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int)]),
     "nvfp4_linear_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int)]),
     "nvfp4_gemm_w4a16": (_int, [_vp, _vp, _vp, _f32, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_gemm_w4a16_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int)]),
     "nvfp4_mxfp8_quantize": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_mxfp8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "nvfp4_mxfp8_quantize_elem": (_int, [_vp, _i64, _i64, _int, _vp, _vp, _vp]),

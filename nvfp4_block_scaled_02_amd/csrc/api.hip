@@ -122,6 +122,17 @@ int validate_gemm(const void* ap, const void* as, float ags, const void* wp, con
   return NVFP4_SUCCESS;
 }
 
+// Shape rules of nvfp4_gemm_w4a16 (its status, 0 when accepted).
+int check_w4a16_shape(int64_t M, int64_t N, int64_t K) {
+  int s = check_shape(M, K);
+  if (s) return s;
+  s = check_shape(N, K);
+  if (s) return s;
+  if (K % 32 != 0 || K > ((int64_t)1 << 22)) return NVFP4_ERROR_INVALID_SHAPE;
+  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
+  return NVFP4_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,16 +204,20 @@ int nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel) {
   return NVFP4_SUCCESS;
 }
 
+int nvfp4_gemm_w4a16_plan(int64_t M, int64_t N, int64_t K, int num_cus, int* kernel) {
+  if (!kernel) return NVFP4_ERROR_INVALID_VALUE;
+  const int s = check_w4a16_shape(M, N, K);
+  if (s) return s;
+  *kernel = (int)nvfp4::plan_gemm_w4a16(M, N, K, num_cus, true);
+  return NVFP4_SUCCESS;
+}
+
 int nvfp4_gemm_w4a16(const void* x, const void* wp, const void* ws, float wgs, int64_t M,
                      int64_t N, int64_t K, void* out, void* stream) {
   if (!x || !wp || !ws || !out) return NVFP4_ERROR_INVALID_VALUE;
   if (!valid_scale(wgs)) return NVFP4_ERROR_INVALID_VALUE;
-  int s = check_shape(M, K);
+  int s = check_w4a16_shape(M, N, K);
   if (s) return s;
-  s = check_shape(N, K);
-  if (s) return s;
-  if (K % 32 != 0 || K > ((int64_t)1 << 22)) return NVFP4_ERROR_INVALID_SHAPE;
-  if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
   if (!aligned(x, 16) || !aligned(wp, 16) || !aligned(out, 16) || !aligned(ws, 4))
     return NVFP4_ERROR_MISALIGNED;
   if (M == 0 || N == 0) return NVFP4_SUCCESS;

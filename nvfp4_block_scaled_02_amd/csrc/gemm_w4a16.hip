@@ -509,26 +509,260 @@ __global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
                          (int64_t)m0 + GS * 32, n_base + 64, lane, stage_area);
 }
 
+// ---- 224 x 256 tiles, waves side by side along N ----------------------------------------
+//
+// Each wave owns 64 weight rows (two groups) and all 224 activation rows (seven groups):
+// 14 MFMAs per k-step as in the 288 x 192 tile, but every weight group is decoded by one
+// wave only (the 2 x 2 layouts decode each weight group in both wave rows), and a stage
+// moves 224 x 128 + 256 x 36 bytes for 224 x 256 outputs instead of 288 x 128 + 192 x 36
+// for 288 x 192 (13% fewer bytes per product). Four stage buffers of 37 KiB; stage t+3's
+// loads are issued during stage t, and the end of stage t waits for the loads issued
+// before stage t-1, so two stages of loads stay in flight across the barrier. 4608 rows
+// make 21 tile rows (the last one 128 rows); every FLUX width is a multiple of 256.
+template <int BM, int BN>
+struct alignas(16) W4A16WideSmem {
+  uint8_t x[4][BM * 128];
+  uint8_t w[4][BN * 32];
+  uint8_t ws[4][BN * 4];
+};
+
+#ifndef NVFP4_W4A16_VALU_PER_MFMA
+#define NVFP4_W4A16_VALU_PER_MFMA 4
+#endif
+
+// Wait until at most n of this wave's vector memory operations are outstanding (n < 64:
+// the counter's low four bits and its two high bits at 15:14).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt_wide() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+// Requires K % 64 == 0, 16-byte aligned x, codes and out, 4-byte aligned scales, and
+// (M + BM) * K * 2 and (N + BN) * K / 2 below 2^31 (32-bit buffer offsets). The grid is
+// the tile count rounded up to a multiple of 8; workgroups past the last tile exit.
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
+  constexpr int NW = 4;
+  __shared__ W4A16WideSmem<BM, BN> sm;
+  constexpr int FM = BM / 32, FN = BN / NW / 32;
+  constexpr int kPx = BM / 8, kPw = BN / 32, kPs = BN / 64;  // loads per stage
+  static_assert(FM * 32 == BM && FN * 32 * NW == BN, "tile shape");
+  static_assert(kPx % NW == 0 && kPw % NW == 0 && kPs % NW == 0, "loads divide among waves");
+  constexpr int kPxW = kPx / NW, kPwW = kPw / NW, kPsW = kPs / NW;
+  constexpr int kLoads = kPxW + kPwW + kPsW;
+  constexpr int kPerStep = (kLoads + 3) / 4;  // loads issued per k-step
+  static_assert(2 * kLoads < 64, "two stages of loads fit the vmcnt counter");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  // tile_order on the tile count rounded up to a multiple of 8 (the XCD count); the
+  // slots past the last tile own nothing
+  const int T = tiles_m * tiles_n;
+  const int Tp = (T + 7) & ~7;
+  const int b = (int)blockIdx.x;
+  const int q = (b % 8) * (Tp / 8) + b / 8;
+  if (q >= T) return;
+  int tile_m, tile_n;
+  {
+    constexpr int G = NVFP4_GEMM_XCD_GROUP > 0 ? NVFP4_GEMM_XCD_GROUP : 1;
+    const int per_group = G * tiles_n;
+    const int gm0 = (q / per_group) * G;
+    const int rows = min(tiles_m - gm0, G);
+    const int r = q % per_group;
+    tile_m = gm0 + r % rows;
+    tile_n = r / rows;
+  }
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int nk = (int)(p.K / 64);
+  const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
+
+  // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
+  const __amdgpu_buffer_rsrc_t rx = window_rsrc(p.x, m0, p.M, xpitch);
+  const __amdgpu_buffer_rsrc_t rw = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rs = window_rsrc(p.w_scales, n0, p.N, spitch);
+
+  // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
+  auto issue = [&](int j, int stage, int buf) {
+    if (j < kPxW) {
+      const int i = j * NW + wave;  // rows 8i .. 8i+7 of the tile
+      buffer_load_lds16(rx, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, xpitch), (uint32_t)stage * 128);
+    } else if (j < kPxW + kPwW) {
+      const int i = (j - kPxW) * NW + wave;  // weight group i: lane (h, r) row 32i + r, half h
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], (uint32_t)(32 * i + r32) * pitch + h * 16u,
+                        (uint32_t)stage * 32);
+    } else {
+      const int i = (j - kPxW - kPwW) * NW + wave;  // weight rows 64i .. 64i+63
+      buffer_load_lds4(rs, &sm.ws[buf][i * 256], (uint32_t)(64 * i + lane) * spitch, (uint32_t)stage * 4);
+    }
+  };
+
+  floatx16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < FM; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  const int xs0 = 16 * ((4 * h) ^ x_swz(r32));  // k-step j: slot offset xs0 ^ (16 j)
+  // weight codes and scale bytes of two stages (by stage parity), fragments of two k-steps
+  u32x4 wraw[2][FN];
+  uint32_t wsb[2][FN];
+  bf16x8_t wf[2][FN], xf[2][FM];
+  auto read_w = [&](int ws, int buf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      wraw[ws][i] = *(const u32x4*)&sm.w[buf][(wave * FN + i) * 1024 + lane * 16];
+      wsb[ws][i] = *(const uint16_t*)&sm.ws[buf][(wave * FN * 32 + i * 32 + r32) * 4 + 2 * h];
+    }
+  };
+  auto read_x = [&](int slot, int buf, int j) {
+#pragma unroll
+    for (int g = 0; g < FM; ++g) {
+      const u32x4 v = *(const u32x4*)&sm.x[buf][g * 4096 + r32 * 128 + (xs0 ^ (16 * j))];
+      xf[slot][g] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  // k-step j of the stage whose weights are in wraw[ws]: lane half h's 8 elements of each
+  // weight group sit in 16-element block 2j/4 + h of the stage's four (scale byte j / 2)
+  auto decode_w = [&](int slot, int ws, int j) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const float2_t sf = scales_to_f32(wsb[ws][i]);
+      wf[slot][i] = decode8_bf16(wraw[ws][i][j], j < 2 ? sf[0] : sf[1]);
+    }
+  };
+
+  // prologue: stages 0, 1 and 2 (a stage past the last reloads the last: same bytes to a
+  // buffer nothing reads), then stage 0's first k-step
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2);
+  wait_vmcnt_wide<2 * kLoads>();
+  __builtin_amdgcn_s_barrier();
+  read_w(0, 0);
+  read_x(0, 0, 0);
+  decode_w(0, 0, 0);
+
+  // One stage. Each k-step issues its share of stage t+3's loads and reads and decodes
+  // the next k-step's fragments under its 14 MFMAs. Before the last k-step's MFMAs the
+  // wave waits for stage t+1's loads (issued during stage t-2; those of stages t+2 and
+  // t+3 may stay in flight) and meets the workgroup at a barrier, then reads stage t+1's
+  // weights and first k-step: the barrier also orders every read of stage t's buffer
+  // (all issued by k-step 2) before stage t+4's loads reuse it.
+  auto stage = [&](int t, const int ws) {
+    const int buf = t & 3;
+    const int nbuf = (t + 1) & 3;
+    const int lbuf = (t + 3) & 3;  // held stage t - 1
+    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
+    const bool more = t + 1 < nk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cur = j & 1;
+#pragma unroll
+      for (int l = 0; l < kPerStep; ++l)
+        if (j * kPerStep + l < kLoads) issue(j * kPerStep + l, lstage, lbuf);
+      if (j < 3) {
+        read_x(cur ^ 1, buf, j + 1);
+        decode_w(cur ^ 1, ws, j + 1);
+      } else {
+        // vmcnt(2 kLoads) and lgkmcnt(0): this wave's reads of stage t (k-step 3's were
+        // issued during k-step 2) have landed before any wave passes the barrier
+        __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * kLoads) & 15) | (((2 * kLoads) >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        if (more) {
+          read_w(ws ^ 1, nbuf);
+          read_x(0, nbuf, 0);
+          decode_w(0, ws ^ 1, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
+      // order: one MFMA, then an LDS read, a global->LDS load and VALU work, so the
+      // matrix pipe never waits behind a burst; on the last k-step the decode starts
+      // after four MFMAs, once the next stage's weight reads have landed
+#pragma unroll
+      for (int q = 0; q < FN * FM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (q < FM + 2 * FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (q < kPerStep && j * kPerStep + q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (j < 3 || q >= 4) __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_W4A16_VALU_PER_MFMA, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int t = 0;
+  for (; t + 2 <= nk; t += 2) {
+    stage(t, 0);
+    stage(t + 1, 1);
+  }
+  if (t < nk) stage(t, 0);
+
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  GemmProblem gq{};
+  gq.out = p.out;
+  gq.M = p.M;
+  gq.N = p.N;
+  gq.K = p.K;
+  gq.alpha = p.alpha;
+  static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
+  store_tile_lds<FM, FN>(acc, gq, Alpha{gq.alpha, 0}, (int64_t)m0, (int64_t)n0 + wave * FN * 32,
+                         lane, (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+}
+
 }  // namespace
 
-hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
+W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bool aligned) {
   // long activations: a tiled kernel when its tiles cover at least a quarter of the
-  // compute units (as the W4A4 planner); 288 x 192 unless 256 x 256 tiles need fewer
-  // passes (measured: 4608 x 3072 x 3072 88.7 us vs 90.4 us, x 12288 x 3072 352.5 vs 365.7)
-  const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
-  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  const int64_t tfit = ((p.M + 287) / 288) * ((p.N + 191) / 192);
-  const bool fits32 = (p.M + 288) * p.K * 2 < ((int64_t)1 << 31) && (p.N + 256) * (p.K / 2) < ((int64_t)1 << 31);
+  // compute units (as the W4A4 planner), the one with the fewest passes over the compute
+  // units weighted by MFMAs per wave and k-step (14 for 224 x 256 and 288 x 192, 16 for
+  // 256 x 256); ties go to 224 x 256, then 288 x 192
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tfit = ((M + 287) / 288) * ((N + 191) / 192);
+  const int64_t twide = ((M + 223) / 224) * ((N + 255) / 256);
+  const bool fits32 = (M + 288) * K * 2 < ((int64_t)1 << 31) && (N + 256) * (K / 2) < ((int64_t)1 << 31);
+  if (K % 64 == 0 && fits32 && aligned && t256 * 4 > cus) {
+    const int64_t pw = (twide + cus - 1) / cus, pf = (tfit + cus - 1) / cus, p256 = (t256 + cus - 1) / cus;
+    if (pw * 14 <= pf * 14 && pw * 14 <= p256 * 16) return W4A16Kernel::kWide;
+    if (pf * 14 <= p256 * 16) return W4A16Kernel::kFit;
+    return W4A16Kernel::kTile256;
+  }
+  return W4A16Kernel::kSplitK;
+}
+
+hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
   const bool aligned = (uintptr_t)p.x % 16 == 0 && (uintptr_t)p.w_packed % 16 == 0 &&
-                       (uintptr_t)p.w_scales % 4 == 0;
-  if (p.K % 64 == 0 && fits32 && aligned && tiles * 4 > cus) {
-    if (tiles > 0x7FFFFFFF || tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // passes over the compute units weighted by MFMAs per wave and k-step (14 vs 16)
-    const int64_t pf = (tfit + cus - 1) / cus, p256 = (tiles + cus - 1) / cus;
-    if (pf * 14 <= p256 * 16)
-      hipLaunchKernelGGL((gemm_w4a16_fit_kernel<288, 192>), dim3((unsigned)tfit), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+                       (uintptr_t)p.w_scales % 4 == 0 && (uintptr_t)p.out % 16 == 0;
+  const W4A16Kernel kind = plan_gemm_w4a16(p.M, p.N, p.K, dev.num_cus, aligned);
+  if (kind == W4A16Kernel::kWide) {
+    const int64_t t = ((p.M + 223) / 224) * ((p.N + 255) / 256);
+    if (t > 0x7FFFFFF0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a16_wide_kernel<224, 256>), dim3((unsigned)((t + 7) & ~7)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (kind == W4A16Kernel::kFit) {
+    const int64_t t = ((p.M + 287) / 288) * ((p.N + 191) / 192);
+    if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a16_fit_kernel<288, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (kind == W4A16Kernel::kTile256) {
+    const int64_t t = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)t), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   // workgroup shape: 32 weight rows x 32B activation rows, B the smallest of 1, 2, 4 that

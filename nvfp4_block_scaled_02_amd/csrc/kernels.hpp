@@ -88,6 +88,10 @@ struct W4A16Problem {
   float alpha;  // the weights' global scale
 };
 
+// W4A16 kernels, in the order of the plan codes: split-K (short activations), the 288 x 192
+// tile, the 256 x 256 tile and the 224 x 256 tile with its waves along N.
+enum class W4A16Kernel { kSplitK = 0, kFit = 1, kTile256 = 2, kWide = 3 };
+W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bool aligned);
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev);
 
 // MXFP8: codes/scales use GemmProblem's a_packed/a_scales/w_packed/w_scales (one byte

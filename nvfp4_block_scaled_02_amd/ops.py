@@ -239,6 +239,17 @@ def gemm_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
     return GEMM_KERNELS[kind.value]
 
 
+W4A16_KERNELS = {0: "splitk", 1: "fit", 2: "tile256", 3: "wide"}
+
+
+def gemm_w4a16_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
+    """Name of the kernel :func:`gemm_w4a16` launches for an M x N x K product on a device
+    with ``num_cus`` compute units (0: 256, an MI355X). Host only."""
+    kind = ctypes.c_int(-1)
+    check(load_library().nvfp4_gemm_w4a16_plan(M, N, K, num_cus, ctypes.byref(kind)), "nvfp4_gemm_w4a16_plan")
+    return W4A16_KERNELS[kind.value]
+
+
 def linear_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
     """"fused" when :func:`linear` runs the shape as one kernel (quantize inside the
     short-activation GEMM), else "two_kernels". Host only."""

@@ -130,7 +130,7 @@ void splitk(Stats& st, int64_t rows, int64_t K, int ngrp) {
   });
 }
 
-// W4A16 tiled kernels: activation pieces of 8 rows x 128 bytes (xpitch 2K, scalar offset
+// W4A16 tiled kernels (256 x 256, 288 x 192, 224 x 256): activation pieces of 8 rows x 128 bytes (xpitch 2K, scalar offset
 // stage * 128), weight groups of 32 rows x 32 bytes (stage * 32), scale pieces of 64 rows
 // x 4 bytes (stage * 4); K % 64 == 0.
 void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN) {
@@ -250,6 +250,7 @@ int main(int argc, char** argv) {
         for (int64_t K : Ks) {
           w4a16_tiled(st, M, N, K, 256, 256);
           w4a16_tiled(st, M, N, K, 288, 192);
+          w4a16_tiled(st, M, N, K, 224, 256);
         }
     report("w4a16-tiled", st, bad);
   }

@@ -145,6 +145,31 @@ def test_gemm_plan_routes_shapes(lib):
     assert lib.nvfp4_gemm_plan(8, 8, 64, 0, None) == L.INVALID_VALUE
 
 
+def test_gemm_w4a16_plan_routes_shapes(lib):
+    """The W4A16 planner (host only): the FLUX activations go to the 224 x 256 tile with
+    its waves along N, short activations to split-K; shapes where 288 x 192 or 256 x 256
+    tiles need fewer passes over the compute units go to those; K % 64 != 0 to split-K."""
+    def plan(M, N, K, cus=0):
+        k = ctypes.c_int(-1)
+        st = lib.nvfp4_gemm_w4a16_plan(M, N, K, cus, ctypes.byref(k))
+        return st, k.value
+
+    SPLIT, FIT, TILE, WIDE = 0, 1, 2, 3
+    for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
+                    (4608, 9216, 3072), (2049, 2081, 64), (2305, 1537, 128)]:
+        assert plan(M, N, K) == (L.SUCCESS, WIDE), (M, N, K)
+    for M in (1, 17, 256, 1000):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    assert plan(4288, 3088, 64) == (L.SUCCESS, FIT)     # 2 passes of 224 x 256, 1 of 288 x 192
+    assert plan(4096, 4096, 64) == (L.SUCCESS, TILE)    # one pass of 256 x 256 tiles
+    assert plan(4608, 3072, 3040) == (L.SUCCESS, SPLIT)  # K % 64 == 32
+    assert plan(1000, 3072, 3072, 32) == (L.SUCCESS, WIDE)  # fewer compute units
+    assert plan(8, 8, 48)[0] == L.INVALID_SHAPE          # K % 32 != 0
+    assert plan(8, 8, 2**22 + 32)[0] == L.INVALID_SHAPE
+    assert plan(-1, 8, 64)[0] == L.INVALID_SHAPE
+    assert lib.nvfp4_gemm_w4a16_plan(8, 8, 64, 0, None) == L.INVALID_VALUE
+
+
 def test_linear_plan_fuses_short_activations(lib):
     """nvfp4_linear runs the shortest activations (at most 32 rows, the split-K GEMM's
     one-group shape, and at most 16384 elements, which every workgroup quantizes into its

@@ -33,18 +33,20 @@ def _check(got, x, wp, ws, wgs, label):
     assert ok, f"{label}: {nbad} elements out of tolerance (worst err/tol {worst:.3g})"
 
 
-@pytest.mark.parametrize("M,N,K", [
-    (1, 64, 64), (17, 72, 128), (33, 100, 96), (64, 3000, 224), (130, 70, 256),
-    (5, 5, 32), (300, 200, 1056), (64, 128, 256),
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (1, 64, 64, "splitk"), (17, 72, 128, "splitk"), (33, 100, 96, "splitk"),
+    (64, 3000, 224, "splitk"), (130, 70, 256, "splitk"), (5, 5, 32, "splitk"),
+    (300, 200, 1056, "splitk"), (64, 128, 256, "splitk"),
     # enough tiles (more than a quarter of the compute units) for the tiled kernels. The
-    # 288 x 192 tile, whenever it needs no more passes than 256 x 256: ragged by one row
-    # and column, one stage (K = 64), several stages
-    (2049, 2081, 64), (2300, 2000, 192), (2304, 2048, 640), (2305, 1537, 128),
-    (2017, 3000, 320),
-    # the 256 x 256 tile (one pass; the 288 x 192 tiling would need two)
-    (4096, 4096, 64),
+    # 224 x 256 tile with its waves along N: ragged by one row and column, one stage
+    # (K = 64), an odd and an even number of stages, more stages than its four buffers
+    (2049, 2081, 64, "wide"), (2300, 2000, 192, "wide"), (2304, 2048, 640, "wide"),
+    (2305, 1537, 128, "wide"), (2017, 3000, 320, "wide"), (2017, 2305, 1088, "wide"),
+    # the 288 x 192 tile (one pass; 224 x 256 would need two) and the 256 x 256 tile
+    (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256"),
 ])
-def test_w4a16_small_shapes_in_full(M, N, K):
+def test_w4a16_small_shapes_in_full(M, N, K, kernel):
+    assert nv.gemm_w4a16_plan(M, N, K) == kernel
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     x = to_bf16_bits((rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))).astype(np.float32))
     w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
@@ -57,11 +59,13 @@ def test_w4a16_small_shapes_in_full(M, N, K):
     _check(got, x, wp, ws, wgs, f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 256, 1024), (2305, 1537, 128), (4096, 4096, 64)])
-def test_w4a16_every_scale_code(M, N, K):
+@pytest.mark.parametrize("M,N,K,kernel", [(17, 256, 1024, "splitk"), (2305, 1537, 128, "wide"),
+                                          (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256")])
+def test_w4a16_every_scale_code(M, N, K, kernel):
     """Weight scales cycling through all 127 finite E4M3 codes (subnormals and 448
-    included) with random codes: pins the scale conversion on every code, in the split-K,
-    288 x 192 and 256 x 256 kernels."""
+    included) with random codes: pins the scale conversion on every code, in every
+    kernel."""
+    assert nv.gemm_w4a16_plan(M, N, K) == kernel
     rng = np.random.default_rng(M + N + K)
     x = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
