@@ -168,11 +168,15 @@ int nvfp4_gemm_w4a16(const void* x_bf16, const void* w_packed, const void* w_sca
 
 /* Kernels nvfp4_gemm_w4a16 chooses among (reported by nvfp4_gemm_w4a16_plan). */
 typedef enum {
-  NVFP4_W4A16_SPLITK = 0,  /* K split over a workgroup's waves: short activations */
+  NVFP4_W4A16_SPLITK = 0,  /* K split over a workgroup's waves: at most 64 rows, or K % 64 != 0 */
   NVFP4_W4A16_FIT = 1,     /* 288 x 192 output tiles (K % 64 == 0) */
   NVFP4_W4A16_TILE256 = 2, /* 256 x 256 output tiles (K % 64 == 0) */
-  NVFP4_W4A16_WIDE = 3     /* 224 x 256 output tiles with the waves side by side along N
+  NVFP4_W4A16_WIDE = 3,    /* 224 x 256 output tiles with the waves side by side along N
                               (K % 64 == 0): each weight group decoded once per tile */
+  NVFP4_W4A16_WIDE128X256 = 4, /* the same layout on 128 x 256, */
+  NVFP4_W4A16_WIDE96X256 = 5,  /* 96 x 256, */
+  NVFP4_W4A16_WIDE128X128 = 6, /* 128 x 128 */
+  NVFP4_W4A16_WIDE64X128 = 7   /* and 64 x 128 tiles: medium and short activations */
 } nvfp4_w4a16_kernel;
 
 /*

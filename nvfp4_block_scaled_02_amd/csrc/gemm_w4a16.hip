@@ -509,33 +509,38 @@ __global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
                          (int64_t)m0 + GS * 32, n_base + 64, lane, stage_area);
 }
 
-// ---- 224 x 256 tiles, waves side by side along N ----------------------------------------
+// ---- tiles with the waves side by side along N (224 x 256 and smaller) -------------------
 //
-// Each wave owns 64 weight rows (two groups) and all 224 activation rows (seven groups):
-// 14 MFMAs per k-step as in the 288 x 192 tile, but every weight group is decoded by one
-// wave only (the 2 x 2 layouts decode each weight group in both wave rows), and a stage
-// moves 224 x 128 + 256 x 36 bytes for 224 x 256 outputs instead of 288 x 128 + 192 x 36
-// for 288 x 192 (13% fewer bytes per product). Four stage buffers of 37 KiB; stage t+3's
-// loads are issued during stage t, and the end of stage t waits for the loads issued
-// before stage t-1, so two stages of loads stay in flight across the barrier. 4608 rows
-// make 21 tile rows (the last one 128 rows); every FLUX width is a multiple of 256.
+// Each wave owns BN/4 weight rows and all BM activation rows: at 224 x 256, two weight
+// groups and seven activation groups, 14 MFMAs per k-step as in the 288 x 192 tile, but
+// every weight group is decoded by one wave only (the 2 x 2 layouts decode each weight
+// group in both wave rows), and a stage moves 13% fewer bytes per product. 4608 rows make
+// 21 tile rows (the last one 128 rows); every FLUX width is a multiple of 256. The 128 x 128
+// and 64 x 128 forms (one weight group per wave) serve short and medium activations.
+//
+// Loads. The direct-to-LDS path costs about the same per 64-byte row segment an
+// instruction touches, whatever the bytes used (measured across these tile shapes), so
+// the weights' scales, 4 bytes per row and stage, are loaded 16 bytes per row for four
+// stages at once (64 rows per load) into two quad buffers; activations take 8 rows x 128
+// bytes per load, weight codes 32 rows x 32 bytes. Four code stage buffers; stage t+3's
+// loads are issued during stage t.
 template <int BM, int BN>
 struct alignas(16) W4A16WideSmem {
   uint8_t x[4][BM * 128];
   uint8_t w[4][BN * 32];
-  uint8_t ws[4][BN * 4];
+  uint8_t ws[2][BN * 16];
 };
 
 #ifndef NVFP4_W4A16_VALU_PER_MFMA
 #define NVFP4_W4A16_VALU_PER_MFMA 4
 #endif
 
-// Wait until at most n of this wave's vector memory operations are outstanding (n < 64:
-// the counter's low four bits and its two high bits at 15:14).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt_wide() {
+// s_waitcnt with vmcnt(n) (n < 64: the counter's low four bits and its two high bits at
+// 15:14) and lgkmcnt(0) when kLds, expcnt left free.
+template <int n, bool kLds>
+__device__ __forceinline__ void wait_vm_wide() {
   static_assert(n >= 0 && n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt((kLds ? 0x0070 : 0x0F70) | (n & 15) | ((n >> 4) << 14));
 }
 
 // Requires K % 64 == 0, 16-byte aligned x, codes and out, 4-byte aligned scales, and
@@ -546,13 +551,14 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   constexpr int NW = 4;
   __shared__ W4A16WideSmem<BM, BN> sm;
   constexpr int FM = BM / 32, FN = BN / NW / 32;
-  constexpr int kPx = BM / 8, kPw = BN / 32, kPs = BN / 64;  // loads per stage
-  static_assert(FM * 32 == BM && FN * 32 * NW == BN, "tile shape");
-  static_assert(kPx % NW == 0 && kPw % NW == 0 && kPs % NW == 0, "loads divide among waves");
-  constexpr int kPxW = kPx / NW, kPwW = kPw / NW, kPsW = kPs / NW;
-  constexpr int kLoads = kPxW + kPwW + kPsW;
-  constexpr int kPerStep = (kLoads + 3) / 4;  // loads issued per k-step
-  static_assert(2 * kLoads < 64, "two stages of loads fit the vmcnt counter");
+  constexpr int kPx = BM / 8, kPw = BN / 32, kPs = BN / 64;  // pieces per stage / quad
+  static_assert(FM * 32 == BM && FN * 32 * NW == BN && BN % 64 == 0, "tile shape");
+  static_assert(kPx % NW == 0 && kPw % NW == 0 && kPs <= NW, "loads divide among waves");
+  constexpr int kPxW = kPx / NW, kPwW = kPw / NW;
+  constexpr int kCode = kPxW + kPwW;  // code loads per wave and stage
+  // loads issued during a stage whose target stage (t + 3) starts a quad: one more
+  constexpr int kPerStep = (kCode + 1 + 3) / 4;  // loads placed per k-step
+  static_assert(2 * kCode + 1 < 64, "two stages of loads fit the vmcnt counter");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -579,6 +585,7 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int nk = (int)(p.K / 64);
+  const int nquad = (nk + 3) >> 2;
   const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
 
   // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
@@ -586,18 +593,26 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   const __amdgpu_buffer_rsrc_t rw = window_rsrc(p.w_packed, n0, p.N, pitch);
   const __amdgpu_buffer_rsrc_t rs = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  // load j of this wave (lists: activation pieces, weight pieces, scale pieces)
-  auto issue = [&](int j, int stage, int buf) {
+  // Load j of this wave for target stage ts (the stage it fills; clamped to the last one
+  // for the loads past the end, which land in buffers no stage reads): activation pieces,
+  // weight pieces, then, when ts starts a quad, the scale piece of that quad (waves past
+  // the last piece repeat it: the same bytes to the same LDS place). A last quad shorter
+  // than four stages reads past its rows' ends: range-checked like every load.
+  auto issue = [&](int j, int ts) {
+    const int buf = ts & 3;
+    const int stage = ts < nk ? ts : nk - 1;
     if (j < kPxW) {
       const int i = j * NW + wave;  // rows 8i .. 8i+7 of the tile
       buffer_load_lds16(rx, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, xpitch), (uint32_t)stage * 128);
-    } else if (j < kPxW + kPwW) {
+    } else if (j < kCode) {
       const int i = (j - kPxW) * NW + wave;  // weight group i: lane (h, r) row 32i + r, half h
       buffer_load_lds16(rw, &sm.w[buf][i * 1024], (uint32_t)(32 * i + r32) * pitch + h * 16u,
                         (uint32_t)stage * 32);
     } else {
-      const int i = (j - kPxW - kPwW) * NW + wave;  // weight rows 64i .. 64i+63
-      buffer_load_lds4(rs, &sm.ws[buf][i * 256], (uint32_t)(64 * i + lane) * spitch, (uint32_t)stage * 4);
+      const int i = min(wave, kPs - 1);  // weight rows 64i .. 64i+63
+      const int quad = min(ts >> 2, nquad - 1);
+      buffer_load_lds16(rs, &sm.ws[(ts >> 2) & 1][i * 1024],
+                        scale_piece_voff(lane, 64 * i, spitch, (uint32_t)quad * 16), 0);
     }
   };
 
@@ -614,11 +629,11 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   u32x4 wraw[2][FN];
   uint32_t wsb[2][FN];
   bf16x8_t wf[2][FN], xf[2][FM];
-  auto read_w = [&](int ws, int buf) {
+  auto read_w = [&](int ws, int ts) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[ws][i] = *(const u32x4*)&sm.w[buf][(wave * FN + i) * 1024 + lane * 16];
-      wsb[ws][i] = *(const uint16_t*)&sm.ws[buf][(wave * FN * 32 + i * 32 + r32) * 4 + 2 * h];
+      wraw[ws][i] = *(const u32x4*)&sm.w[ts & 3][(wave * FN + i) * 1024 + lane * 16];
+      wsb[ws][i] = *(const uint16_t*)&sm.ws[(ts >> 2) & 1][(wave * FN * 32 + i * 32 + r32) * 16 + 4 * (ts & 3) + 2 * h];
     }
   };
   auto read_x = [&](int slot, int buf, int j) {
@@ -629,7 +644,7 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
     }
   };
   // k-step j of the stage whose weights are in wraw[ws]: lane half h's 8 elements of each
-  // weight group sit in 16-element block 2j/4 + h of the stage's four (scale byte j / 2)
+  // weight group sit in 16-element block 2h + j / 2 of the stage's four (scale byte j / 2)
   auto decode_w = [&](int slot, int ws, int j) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -638,49 +653,51 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
     }
   };
 
-  // prologue: stages 0, 1 and 2 (a stage past the last reloads the last: same bytes to a
-  // buffer nothing reads), then stage 0's first k-step
+  // prologue: stages 0, 1 and 2 and the scales of quad 0, then stage 0's first k-step.
+  // Outstanding after it: stages 1 and 2's code loads.
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
+  for (int j = 0; j <= kCode; ++j) issue(j, 0);
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1);
+  for (int j = 0; j < kCode; ++j) issue(j, 1);
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2);
-  wait_vmcnt_wide<2 * kLoads>();
+  for (int j = 0; j < kCode; ++j) issue(j, 2);
+  wait_vm_wide<2 * kCode, false>();
   __builtin_amdgcn_s_barrier();
   read_w(0, 0);
   read_x(0, 0, 0);
   decode_w(0, 0, 0);
 
-  // One stage. Each k-step issues its share of stage t+3's loads and reads and decodes
-  // the next k-step's fragments under its 14 MFMAs. Before the last k-step's MFMAs the
-  // wave waits for stage t+1's loads (issued during stage t-2; those of stages t+2 and
-  // t+3 may stay in flight) and meets the workgroup at a barrier, then reads stage t+1's
-  // weights and first k-step: the barrier also orders every read of stage t's buffer
-  // (all issued by k-step 2) before stage t+4's loads reuse it.
-  auto stage = [&](int t, const int ws) {
+  // One stage; ph = t % 4 (a constant). Each k-step issues its share of stage t+3's loads
+  // and reads and decodes the next k-step's fragments under its MFMAs. Before the last
+  // k-step's MFMAs the wave waits for stage t+1's loads (issued during stage t-2; those of
+  // stages t+2 and t+3 may stay in flight) with its own LDS reads of stage t landed, and
+  // meets the workgroup at a barrier; then it reads stage t+1's weights and first k-step.
+  // The barrier also orders every read of stage t's buffers before stage t+4's loads reuse
+  // them (a quad buffer is reused four stages after its last read).
+  auto stage = [&](int t, const int ph) {
+    const int ws = ph & 1;
     const int buf = t & 3;
-    const int nbuf = (t + 1) & 3;
-    const int lbuf = (t + 3) & 3;  // held stage t - 1
-    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
+    const bool quad_load = ((ph + 3) & 3) == 0;  // stage t + 3 starts a quad
+    const int nl = kCode + (quad_load ? 1 : 0);
+    // loads of stages t+2 (issued during t-1) and t+3 (issued during t)
+    const bool quad_prev = ((ph + 2) & 3) == 0;
     const bool more = t + 1 < nk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cur = j & 1;
 #pragma unroll
       for (int l = 0; l < kPerStep; ++l)
-        if (j * kPerStep + l < kLoads) issue(j * kPerStep + l, lstage, lbuf);
+        if (j * kPerStep + l < nl) issue(j * kPerStep + l, t + 3);
       if (j < 3) {
         read_x(cur ^ 1, buf, j + 1);
         decode_w(cur ^ 1, ws, j + 1);
       } else {
-        // vmcnt(2 kLoads) and lgkmcnt(0): this wave's reads of stage t (k-step 3's were
-        // issued during k-step 2) have landed before any wave passes the barrier
-        __builtin_amdgcn_s_waitcnt(0x0070 | ((2 * kLoads) & 15) | (((2 * kLoads) >> 4) << 14));
+        if (quad_load || quad_prev) wait_vm_wide<2 * kCode + 1, true>();
+        else wait_vm_wide<2 * kCode, true>();
         __builtin_amdgcn_s_barrier();
         if (more) {
-          read_w(ws ^ 1, nbuf);
-          read_x(0, nbuf, 0);
+          read_w(ws ^ 1, t + 1);
+          read_x(0, (t + 1) & 3, 0);
           decode_w(0, ws ^ 1, 0);
         }
       }
@@ -693,21 +710,25 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
       // matrix pipe never waits behind a burst; on the last k-step the decode starts
       // after four MFMAs, once the next stage's weight reads have landed
 #pragma unroll
-      for (int q = 0; q < FN * FM; ++q) {
+      for (int qq = 0; qq < FN * FM; ++qq) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        if (q < FM + 2 * FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        if (q < kPerStep && j * kPerStep + q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        if (j < 3 || q >= 4) __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_W4A16_VALU_PER_MFMA, 0);
+        if (qq < FM + 2 * FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (qq < kPerStep && j * kPerStep + qq < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (j < 3 || qq >= 4) __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_W4A16_VALU_PER_MFMA, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   int t = 0;
-  for (; t + 2 <= nk; t += 2) {
+  for (; t + 4 <= nk; t += 4) {
     stage(t, 0);
     stage(t + 1, 1);
+    stage(t + 2, 2);
+    stage(t + 3, 3);
   }
   if (t < nk) stage(t, 0);
+  if (t + 1 < nk) stage(t + 1, 1);
+  if (t + 2 < nk) stage(t + 2, 2);
 
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
@@ -724,46 +745,97 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
 
 }  // namespace
 
+namespace {
+
+struct WideShape {
+  W4A16Kernel kind;
+  int bm, bn;
+};
+// the tiles with their waves along N, largest first
+constexpr WideShape kWide[] = {{W4A16Kernel::kWide, 224, 256},
+                               {W4A16Kernel::kWide128x256, 128, 256},
+                               {W4A16Kernel::kWide96x256, 96, 256},
+                               {W4A16Kernel::kWide128x128, 128, 128},
+                               {W4A16Kernel::kWide64x128, 64, 128}};
+
+// Cost of one stage (64 elements of K) of one tile, in 64-byte row segments loaded per
+// compute unit: the tiled kernels' loads cost about 2.1 cycles per segment whatever the
+// bytes used (measured over these tile shapes at one tile per compute unit), and a tile
+// whose MFMAs take longer than its loads pays those instead (14 or 16 MFMAs of 32 cycles
+// per wave and k-step for the largest tiles). Activation loads touch 16 segments per
+// 8 rows; weight codes 32 per 32 rows; scales 64 per 64 rows, every stage (288 x 192,
+// 256 x 256) or every fourth stage (the tiles along N).
+double tile_stage_cost(int bm, int bn, bool quad_scales) {
+  const double segs = 2.0 * bm + bn + (quad_scales ? bn / 4.0 : (double)bn);
+  const double mfma = (double)(bm / 32) * (bn / 32) / 4.0 * 4.0 * 32.0 / 2.1;  // per wave
+  return segs > mfma ? segs : mfma;
+}
+
+}  // namespace
+
 W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bool aligned) {
-  // long activations: a tiled kernel when its tiles cover at least a quarter of the
-  // compute units (as the W4A4 planner), the one with the fewest passes over the compute
-  // units weighted by MFMAs per wave and k-step (14 for 224 x 256 and 288 x 192, 16 for
-  // 256 x 256); ties go to 224 x 256, then 288 x 192
+  // Activations of at most 64 rows: split-K (it reads the weights once and fills the chip
+  // with 32-row workgroups). Longer ones: the tiled kernel with the fewest passes over the
+  // compute units times its stage cost.
   const int64_t cus = num_cus > 0 ? num_cus : 256;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t tfit = ((M + 287) / 288) * ((N + 191) / 192);
-  const int64_t twide = ((M + 223) / 224) * ((N + 255) / 256);
   const bool fits32 = (M + 288) * K * 2 < ((int64_t)1 << 31) && (N + 256) * (K / 2) < ((int64_t)1 << 31);
-  if (K % 64 == 0 && fits32 && aligned && t256 * 4 > cus) {
-    const int64_t pw = (twide + cus - 1) / cus, pf = (tfit + cus - 1) / cus, p256 = (t256 + cus - 1) / cus;
-    if (pw * 14 <= pf * 14 && pw * 14 <= p256 * 16) return W4A16Kernel::kWide;
-    if (pf * 14 <= p256 * 16) return W4A16Kernel::kFit;
-    return W4A16Kernel::kTile256;
+  if (K % 64 != 0 || !fits32 || !aligned || M <= 64) return W4A16Kernel::kSplitK;
+  auto cost = [&](int bm, int bn, bool quad) {
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    return (double)((tiles + cus - 1) / cus) * tile_stage_cost(bm, bn, quad);
+  };
+  W4A16Kernel best = W4A16Kernel::kFit;
+  double cbest = cost(288, 192, false);
+  const double c256 = cost(256, 256, false);
+  if (c256 < cbest) { best = W4A16Kernel::kTile256; cbest = c256; }
+  for (const WideShape& w : kWide) {
+    const double c = cost(w.bm, w.bn, true);
+    if (c <= cbest) { best = w.kind; cbest = c; }
   }
-  return W4A16Kernel::kSplitK;
+  return best;
 }
 
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev) {
   const bool aligned = (uintptr_t)p.x % 16 == 0 && (uintptr_t)p.w_packed % 16 == 0 &&
                        (uintptr_t)p.w_scales % 4 == 0 && (uintptr_t)p.out % 16 == 0;
   const W4A16Kernel kind = plan_gemm_w4a16(p.M, p.N, p.K, dev.num_cus, aligned);
-  if (kind == W4A16Kernel::kWide) {
-    const int64_t t = ((p.M + 223) / 224) * ((p.N + 255) / 256);
-    if (t > 0x7FFFFFF0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_w4a16_wide_kernel<224, 256>), dim3((unsigned)((t + 7) & ~7)), dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
-  if (kind == W4A16Kernel::kFit) {
-    const int64_t t = ((p.M + 287) / 288) * ((p.N + 191) / 192);
-    if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_w4a16_fit_kernel<288, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
-  if (kind == W4A16Kernel::kTile256) {
-    const int64_t t = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)t), dim3(256), 0, stream, p);
-    return hipGetLastError();
+  auto tiles_of = [&](int bm, int bn, bool round8) -> int64_t {
+    const int64_t t = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    return round8 ? (t + 7) & ~(int64_t)7 : t;
+  };
+  switch (kind) {
+    case W4A16Kernel::kWide:
+    case W4A16Kernel::kWide128x256:
+    case W4A16Kernel::kWide96x256:
+    case W4A16Kernel::kWide128x128:
+    case W4A16Kernel::kWide64x128: {
+      int bm = 0, bn = 0;
+      for (const WideShape& w : kWide)
+        if (w.kind == kind) { bm = w.bm; bn = w.bn; }
+      const int64_t g = tiles_of(bm, bn, true);
+      if (g > 0x7FFFFFF8) return hipErrorInvalidValue;
+      const dim3 gd((unsigned)g), bd(256);
+      if (kind == W4A16Kernel::kWide) hipLaunchKernelGGL((gemm_w4a16_wide_kernel<224, 256>), gd, bd, 0, stream, p);
+      else if (kind == W4A16Kernel::kWide128x256) hipLaunchKernelGGL((gemm_w4a16_wide_kernel<128, 256>), gd, bd, 0, stream, p);
+      else if (kind == W4A16Kernel::kWide96x256) hipLaunchKernelGGL((gemm_w4a16_wide_kernel<96, 256>), gd, bd, 0, stream, p);
+      else if (kind == W4A16Kernel::kWide128x128) hipLaunchKernelGGL((gemm_w4a16_wide_kernel<128, 128>), gd, bd, 0, stream, p);
+      else hipLaunchKernelGGL((gemm_w4a16_wide_kernel<64, 128>), gd, bd, 0, stream, p);
+      return hipGetLastError();
+    }
+    case W4A16Kernel::kFit: {
+      const int64_t t = tiles_of(288, 192, false);
+      if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_w4a16_fit_kernel<288, 192>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case W4A16Kernel::kTile256: {
+      const int64_t t = tiles_of(256, 256, false);
+      if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case W4A16Kernel::kSplitK:
+      break;
   }
   // workgroup shape: 32 weight rows x 32B activation rows, B the smallest of 1, 2, 4 that
   // covers min(M, 128) rows

@@ -89,8 +89,12 @@ struct W4A16Problem {
 };
 
 // W4A16 kernels, in the order of the plan codes: split-K (short activations), the 288 x 192
-// tile, the 256 x 256 tile and the 224 x 256 tile with its waves along N.
-enum class W4A16Kernel { kSplitK = 0, kFit = 1, kTile256 = 2, kWide = 3 };
+// tile, the 256 x 256 tile, and the tiles with their waves along N: 224 x 256, 128 x 256,
+// 96 x 256, 128 x 128 and 64 x 128.
+enum class W4A16Kernel {
+  kSplitK = 0, kFit = 1, kTile256 = 2, kWide = 3, kWide128x256 = 4, kWide96x256 = 5,
+  kWide128x128 = 6, kWide64x128 = 7
+};
 W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bool aligned);
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev);
 

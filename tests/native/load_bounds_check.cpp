@@ -130,10 +130,11 @@ void splitk(Stats& st, int64_t rows, int64_t K, int ngrp) {
   });
 }
 
-// W4A16 tiled kernels (256 x 256, 288 x 192, 224 x 256): activation pieces of 8 rows x 128 bytes (xpitch 2K, scalar offset
-// stage * 128), weight groups of 32 rows x 32 bytes (stage * 32), scale pieces of 64 rows
-// x 4 bytes (stage * 4); K % 64 == 0.
-void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN) {
+// W4A16 tiled kernels: activation pieces of 8 rows x 128 bytes (xpitch 2K, scalar offset
+// stage * 128), weight groups of 32 rows x 32 bytes (stage * 32); scale pieces of 64 rows
+// x 4 bytes (stage * 4) for the 256 x 256 and 288 x 192 tiles, or (quad_scales, the tiles
+// with their waves along N) 64 rows x 16 bytes for four stages at byte 16 * quad; K % 64 == 0.
+void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN, bool quad_scales = false) {
   const uint32_t xpitch = (uint32_t)(2 * K), pitch = (uint32_t)(K / 2), spitch = (uint32_t)(K / 16);
   const int nk = (int)(K / 64);
   for_tiles(M, BM, [&](int64_t m0) {
@@ -153,11 +154,13 @@ void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN) {
         for (int i = 0; i < BN / 32; ++i)
           check_load(st, "w4a16-w", N, pitch, n0, (uint32_t)(32 * i + r32) * pitch + h * 16u,
                      (uint32_t)stage * 32, 16, n0 + 32 * i + r32, (int64_t)stage * 32 + 16 * h);
-        for (int i = 0; i < (BN + 63) / 64; ++i)
-          check_load(st, "w4a16-s", N, spitch, n0, (uint32_t)(64 * i + lane) * spitch,
-                     (uint32_t)stage * 4, 4, n0 + 64 * i + lane, (int64_t)stage * 4);
+        if (!quad_scales)
+          for (int i = 0; i < (BN + 63) / 64; ++i)
+            check_load(st, "w4a16-s", N, spitch, n0, (uint32_t)(64 * i + lane) * spitch,
+                       (uint32_t)stage * 4, 4, n0 + 64 * i + lane, (int64_t)stage * 4);
       }
   });
+  if (quad_scales) scale_pieces(st, "w4a16-quad-s", N, BN, BN, spitch, (nk + 3) / 4);
 }
 
 // W4A16 split-K: window of 32 B activation rows at m0 and 32 weight rows at n0; lane
@@ -244,13 +247,15 @@ int main(int argc, char** argv) {
   }
   {
     Stats st;
-    const int64_t Ks[] = {64, 192, 3072};
+    const int64_t Ks[] = {64, 192, 320, 448, 3072};
     for (int64_t M : {1, 33, 289, 777, 1000})
       for (int64_t N : {17, 193, 385, 1000})
         for (int64_t K : Ks) {
           w4a16_tiled(st, M, N, K, 256, 256);
           w4a16_tiled(st, M, N, K, 288, 192);
-          w4a16_tiled(st, M, N, K, 224, 256);
+          w4a16_tiled(st, M, N, K, 224, 256, true);
+          w4a16_tiled(st, M, N, K, 128, 128, true);
+          w4a16_tiled(st, M, N, K, 64, 128, true);
         }
     report("w4a16-tiled", st, bad);
   }

@@ -146,21 +146,30 @@ def test_gemm_plan_routes_shapes(lib):
 
 
 def test_gemm_w4a16_plan_routes_shapes(lib):
-    """The W4A16 planner (host only): the FLUX activations go to the 224 x 256 tile with
-    its waves along N, short activations to split-K; shapes where 288 x 192 or 256 x 256
-    tiles need fewer passes over the compute units go to those; K % 64 != 0 to split-K."""
+    """The W4A16 planner (host only): at most 64 rows (or K % 64 != 0) go to split-K;
+    longer activations to the tiled kernel with the fewest passes over the compute units
+    times its per-stage load cost: the FLUX activations to the 224 x 256 tile with its
+    waves along N, medium ones to the smaller tiles along N, and the shapes where 288 x 192
+    or 256 x 256 tiles need fewer passes to those."""
     def plan(M, N, K, cus=0):
         k = ctypes.c_int(-1)
         st = lib.nvfp4_gemm_w4a16_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    SPLIT, FIT, TILE, WIDE = 0, 1, 2, 3
+    SPLIT, FIT, TILE, WIDE, W128x256, W96x256, W128x128, W64x128 = range(8)
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
-                    (4608, 9216, 3072), (2049, 2081, 64), (2305, 1537, 128)]:
+                    (4608, 9216, 3072), (18432, 12288, 3072), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, WIDE), (M, N, K)
-    for M in (1, 17, 256, 1000):
+    for M in (1, 17, 64):
         assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
-    assert plan(4288, 3088, 64) == (L.SUCCESS, FIT)     # 2 passes of 224 x 256, 1 of 288 x 192
+    for M in (65, 128, 256, 512):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, W64x128), M
+    assert plan(1000, 3072, 3072) == (L.SUCCESS, W128x128)
+    assert plan(256, 12288, 3072) == (L.SUCCESS, W128x128)
+    for M in (1500, 2000):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, W96x256), M
+    assert plan(2017, 3000, 320) == (L.SUCCESS, W128x256)
+    assert plan(4288, 3088, 64) == (L.SUCCESS, FIT)     # 1 pass of 288 x 192, 2 of the others
     assert plan(4096, 4096, 64) == (L.SUCCESS, TILE)    # one pass of 256 x 256 tiles
     assert plan(4608, 3072, 3040) == (L.SUCCESS, SPLIT)  # K % 64 == 32
     assert plan(1000, 3072, 3072, 32) == (L.SUCCESS, WIDE)  # fewer compute units

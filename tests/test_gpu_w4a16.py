@@ -34,15 +34,19 @@ def _check(got, x, wp, ws, wgs, label):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [
+    # split-K: at most 64 rows, or K % 64 == 32
     (1, 64, 64, "splitk"), (17, 72, 128, "splitk"), (33, 100, 96, "splitk"),
-    (64, 3000, 224, "splitk"), (130, 70, 256, "splitk"), (5, 5, 32, "splitk"),
-    (300, 200, 1056, "splitk"), (64, 128, 256, "splitk"),
-    # enough tiles (more than a quarter of the compute units) for the tiled kernels. The
-    # 224 x 256 tile with its waves along N: ragged by one row and column, one stage
-    # (K = 64), an odd and an even number of stages, more stages than its four buffers
-    (2049, 2081, 64, "wide"), (2300, 2000, 192, "wide"), (2304, 2048, 640, "wide"),
-    (2305, 1537, 128, "wide"), (2017, 3000, 320, "wide"), (2017, 2305, 1088, "wide"),
-    # the 288 x 192 tile (one pass; 224 x 256 would need two) and the 256 x 256 tile
+    (64, 3000, 224, "splitk"), (5, 5, 32, "splitk"), (300, 200, 1056, "splitk"),
+    (64, 128, 256, "splitk"),
+    # the tiles with their waves along N, each ragged in M and N, with one stage (K = 64),
+    # a partial last quad of scale stages (K / 64 = 3, 5, 7, 17) and whole quads (10)
+    (130, 70, 256, "wide64x128"), (65, 3000, 448, "wide64x128"),
+    (1001, 3001, 192, "wide128x128"), (2305, 1537, 128, "wide128x128"),
+    (2049, 2081, 64, "wide96x256"), (2300, 2000, 192, "wide96x256"),
+    (2017, 2305, 1088, "wide96x256"), (2304, 2048, 640, "wide96x256"),
+    (2017, 3000, 320, "wide128x256"),
+    (3001, 2999, 192, "wide"), (3300, 2600, 320, "wide"),
+    # the 288 x 192 tile (one pass where the others need two) and the 256 x 256 tile
     (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256"),
 ])
 def test_w4a16_small_shapes_in_full(M, N, K, kernel):
@@ -59,8 +63,10 @@ def test_w4a16_small_shapes_in_full(M, N, K, kernel):
     _check(got, x, wp, ws, wgs, f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K,kernel", [(17, 256, 1024, "splitk"), (2305, 1537, 128, "wide"),
-                                          (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256")])
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (17, 256, 1024, "splitk"), (130, 70, 256, "wide64x128"), (2305, 1537, 128, "wide128x128"),
+    (2049, 2081, 64, "wide96x256"), (2017, 3000, 320, "wide128x256"), (3001, 2999, 192, "wide"),
+    (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256")])
 def test_w4a16_every_scale_code(M, N, K, kernel):
     """Weight scales cycling through all 127 finite E4M3 codes (subnormals and 448
     included) with random codes: pins the scale conversion on every code, in every
