@@ -424,8 +424,8 @@ def context_legs(nv, lib, timer, stream, n):
             # W4A16: NVFP4 weights, bf16 activations
             a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
             ms16, _ = timer.launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, warm)
-            out["w4a16"] = {"shape": [M, N, K], "avg_ms": round(ms16, 5),
-                            "TFLOP/s": round(fl / (ms16 * 1e-3) / 1e12, 1)}
+            out["w4a16"] = {"shape": [M, N, K], "kernel": nv.gemm_w4a16_plan(M, N, K),
+                            "avg_ms": round(ms16, 5), "TFLOP/s": round(fl / (ms16 * 1e-3) / 1e12, 1)}
         del x, w, wp, ws, work, ap, as_, y
         torch.cuda.empty_cache()
     # short activations: the weights dominate the bytes (K/2 + K/16 bytes per weight row)
@@ -452,7 +452,7 @@ def context_legs(nv, lib, timer, stream, n):
             "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K), "w4a4_avg_ms": round(ms, 5),
             "w4a4_weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
             "linear": nv.linear_plan(M, N, K), "linear_avg_ms": round(msl, 5),
-            "w4a16_avg_ms": round(ms16, 5),
+            "w4a16_kernel": nv.gemm_w4a16_plan(M, N, K), "w4a16_avg_ms": round(ms16, 5),
             "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
     return out
 
