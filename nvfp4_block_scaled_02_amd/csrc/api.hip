@@ -271,7 +271,7 @@ int nvfp4_mxfp8_gemm_elem(const void* ac, const void* as, int a_element, const v
   if (K % 128 != 0) return NVFP4_ERROR_INVALID_SHAPE;
   if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
   // 32-bit buffer offsets, with one 256-row tile past the end
-  if ((M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
+  if (!nvfp4::fits_i31(M + 256, K) || !nvfp4::fits_i31(N + 256, K))
     return NVFP4_ERROR_INVALID_SHAPE;
   if (!aligned(ac, 16) || !aligned(wc, 16) || !aligned(out, 16) || !aligned(as, 4) ||
       !aligned(ws, 4))
@@ -311,7 +311,7 @@ int nvfp4_fp8r_gemm(const void* ac, const void* as, const void* wc, const void* 
   if (K % 128 != 0) return NVFP4_ERROR_INVALID_SHAPE;
   if (M > 0 && N > ((int64_t)1 << 61) / M) return NVFP4_ERROR_INVALID_SHAPE;
   // 32-bit buffer offsets, with one 256-row tile past the end (codes and fp32 scales)
-  if ((M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
+  if (!nvfp4::fits_i31(M + 256, K) || !nvfp4::fits_i31(N + 256, K))
     return NVFP4_ERROR_INVALID_SHAPE;
   if (!aligned(ac, 16) || !aligned(wc, 16) || !aligned(out, 16) || !aligned(as, 4) ||
       !aligned(ws, 4))

@@ -1163,10 +1163,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   cus = cus > 0 ? cus : 256;
   // 32-bit buffer offsets (with one tile of rows past the end) for the 256x256, fit and
   // split-K kernels
-  const bool fits32 = (M + FBM) * (K / 2) < ((int64_t)1 << 31) &&
-                      (N + FBN) * (K / 2) < ((int64_t)1 << 31);
-  const bool fits32_256 = (M + BM) * (K / 2) < ((int64_t)1 << 31) &&
-                          (N + BN) * (K / 2) < ((int64_t)1 << 31);
+  const bool fits32 = fits_i31(M + FBM, K / 2) && fits_i31(N + FBN, K / 2);
+  const bool fits32_256 = fits_i31(M + BM, K / 2) && fits_i31(N + BN, K / 2);
   const bool fast = aligned && (K % (64 * KC) == 0) && fits32_256;
   const int64_t nk = K / 128;
   // tiled kernels: one tile per compute unit at a time, plus epilogue and prologue

@@ -778,7 +778,7 @@ W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bo
   // with 32-row workgroups). Longer ones: the tiled kernel with the fewest passes over the
   // compute units times its stage cost.
   const int64_t cus = num_cus > 0 ? num_cus : 256;
-  const bool fits32 = (M + 288) * K * 2 < ((int64_t)1 << 31) && (N + 256) * (K / 2) < ((int64_t)1 << 31);
+  const bool fits32 = fits_i31(M + 288, 2 * K) && fits_i31(N + 256, K / 2);
   if (K % 64 != 0 || !fits32 || !aligned || M <= 64) return W4A16Kernel::kSplitK;
   auto cost = [&](int bm, int bn, bool quad) {
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);

@@ -13,6 +13,13 @@ struct LaunchInfo {
   int device;   // its index
 };
 
+// rows * row_bytes < 2^31 (a tile's 32-bit buffer offsets), for rows, row_bytes >= 0,
+// evaluated without forming the product (which can exceed int64 for shapes the size
+// checks accept, such as one row of 2^61 elements).
+inline bool fits_i31(int64_t rows, int64_t row_bytes) {
+  return row_bytes <= 0 || rows <= ((((int64_t)1) << 31) - 1) / row_bytes;
+}
+
 // gs_dev non-null: the global scale is read on the device from *gs_dev (clamped into
 // [2^-90, 2^90], NaN read as 1) and `gs` is ignored.
 hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* packed,

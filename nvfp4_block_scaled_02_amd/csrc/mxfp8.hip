@@ -614,7 +614,7 @@ hipError_t launch_fp8_gemm(const GemmProblem& p, hipStream_t stream, const Launc
   const int64_t cus = dev.num_cus > 0 ? dev.num_cus : 256;
   const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   const int64_t tfit = ((p.M + 287) / 288) * ((p.N + 191) / 192);
-  const bool fit32 = (p.M + 320) * p.K < ((int64_t)1 << 31) && (p.N + 192) * p.K < ((int64_t)1 << 31);
+  const bool fit32 = fits_i31(p.M + 320, p.K) && fits_i31(p.N + 192, p.K);
   const int64_t pass256 = (t256 + cus - 1) / cus, passfit = (tfit + cus - 1) / cus;
   if (fit32 && passfit * 14 <= pass256 * 16) {
     if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
