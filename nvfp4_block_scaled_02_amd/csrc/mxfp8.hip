@@ -347,21 +347,42 @@ __global__ void __launch_bounds__(256) gemm_mx_kernel(GemmProblem p) {
 // 0..3 (m = 0) or 5..8 (m = 1), and the middle activation group 4 is split by weight
 // block: wave (0, n) takes its blocks with weight groups 3n and 3n+1, wave (1, n) the one
 // with 3n+2. So the waves issue 14 and 13 MFMAs per stage (the 256 x 256 tile: 16) and no
-// partial sums need to meet. Loads, LDS layout and the stage pipeline are those of the
-// 256 x 256 kernel: 4 code buffers of 30 KiB and 2 scale buffers of 8 KiB (activation
-// scale rows rounded up to whole 64-row pieces), 136 KiB in all.
+// partial sums need to meet.
+//
+// The codes are loaded two stages (128 elements of K, a whole 128-byte line per row) at a
+// time: each load fills 8 rows x 128 bytes (eight lanes per row), where the 256 x 256
+// kernel's loads fill 16 rows x 64 bytes. Direct-to-LDS loads cost by the cache lines
+// they touch, and this halves the lines per byte (measured on the device: 88.6 against
+// 51.3 GB/s per compute unit of L2-resident data). LDS: two double-stage buffers (the bytes of four single stages), each row's 128
+// bytes as eight 16-byte chunks at slots c ^ x_swz(row % 32), so the fragment reads (lane
+// (h, r) of stage s reads chunks 4s + h and 4s + 2 + h of row r) hit distinct banks.
+//
+// Pipeline over double stages d (stages 2d, 2d+1, buffer d & 1):
+//  * even stage 2d: MFMAs on stage 2d's fragments while stage 2d+1's are read (same
+//    buffer); every 8 stages, the next scale group's loads;
+//  * odd stage 2d+1: half of its MFMAs, then the wave waits for all its loads (those of
+//    double stage d+1, issued during stage 2d-1) with its LDS reads landed and meets the
+//    workgroup at a barrier; then, under the other MFMAs, it issues the loads of double
+//    stage d+2 into buffer d & 1 (whose last fragments, stage 2d+1's, every wave read
+//    during stage 2d) and reads stage 2d+2's fragments from buffer (d+1) & 1.
+// So a load has about two stages of lead and LDS reads never wait at a stage boundary.
+// The barrier's place in the odd stage (after NVFP4_MX_FIT_HALF of its MFMAs) was swept:
+// 1 to 4 alike, later ones slower (4608 x 3072 x 12288: 130 us at 4, 135 at 7, 141 at 11).
+#ifndef NVFP4_MX_FIT_HALF
+#define NVFP4_MX_FIT_HALF 4
+#endif
+
 template <int BM, int BN>
 struct alignas(16) MxFitSmem {
   static constexpr int kScaleRowsX = (BM + 63) / 64 * 64;
-  uint8_t x[4][BM * 64];
-  uint8_t w[4][BN * 64];
+  uint8_t x[2][BM * 128];
+  uint8_t w[2][BN * 128];
   uint8_t sc[2][(kScaleRowsX + BN) * 16];
 };
 
-// One wave's program; kS = number of middle-group blocks this wave owns (2 or 1).
 template <int BM, int BN, bool kRowwise, int kS, int kFw, int kFx>
 __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, BN>& sm, int lane,
-                                            int wave, int m0, int n0) {
+                                             int wave, int m0, int n0) {
   constexpr int NW = 4;
   constexpr int GX = BM / 32, GW = BN / 32;
   static_assert(GX * 32 == BM && GW * 32 == BN && GX % 2 == 1 && GW % 2 == 0, "fit tile shape");
@@ -369,22 +390,28 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   constexpr int FN = GW / 2;  // weight groups per wave
   constexpr int GS = FM;      // the middle activation group
   constexpr int kI0 = kS == FN - 1 ? 0 : FN - kS;  // first weight block of the middle group
-  constexpr int kPa = BM / 16, kPw = BN / 16;
-  constexpr int kPaW = (kPa + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW;
-  constexpr int kLoads = kPaW + kPwW;
+  constexpr int kPx = BM / 8, kPw = BN / 8;        // 1 KiB pieces per double stage
+  static_assert((kPx + kPw) % NW == 0, "code pieces divide among waves");
+  constexpr int kCode = (kPx + kPw) / NW;
   constexpr int kRowsSx = MxFitSmem<BM, BN>::kScaleRowsX;
   constexpr int kSx = kRowsSx / 64;
   static_assert(BN % 64 == 0 && (kSx + BN / 64) % NW == 0, "scale pieces divide among waves");
   constexpr int kSLoads = kRowwise ? 0 : (kSx + BN / 64) / NW;
   constexpr int kMfma = FN * FM + kS;
-  static_assert(kLoads + kSLoads <= kMfma && kLoads + kSLoads < 16, "loads fit the schedule");
+  constexpr int kHalf = NVFP4_MX_FIT_HALF;       // MFMAs of an odd stage before its barrier
+  static_assert(kHalf < kMfma, "the barrier sits inside the odd stage");
+  constexpr int kFrags = FN + FM + 1;
+  constexpr int kReads = 3 * kFrags;             // fragment halves and scale bytes per stage
+  constexpr int kTail = kMfma - kHalf;
+  constexpr int kCodePer = (kCode + kTail - 1) / kTail;
 
   const int wave_n = wave & 1;
   const int wave_m = wave >> 1;
   const int h = lane >> 5;
   const int r32 = lane & 31;
-  const int nk = (int)(p.K / 64);
-  const int ngrp = (nk + 7) >> 3;
+  const int nk = (int)(p.K / 64);  // stages (even: K % 128 == 0)
+  const int nd = nk >> 1;          // double stages
+  const int ngrp = (nk + 7) >> 3;  // scale groups of 8 stages
   const uint32_t pitch = (uint32_t)p.K;
   const uint32_t spitch = (uint32_t)(p.K >> 5);
 
@@ -394,19 +421,17 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
   const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
   const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  auto issue_codes = [&](int j, int stage, int buf) {
-    if (j < kPaW) {
-      const int i = min(j * NW + wave, kPa - 1);
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
-    } else {
-      const int i = min((j - kPaW) * NW + wave, kPw - 1);
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
-    }
+  // code piece j * NW + wave of double stage ds into buffer buf: activation pieces
+  // (rows 8i .. 8i+7), then weight pieces
+  auto issue_code = [&](int j, int ds, int buf) {
+    const int i = j * NW + wave;
+    if (i < kPx)
+      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, pitch), (uint32_t)ds * 128);
+    else
+      buffer_load_lds16(rwp, &sm.w[buf][(i - kPx) * 1024], x_piece_voff(lane, 8 * (i - kPx), pitch),
+                        (uint32_t)ds * 128);
   };
-  // scale piece j * NW + wave (64 rows x 16 bytes): activation rows first, then weight
-  // rows (selects, no branch)
+  // scale piece j * NW + wave (64 rows x 16 bytes): activation rows first, then weight rows
   auto issue_scales = [&](int j, int grp, int sbuf) {
     const int i = j * NW + wave;
     const bool isx = i < kSx;
@@ -427,26 +452,25 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
 #pragma unroll
     for (int v = 0; v < 16; ++v) accs[s][v] = 0.0f;
 
-  // fragments: weights FN, activations FM + the middle group (index FM)
   v8i_t wf[2][FN], xf[2][FM + 1];
   int wsc[2][FN], xsc[2][FM + 1];
-  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
-  const int fr1 = fr0 ^ 32;
+  const int rbase = (r32 >> 3) * 1024 + (r32 & 7) * 128;  // lane's row within a 32-row group
+  const int sw = x_swz(r32);
   const int xg0 = wave_m ? GS + 1 : 0;
-  // LDS reads of a stage in the order the MFMAs need them: w0, x0..x(FM-1), w1, .., the
-  // middle group last; read k is a fragment half or a scale byte
-  constexpr int kFrags = FN + FM + 1;
-  constexpr int kReads = 3 * kFrags;
-  auto read_one = [&](int k, int par, int buf, int stage) {
-    const int sbuf = (stage >> 3) & 1;
-    const int sbyte = (stage & 7) * 2 + h;
+  // read k of a stage (st: its index, for the buffer half and the scale byte): fragment
+  // halves in the order the MFMAs need them (w0, x0..x(FM-1), w1, .., the middle group
+  // last), each followed by its scale byte
+  auto read_one = [&](int k, int par, int buf, int st) {
+    const int sbuf = (st >> 3) & 1;
+    const int sbyte = (st & 7) * 2 + h;
     const int f = k / 3, part = k % 3;
     const bool is_w = f == 0 || (f > FM && f < kFrags - 1);
     const int idx = f == 0 ? 0 : (f <= FM ? f - 1 : (f < kFrags - 1 ? f - FM : FM));
     const int grp = is_w ? wave_n * FN + idx : (idx < FM ? xg0 + idx : GS);
-    const uint8_t* base = is_w ? &sm.w[buf][grp * 2048] : &sm.x[buf][grp * 2048];
     if (part < 2) {
-      const u32x4 a = *(const u32x4*)&base[part ? fr1 : fr0];
+      const int chunk = 4 * (st & 1) + 2 * part + h;
+      const uint8_t* base = is_w ? &sm.w[buf][grp * 4096] : &sm.x[buf][grp * 4096];
+      const u32x4 a = *(const u32x4*)&base[rbase + 16 * (chunk ^ sw)];
       const int o = 4 * part;
       if (is_w) {
         wf[par][idx][o] = (int)a.x; wf[par][idx][o + 1] = (int)a.y;
@@ -462,61 +486,81 @@ __device__ __forceinline__ void mx_fit_wave(const GemmProblem& p, MxFitSmem<BM, 
       else xsc[par][idx] = v;
     }
   };
+  auto mfma = [&](int q, int cur) {
+    if (q < FN * FM) {
+      const int i = q / FM, g = q % FM;
+      acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          wf[cur][i], xf[cur][g], acc[i][g], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
+          kRowwise ? 127 : xsc[cur][g]);
+    } else {
+      const int sidx = q - FN * FM, i = kI0 + sidx;
+      accs[sidx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          wf[cur][i], xf[cur][FM], accs[sidx], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
+          kRowwise ? 127 : xsc[cur][FM]);
+    }
+  };
 
+  // prologue: scales of group 0 and double stage 0, wait, then double stage 1's loads
+  // (a double stage past the last reloads the last one into the free buffer) and stage
+  // 0's fragments
 #pragma unroll
   for (int j = 0; j < kSLoads; ++j) issue_scales(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_codes(j, 0, 0);
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 1 ? 1 : nk - 1, 1);
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_codes(j, nk > 2 ? 2 : nk - 1, 2);
-  // scales and stages 0 and 1 (stage 0 reads stage 1's fragments ahead); stage 2's loads
-  // may still be in flight: the wait at the end of stage 0 covers them
-  wait_vmcnt<kLoads>();
+  for (int j = 0; j < kCode; ++j) issue_code(j, 0, 0);
+  wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int j = 0; j < kCode; ++j) issue_code(j, nd > 1 ? 1 : 0, 1);
 #pragma unroll
   for (int k = 0; k < kReads; ++k) read_one(k, 0, 0, 0);
 
-  auto stage = [&](int t, int buf, const int cur, const bool sload) {
-    const int nbuf = (buf + 1) & 3;
-    const int lbuf = (buf + 3) & 3;
-    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
-    const int rstage = t + 1 < nk ? t + 1 : t;
-    const int sgrp = (t >> 3) + 1 < ngrp ? (t >> 3) + 1 : ngrp - 1;
+  // double stage d in buffer buf (a constant); sload: d % 4 == 0, so stage 2d starts a
+  // scale group and the next group's scales load during it
+  auto dstage = [&](int d, const int buf, const bool sload) {
+    const int t0 = 2 * d;
+    const int sgrp = (t0 >> 3) + 1 < ngrp ? (t0 >> 3) + 1 : ngrp - 1;
+    // even stage: stage t0 + 1's fragments from the same buffer
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
-      if (q < FN * FM) {
-        const int i = q / FM, g = q % FM;
-        acc[i][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[cur][i], xf[cur][g], acc[i][g], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
-            kRowwise ? 127 : xsc[cur][g]);
-      } else {
-        const int sidx = q - FN * FM, i = kI0 + sidx;
-        accs[sidx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wf[cur][i], xf[cur][FM], accs[sidx], kFw, kFx, 0, kRowwise ? 127 : wsc[cur][i], 0,
-            kRowwise ? 127 : xsc[cur][FM]);
-      }
-      if (q < kLoads) issue_codes(q, lstage, lbuf);
-      else if (q < kLoads + kSLoads && sload) issue_scales(q - kLoads, sgrp, ((t >> 3) + 1) & 1);
+      mfma(q, 0);
+      if (sload && q < kSLoads) issue_scales(q, sgrp, ((t0 >> 3) + 1) & 1);
 #pragma unroll
-      for (int k = q * kReads / kMfma; k < (q + 1) * kReads / kMfma; ++k) read_one(k, cur ^ 1, nbuf, rstage);
+      for (int k = q * kReads / kMfma; k < (q + 1) * kReads / kMfma; ++k) read_one(k, 1, buf, t0 + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (sload) wait_vmcnt<kLoads + kSLoads>();
-    else wait_vmcnt<kLoads>();
-    __builtin_amdgcn_s_barrier();
-  };
-  int t = 0;
-  for (; t + 8 <= nk; t += 8) {
-    stage(t, 0, 0, true);
+    // odd stage: first part, then every load of double stage d + 1 landed and the barrier
 #pragma unroll
-    for (int u = 1; u < 8; ++u) stage(t + u, u & 3, u & 1, false);
+    for (int q = 0; q < kHalf; ++q) {
+      mfma(q, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    const int lds_ = d + 2 < nd ? d + 2 : nd - 1;  // double stage loaded into buf
+#pragma unroll
+    for (int q = kHalf; q < kMfma; ++q) {
+      mfma(q, 1);
+      const int u = q - kHalf;
+#pragma unroll
+      for (int l = 0; l < kCodePer; ++l)
+        if (u * kCodePer + l < kCode) issue_code(u * kCodePer + l, lds_, buf);
+      // (after the last double stage these reads fetch bytes nothing uses: reading
+      // unconditionally keeps the previous fragments from staying live)
+#pragma unroll
+      for (int k = u * kReads / kTail; k < (u + 1) * kReads / kTail; ++k) read_one(k, 0, buf ^ 1, t0 + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int d = 0;
+  for (; d + 4 <= nd; d += 4) {
+    dstage(d, 0, true);
+    dstage(d + 1, 1, false);
+    dstage(d + 2, 0, false);
+    dstage(d + 3, 1, false);
   }
-  for (; t < nk; t += 2) {
-    stage(t, t & 3, 0, false);
-    stage(t + 1, (t + 1) & 3, 1, false);
-  }
+  if (d < nd) dstage(d, 0, false);
+  if (d + 1 < nd) dstage(d + 1, 1, false);
+  if (d + 2 < nd) dstage(d + 2, 0, false);
 
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();

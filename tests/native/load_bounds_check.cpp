@@ -82,6 +82,22 @@ void code_pieces(Stats& st, const char* fam, int64_t rows, int64_t K, int tile, 
   (void)K;
 }
 
+// Direct-to-LDS pieces of 8 rows x 128 bytes (eight lanes per row, chunk (l % 8) ^
+// x_swz(row % 32)), scalar offset seg * 128: the W4A16 activations (pitch 2K, one stage per
+// segment) and the double-stage MXFP8 / fp8r codes (pitch K, two stages per segment).
+void row128_pieces(Stats& st, const char* fam, int64_t rows, int tile, uint32_t pitch, int nseg) {
+  for_tiles(rows, tile, [&](int64_t r0) {
+    for (int i = 0; i < tile / 8; ++i)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int seg = 0; seg < nseg; ++seg) {
+          const int xr = lane >> 3;
+          const int chunk = (lane & 7) ^ x_swz((8 * i + xr) & 31);
+          check_load(st, fam, rows, pitch, r0, x_piece_voff(lane, 8 * i, pitch), (uint32_t)seg * 128,
+                     16, r0 + 8 * i + xr, (int64_t)seg * 128 + 16 * chunk);
+        }
+  });
+}
+
 // Direct-to-LDS scale pieces: 64 rows x 16 bytes per piece at byte 16 * group of the row
 // (a pair of NVFP4 stages, or 8 MXFP8 stages), `srows` rows per tile (rounded up to whole
 // pieces, so the last piece may reach into the next tile).
@@ -241,6 +257,7 @@ int main(int argc, char** argv) {
         for (int tile : {288, 192, 256}) {
           const int nk = (int)(K / 64);
           code_pieces(st, "mxfp8-codes", R, K, tile, (uint32_t)K, nk);
+          if (tile != 256) row128_pieces(st, "mxfp8-codes-128", R, tile, (uint32_t)K, nk / 2);
           scale_pieces(st, "mxfp8-scales", R, tile, (tile + 63) / 64 * 64, (uint32_t)(K / 32), (nk + 7) / 8);
         }
     report("mxfp8", st, bad);
