@@ -20,11 +20,13 @@
 //    below an f16-staged design.
 //  * LDS layout of a packed tile: a lane reads its operand fragment for a 64-element
 //    chunk (row r, bytes [16h, 16h+16) of the chunk) with one 16-byte LDS load, free of
-//    bank conflicts. The direct-to-LDS kernels (288 x 192, 256 x 256, 128 x 192, 128 x 128
-//    and 128 x 64 tiles) keep each row's 64 bytes of a stage together in 1 KiB pieces of 16 rows with the 16-byte
-//    chunks swizzled (chunk_swz), because their loads read whole 64-byte row segments;
-//    the register-staged kernel stores 64 slots of 16 bytes per 32-row group and chunk
-//    in MFMA lane order.
+//    bank conflicts. The 288 x 192 kernel keeps each row's 128 bytes of a double stage
+//    together in 1 KiB pieces of 8 rows (16-byte chunks swizzled by x_swz), because its
+//    loads read whole 128-byte lines; the other direct-to-LDS kernels (256 x 256,
+//    128 x 192, 128 x 128 and 128 x 64 tiles) keep a row's 64 bytes of a stage in 1 KiB
+//    pieces of 16 rows (chunk_swz), their loads reading 64-byte row segments; the
+//    register-staged kernel stores 64 slots of 16 bytes per 32-row group and chunk in
+//    MFMA lane order.
 //  * K mapping: lane half h of a fragment feeds the MFMA's K slots [8h, 8h+8) with
 //    elements 32h + 8j .. 32h + 8j + 7 of the chunk on k-step j (j = 0..3). Both
 //    operands use the same mapping, so each product pairs equal k; each lane's 8
@@ -288,8 +290,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
 // 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
 // 2 x 3 for 128 x 192, 2 x 2 for 128 x 128 and 2 x 1 for 128 x 64 (medium M: more tiles,
 // so fewer rows still fill the chip, at a higher decode cost per MFMA). Loads, LDS image
-// and stage pipeline are the fit kernel's (below): code loads of 16 rows x the stage's
-// 64 bytes (4 lanes per row) into 1 KiB pieces whose 16-byte chunks are swizzled by
+// and stage pipeline: code loads of 16 rows x the stage's 64 bytes (4 lanes per row) into 1 KiB pieces whose 16-byte chunks are swizzled by
 // chunk_swz, scale loads of 64 rows x 16 bytes (a pair of stages) into three pair
 // buffers, four code buffers filled three stages ahead, one wait and barrier per stage;
 // range-checked buffer loads over row windows (window_rsrc), so a ragged tile needs no
@@ -504,35 +505,38 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
 // partial sums of group 4 meet in LDS.
 //
 // Loads. The direct-to-LDS path costs by the cache lines an instruction touches rather
-// than by its bytes, so a code load reads whole 64-byte row segments (16 rows x the
-// stage's 64 bytes, 4 lanes per row) and a scale load 64 rows x 16 bytes (the scales of
-// two stages).
+// than by its bytes (measured on the device: 88.6 GB/s per compute unit of L2-resident
+// data for 8 rows x 128 bytes per load, 51.3 for 16 rows x 64 bytes), so the codes are
+// loaded two stages (256 elements of K: a whole 128-byte line per row) at a time, 8 rows x
+// 128 bytes per load, and a double stage's scales (16 bytes per row) 64 rows per load.
+// LDS: two double-stage code buffers and two scale buffers (136 KiB); each row's 128
+// bytes as eight 16-byte chunks at slots q ^ x_swz(row % 32), so the fragment reads (lane
+// (h, r) of chunk c of the double stage reads 16-byte chunk 2c + h of row r) hit distinct
+// banks. Scales: activation rows (rounded up to whole 64-row pieces) first, then weight
+// rows. The double stage's byte offset along the row rides in the per-lane offset, so for
+// an odd number of stages the unused second half of the last double stage is
+// range-checked like any load (zero past the operand's end).
 //
-// LDS image of a stage: per 16-row piece 1 KiB, row r's 64 bytes (chunk 0, then chunk 1)
-// at 64 r, its 16-byte pieces q = 2 * chunk + half swizzled to slot q ^ chunk_swz(r).
-// Scales: 16 bytes per row for a pair of stages, activation rows (rounded up to whole
-// 64-row pieces) first, then weight rows; three pair buffers.
+// Pipeline over double stages d (stages 2d, 2d+1, buffers d & 1), each stage's chunks in
+// the wave's own order:
+//  * stage 2d reads its second chunk and then stage 2d+1's first chunk from the same
+//    buffer under its MFMAs;
+//  * stage 2d+1 reads its second chunk under its first k-steps; then the wave waits for
+//    all its loads (double stage d+1's, issued during stage 2d-1) with its LDS reads
+//    landed and meets the workgroup at a barrier, reads double stage d+1's first chunk,
+//    and issues double stage d+2's loads into buffer d & 1, whose reads all ended before
+//    the barrier.
+// Each k-step decodes the next one's fragments under its MFMAs.
 template <int BM, int BN>
 struct alignas(16) GemmSmemFit {
   static constexpr int kScaleRowsX = (BM + 63) / 64 * 64;
-  uint8_t x[4][BM * 64];  // activations: [stage buffer][16-row piece]
-  uint8_t w[4][BN * 64];  // weights
-  uint8_t sc[3][(kScaleRowsX + BN) * 16];  // scale bytes: [pair buffer][row][16]
+  uint8_t x[2][BM * 128];
+  uint8_t w[2][BN * 128];
+  uint8_t sc[2][(kScaleRowsX + BN) * 16];
 };
 
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
 // (rows + one tile) x K/2 below 2^31 for both operands (32-bit buffer offsets).
-//
-// Stage t lives in LDS buffer t % 4; its loads are issued during stage t-3, spread over
-// the first k-steps. At the end of stage t each wave waits until every load it issued
-// before stage t has landed (stages up to t+2; those for t+3 stay in flight) and the
-// workgroup meets at a barrier. So stage t+1 is complete in LDS throughout stage t, whose
-// second chunk reads stage t+1's first chunk and decodes its first k-step; and by the
-// barrier every wave has consumed its reads of stage t, whose buffer the loads issued
-// during stage t+1 overwrite. The scales of stage pair u (stages 2u, 2u+1) live in pair
-// buffer u % 3 and are loaded during stages 2u-4 and 2u-3 (one load per wave each), so
-// they are complete before stage 2u-1 first reads them, and their buffer's previous pair
-// was last read in stage 2u-5.
 template <int BM, int BN, bool kExp>
 __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int NW = 4;
@@ -545,19 +549,15 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   constexpr int kSteps = 8;   // 16-element k-steps per stage (two chunks of 4)
   __shared__ GemmSmemFit<BM, BN> sm;
 
-  // Loads per stage: one 16-byte load per lane fills a 16-row code piece of 1 KiB. Two
-  // lists (packed x, packed w); wave w takes entries j * NW + w of each. Every wave issues
-  // the same number of loads, so the vmcnt wait counts the same; entries past a list
-  // repeat its last one, which writes the same bytes to the same place. Plus one scale
-  // load per wave: a pair's 2 * NW scale pieces (64 rows x 16 bytes) over its two stages.
-  constexpr int kPa = BM / 16, kPw = BN / 16;
-  constexpr int kPaW = (kPa + NW - 1) / NW, kPwW = (kPw + NW - 1) / NW;
+  constexpr int kPx = BM / 8, kPw = BN / 8;  // 1 KiB code pieces per double stage
+  static_assert((kPx + kPw) % NW == 0, "code pieces divide among waves");
+  constexpr int kCode = (kPx + kPw) / NW;
   constexpr int kRowsSx = GemmSmemFit<BM, BN>::kScaleRowsX;
   constexpr int kSx = kRowsSx / 64;
-  static_assert(BN % 64 == 0 && kSx + BN / 64 == 2 * NW, "one scale load per wave and stage");
-  constexpr int kLoadsPerWave = kPaW + kPwW + 1;
-  static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
-  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
+  static_assert(BN % 64 == 0 && kSx + BN / 64 == 2 * NW, "two scale loads per wave and double stage");
+  constexpr int kLoads = kCode + 2;                   // per wave and double stage
+  static_assert(kLoads < 64, "a double stage of loads fits the vmcnt counter");
+  constexpr int kLoadsPerStep = (kLoads + 3) / 4;     // over the odd stage's last 4 k-steps
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -572,40 +572,32 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
-  const int nk = (int)(p.K / 128);
-  const int npair = (nk + 1) >> 1;
+  const int nk = (int)(p.K / 128);      // stages
+  const int nd = (nk + 1) >> 1;         // double stages (the last one half used when nk is odd)
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
-  // Buffer resources over the row windows [m0, M) and [n0, N): rows past M (or N) are
-  // out of range and read as zero, so a ragged last tile needs no clamping.
   const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, m0, p.M, pitch);
   const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
   const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
   const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  // Scale piece `half` * NW + wave of stage pair `pair` into pair buffer `sb`; pieces below
-  // kSx hold activation rows, the rest weight rows (selects, no branch).
-  auto issue_scale = [&](int pair, int half, int sb) {
-    const int i = half * NW + wave;
-    const bool isx = i < kSx;
-    const int prow = isx ? 64 * i : 64 * (i - kSx);
-    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024],
-                      scale_piece_voff(lane, prow, spitch, (uint32_t)pair * 16), 0);
-  };
-  // Load j of this wave in stage t: code pieces of stage `stage` into buffer `buf`, the
-  // last one the stage's scale piece (pair `spair` into pair buffer `sb`).
-  auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
-    if (j < kPaW) {
-      const int i = min(j * NW + wave, kPa - 1);
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
-    } else if (j < kPaW + kPwW) {
-      const int i = min((j - kPaW) * NW + wave, kPw - 1);
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
+  // Load j of this wave for double stage ds into buffer buf: code pieces (activation
+  // rows 8i .. 8i+7, then weight rows), then the two scale pieces (64 rows x 16 bytes;
+  // activation rows first, selects, no branch).
+  auto issue = [&](int j, int ds, int buf) {
+    if (j < kCode) {
+      const int i = j * NW + wave;
+      const bool isx = i < kPx;
+      const int prow = 8 * (isx ? i : i - kPx);
+      buffer_load_lds16(isx ? rxp : rwp, isx ? &sm.x[buf][i * 1024] : &sm.w[buf][(i - kPx) * 1024],
+                        x_piece_voff(lane, prow, pitch) + (uint32_t)ds * 128, 0);
     } else {
-      issue_scale(spair, t & 1, sb);
+      const int i = (j - kCode) * NW + wave;
+      const bool isx = i < kSx;
+      const int prow = isx ? 64 * i : 64 * (i - kSx);
+      buffer_load_lds16(isx ? rxs : rws, &sm.sc[buf][i * 1024],
+                        scale_piece_voff(lane, prow, spitch, (uint32_t)ds * 16), 0);
     }
   };
 
@@ -620,14 +612,12 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
   }
 
-  // Fragments of two chunks (by the wave's own chunk order: 0 = first, 1 = second) and
-  // decoded operands of two k-steps.
   const int xg0 = wave_m ? GS + 1 : 0;  // first whole activation group of this wave
-  // lane's 16-byte piece of chunk 0 within a 32-row group (2 KiB); chunk 1's is 32 over
-  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
-  const int wfrag = wave_n * FN * 2048;
-  const int xfrag = xg0 * 2048;
-  const int sfrag = GS * 2048;
+  const int rbase = (r32 >> 3) * 1024 + (r32 & 7) * 128;  // lane's row in a 32-row group
+  const int sw = x_swz(r32);
+  const int wfrag = wave_n * FN * 4096;
+  const int xfrag = xg0 * 4096;
+  const int sfrag = GS * 4096;
   const int wsw = (kRowsSx + wave_n * FN * 32 + r32) * 16 + 2 * h;  // scale byte offsets
   const int xsw = (xg0 * 32 + r32) * 16 + 2 * h;
   const int ssw = (GS * 32 + r32) * 16 + 2 * h;
@@ -635,22 +625,21 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
   uint32_t wsr[2][FN], xsr[2][FM], ssr;
   half2_t wsc[FN], xsc[FM], ssc;
   half8_t wf[2][FN], xf[2][FM], sf[2];
-  // read the fragments of chunk `c` (physical) of stage buffer `buf` as the wave's chunk
-  // `par`, with the scales of the stage (pair buffer `sb`, stage `sub` of the pair); the
-  // shared group only in its first chunk
-  auto read_chunk = [&](int par, int buf, int c, int sb, int sub) {
-    const int fr = fr0 ^ (32 * c);
+  // read chunk cc (physical, 0 or 1) of stage half hs of the double stage in buffer buf
+  // as the wave's chunk par; the shared group only in its first chunk
+  auto read_chunk = [&](int par, int buf, int hs, int cc) {
+    const int fr = rbase + 16 * ((2 * (2 * hs + cc) + h) ^ sw);
     const uint8_t* wb = &sm.w[buf][wfrag + fr];
     const uint8_t* xb = &sm.x[buf][xfrag + fr];
-    const uint8_t* scb = &sm.sc[sb][sub * 8 + c * 4];
+    const uint8_t* scb = &sm.sc[buf][hs * 8 + cc * 4];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[par][i] = *(const u32x4*)(wb + i * 2048);
+      wraw[par][i] = *(const u32x4*)(wb + i * 4096);
       wsr[par][i] = *(const uint16_t*)(scb + wsw + i * 512);
     }
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      xraw[par][f] = *(const u32x4*)(xb + f * 2048);
+      xraw[par][f] = *(const u32x4*)(xb + f * 4096);
       xsr[par][f] = *(const uint16_t*)(scb + xsw + f * 512);
     }
     if (par == 0) {
@@ -673,43 +662,40 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
     if (par == 0) sf[slot] = decode8<true>(sraw[j], j < 2 ? ssc.xx : ssc.yy);
   };
 
-  // prologue: scales of pairs 0 and 1, codes of stages 0, 1 and 2
-  issue_scale(0, 0, 0);
-  issue_scale(0, 1, 0);
-  issue_scale(npair > 1 ? 1 : 0, 0, 1);
-  issue_scale(npair > 1 ? 1 : 0, 1, 1);
+  // prologue: double stages 0 and 1 (a double stage past the last reloads the last into
+  // the free buffer); wait for 0 (1 may stay in flight), read its first chunk
 #pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, 0, 0, 0, 0, 0);
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
-#pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
-  // stages 0 and 1 (stage 0 reads stage 1's first chunk ahead); stage 2's loads may
-  // still be in flight: the wait at the end of stage 0 covers them
-  wait_vmcnt<kPaW + kPwW>();
+  for (int j = 0; j < kLoads; ++j) issue(j, nd > 1 ? 1 : 0, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 15) | ((kLoads >> 4) << 14));
   __builtin_amdgcn_s_barrier();
-  read_chunk(0, 0, wave_m, 0, 0);
+  read_chunk(0, 0, 0, wave_m);
   decode_step(0, 0, 0);
 
-  int buf = 0;
-  for (int t = 0; t < nk; ++t) {
-    const int nbuf = (buf + 1) & 3;  // stage t + 1 (complete since the end of stage t - 2)
-    const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
-    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
-    const int pair = t >> 1;
-    const int sb = pair % 3, sbn = ((t + 1) >> 1) % 3;        // pair buffers of t and t + 1
-    const int spair = pair + 2 < npair ? pair + 2 : npair - 1;  // pair loaded in this stage
-    const int sbl = (pair + 2) % 3;
+  // stage half hs (a constant) of double stage d in buffer b (a constant)
+  auto stage = [&](int d, const int b, const int hs) {
+    const int lds_ = d + 2 < nd ? d + 2 : nd - 1;  // double stage loaded into b at the end
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;
       const int par = st >> 2, j = st & 3;
+      if (st == 0) read_chunk(1, b, hs, wave_m ^ 1);  // this stage's second chunk
+      if (st == 4) {
+        if (hs == 0) {
+          read_chunk(0, b, 1, wave_m);  // stage 2d+1's first chunk, same buffer
+        } else {
+          // vmcnt(0) and lgkmcnt(0): double stage d+1 loaded, this wave's reads of b done
+          __builtin_amdgcn_s_waitcnt(0x0070);
+          __builtin_amdgcn_s_barrier();
+          read_chunk(0, b ^ 1, 0, wave_m);  // double stage d+1's first chunk
+        }
+      }
+      const bool loads = hs == 1 && st >= 4;
+      if (loads) {
 #pragma unroll
-      for (int l = 0; l < kLoadsPerStep; ++l)
-        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf, t, spair, sbl);
-      if (j == 0) {  // the wave's second chunk of this stage, or its first of the next
-        if (par == 0) read_chunk(1, buf, wave_m ^ 1, sb, t & 1);
-        else read_chunk(0, nbuf, wave_m, sbn, (t + 1) & 1);
+        for (int l = 0; l < kLoadsPerStep; ++l)
+          if ((st - 4) * kLoadsPerStep + l < kLoads) issue((st - 4) * kLoadsPerStep + l, lds_, b);
       }
       decode_step(((st + 1) >> 2) & 1, (st + 1) & 3, cur ^ 1);
 #pragma unroll
@@ -726,20 +712,27 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
         if (q < nmfma) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           if (j == 0 && q < kReads / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-          if (q < kLoadsPerStep && st * kLoadsPerStep + q < kLoadsPerWave)
+          if (loads && q < kLoadsPerStep && (st - 4) * kLoadsPerStep + q < kLoads)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
           __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<kLoadsPerWave>();
-    __builtin_amdgcn_s_barrier();
-    buf = nbuf;
+  };
+  int d = 0;
+  for (; 2 * d + 4 <= nk; d += 2) {
+    stage(d, 0, 0);
+    stage(d, 0, 1);
+    stage(d + 1, 1, 0);
+    stage(d + 1, 1, 1);
   }
+  if (2 * d < nk) stage(d, 0, 0);
+  if (2 * d + 1 < nk) stage(d, 0, 1);
+  if (2 * d + 2 < nk) stage(d + 1, 1, 0);
 
   // The two partial sums of the shared group: drain the last (unused) loads, then swap
-  // them through LDS (the stage buffers are free now).
+  // them through LDS (the buffers are free now).
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   float* xch = (float*)&sm.x[0][0];

@@ -83,17 +83,22 @@ void code_pieces(Stats& st, const char* fam, int64_t rows, int64_t K, int tile, 
 }
 
 // Direct-to-LDS pieces of 8 rows x 128 bytes (eight lanes per row, chunk (l % 8) ^
-// x_swz(row % 32)), scalar offset seg * 128: the W4A16 activations (pitch 2K, one stage per
-// segment) and the double-stage MXFP8 / fp8r codes (pitch K, two stages per segment).
-void row128_pieces(Stats& st, const char* fam, int64_t rows, int tile, uint32_t pitch, int nseg) {
+// x_swz(row % 32)) at byte seg * 128 of the row: the W4A16 activations (pitch 2K, one stage
+// per segment, scalar offset) and the double-stage MXFP8 / fp8r codes (pitch K, two
+// stages per segment, scalar offset), or, with seg_in_voff, the double-stage NVFP4 codes
+// (pitch K/2, the segment's offset in the per-lane offset: the last segment of an odd
+// stage count reaches past the row's end).
+void row128_pieces(Stats& st, const char* fam, int64_t rows, int tile, uint32_t pitch, int nseg,
+                   bool seg_in_voff = false) {
   for_tiles(rows, tile, [&](int64_t r0) {
     for (int i = 0; i < tile / 8; ++i)
       for (int lane = 0; lane < 64; ++lane)
         for (int seg = 0; seg < nseg; ++seg) {
           const int xr = lane >> 3;
           const int chunk = (lane & 7) ^ x_swz((8 * i + xr) & 31);
-          check_load(st, fam, rows, pitch, r0, x_piece_voff(lane, 8 * i, pitch), (uint32_t)seg * 128,
-                     16, r0 + 8 * i + xr, (int64_t)seg * 128 + 16 * chunk);
+          const uint32_t so = (uint32_t)seg * 128;
+          check_load(st, fam, rows, pitch, r0, x_piece_voff(lane, 8 * i, pitch) + (seg_in_voff ? so : 0),
+                     seg_in_voff ? 0 : so, 16, r0 + 8 * i + xr, (int64_t)so + 16 * chunk);
         }
   });
 }
@@ -227,7 +232,12 @@ int main(int argc, char** argv) {
     const int64_t Ks[] = {128, 384, 640, 3072};
     for (int64_t R : rows_list)
       for (int64_t K : Ks)
-        for (int tile : {288, 192, 256, 128, 64}) code_pieces(st, "nvfp4-codes", R, K, tile, (uint32_t)(K / 2), (int)(K / 128));
+        for (int tile : {288, 192, 256, 128, 64}) {
+          code_pieces(st, "nvfp4-codes", R, K, tile, (uint32_t)(K / 2), (int)(K / 128));
+          // the fit tile's double-stage loads (an odd stage count leaves half a segment)
+          if (tile == 288 || tile == 192)
+            row128_pieces(st, "nvfp4-codes-128", R, tile, (uint32_t)(K / 2), (int)(K / 128 + 1) / 2, true);
+        }
     report("nvfp4-code-pieces", st, bad);
   }
   {
