@@ -284,23 +284,22 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmProblem p) {
   store_tile<FM, FN, kExp>(acc, p, gemm_alpha(p), m0 + wave_m * WTM, n0 + wave_n * WTN, lane);
 }
 
-// ---- 256 x 256 and 128 x 192 tiles: direct-to-LDS loads, four code stages, one pipeline
-// across stages ----
+// ---- 256 x 256, 128 x 192, 128 x 128 and 128 x 64 tiles: direct-to-LDS loads ----------
 //
 // 2 x 2 waves of BM/2 x BN/2: 4 x 4 blocks of 32 x 32 for 256 x 256 (the large-M tile),
 // 2 x 3 for 128 x 192, 2 x 2 for 128 x 128 and 2 x 1 for 128 x 64 (medium M: more tiles,
 // so fewer rows still fill the chip, at a higher decode cost per MFMA). Loads, LDS image
-// and stage pipeline: code loads of 16 rows x the stage's 64 bytes (4 lanes per row) into 1 KiB pieces whose 16-byte chunks are swizzled by
-// chunk_swz, scale loads of 64 rows x 16 bytes (a pair of stages) into three pair
-// buffers, four code buffers filled three stages ahead, one wait and barrier per stage;
-// range-checked buffer loads over row windows (window_rsrc), so a ragged tile needs no
-// clamping. 4 x 32 KiB + 3 x 8 KiB = 152 KiB of LDS at 256 x 256, 4 x 20 KiB + 3 x 5 KiB
-// = 95 KiB at 128 x 192.
+// and pipeline are the 288 x 192 kernel's (below): codes two stages at a time in 8-row x
+// 128-byte pieces (x_swz chunk swizzle), a double stage's scales in 64-row x 16-byte
+// pieces, two double-stage code buffers and two scale buffers, one wait and barrier per
+// double stage inside its second stage; range-checked buffer loads over row windows
+// (window_rsrc), so a ragged tile needs no clamping. 2 x 64 KiB + 2 x 8 KiB = 144 KiB of
+// LDS at 256 x 256, 2 x 40 KiB + 2 x 5 KiB = 90 KiB at 128 x 192.
 template <int BM, int BN>
 struct alignas(16) GemmSmem256 {
-  uint8_t x[4][BM * 64];
-  uint8_t w[4][BN * 64];
-  uint8_t sc[3][(BM + BN) * 16];
+  uint8_t x[2][BM * 128];
+  uint8_t w[2][BN * 128];
+  uint8_t sc[2][(BM + BN) * 16];
 };
 
 // Requires K % 128 == 0, 16-byte aligned packed operands, 4-byte aligned scales, and
@@ -312,15 +311,15 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int kSteps = 8;  // 16-element k-steps per stage (two chunks of 4)
-  constexpr int kPa = BM / 16, kPw = BN / 16;
-  static_assert(kPa % NW == 0 && kPw % NW == 0, "code pieces divide among waves");
-  constexpr int kPaW = kPa / NW, kPwW = kPw / NW;
-  constexpr int kSx = BM / 64;
-  constexpr int kSp = kSx + BN / 64;  // scale pieces per pair of stages
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && kSp <= 2 * NW, "one scale load per wave and stage");
-  constexpr int kLoadsPerWave = kPaW + kPwW + 1;
-  static_assert(kLoadsPerWave < 16, "one stage of loads fits the vmcnt immediate");
-  constexpr int kLoadsPerStep = (kLoadsPerWave + kSteps - 3) / (kSteps - 2);
+  constexpr int kPx = BM / 8, kPw = BN / 8;  // 1 KiB code pieces per double stage
+  static_assert((kPx + kPw) % NW == 0, "code pieces divide among waves");
+  constexpr int kCode = (kPx + kPw) / NW;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 64-row scale pieces");
+  constexpr int kSp = (BM + BN) / 64;             // scale pieces per double stage
+  constexpr int kScale = (kSp + NW - 1) / NW;     // per wave (the last piece repeated)
+  constexpr int kLoads = kCode + kScale;
+  static_assert(kLoads < 64, "a double stage of loads fits the vmcnt counter");
+  constexpr int kLoadsPerStep = (kLoads + 3) / 4;  // over the odd stage's last 4 k-steps
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -335,8 +334,8 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
-  const int nk = (int)(p.K / 128);
-  const int npair = (nk + 1) >> 1;
+  const int nk = (int)(p.K / 128);  // stages
+  const int nd = (nk + 1) >> 1;     // double stages
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
@@ -346,26 +345,23 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
   const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
   const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  // scale piece half * NW + wave of a pair (slots past the last piece repeat it, writing
-  // the same bytes to the same place)
-  auto issue_scale = [&](int pair, int half, int sb) {
-    const int i = min(half * NW + wave, kSp - 1);
-    const bool isx = i < kSx;
-    const int prow = isx ? 64 * i : 64 * (i - kSx);
-    buffer_load_lds16(isx ? rxs : rws, &sm.sc[sb][i * 1024],
-                      scale_piece_voff(lane, prow, spitch, (uint32_t)pair * 16), 0);
-  };
-  auto issue = [&](int j, int stage, int buf, int t, int spair, int sb) {
-    if (j < kPaW) {
+  // load j of this wave for double stage ds into buffer buf: code pieces (activation
+  // rows 8i .. 8i+7, then weight rows), then scale pieces (64 rows x 16 bytes, activation
+  // rows first; slots past the last piece repeat it, writing the same bytes to the same
+  // place)
+  auto issue = [&](int j, int ds, int buf) {
+    if (j < kCode) {
       const int i = j * NW + wave;
-      buffer_load_lds16(rxp, &sm.x[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
-    } else if (j < kPaW + kPwW) {
-      const int i = (j - kPaW) * NW + wave;
-      buffer_load_lds16(rwp, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch),
-                        (uint32_t)stage * 64);
+      const bool isx = i < kPx;
+      const int prow = 8 * (isx ? i : i - kPx);
+      buffer_load_lds16(isx ? rxp : rwp, isx ? &sm.x[buf][i * 1024] : &sm.w[buf][(i - kPx) * 1024],
+                        x_piece_voff(lane, prow, pitch) + (uint32_t)ds * 128, 0);
     } else {
-      issue_scale(spair, t & 1, sb);
+      const int i = min((j - kCode) * NW + wave, kSp - 1);
+      const bool isx = i < BM / 64;
+      const int prow = isx ? 64 * i : 64 * (i - BM / 64);
+      buffer_load_lds16(isx ? rxs : rws, &sm.sc[buf][i * 1024],
+                        scale_piece_voff(lane, prow, spitch, (uint32_t)ds * 16), 0);
     }
   };
 
@@ -377,29 +373,31 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
 
-  // fragments of two chunks (by chunk order) and decoded operands of two k-steps
-  const int fr0 = (r32 >> 4) * 1024 + (r32 & 15) * 64 + 16 * (h ^ chunk_swz(r32 & 15));
-  const int wfrag = wave_n * FN * 2048;
-  const int xfrag = wave_m * FM * 2048;
+  // fragments of two chunks and decoded operands of two k-steps
+  const int rbase = (r32 >> 3) * 1024 + (r32 & 7) * 128;  // lane's row in a 32-row group
+  const int sw = x_swz(r32);
+  const int wfrag = wave_n * FN * 4096;
+  const int xfrag = wave_m * FM * 4096;
   const int wsw = (BM + wave_n * WTN + r32) * 16 + 2 * h;
   const int xsw = (wave_m * WTM + r32) * 16 + 2 * h;
   u32x4 wraw[2][FN], xraw[2][FM];
   uint32_t wsr[2][FN], xsr[2][FM];
   half2_t wsc[FN], xsc[FM];
   half8_t wf[2][FN], xf[2][FM];
-  auto read_chunk = [&](int par, int buf, int c, int sb, int sub) {
-    const int fr = fr0 ^ (32 * c);
+  // chunk c of stage half hs of the double stage in buffer buf, as chunk par
+  auto read_chunk = [&](int par, int buf, int hs, int c) {
+    const int fr = rbase + 16 * ((2 * (2 * hs + c) + h) ^ sw);
     const uint8_t* wb = &sm.w[buf][wfrag + fr];
     const uint8_t* xb = &sm.x[buf][xfrag + fr];
-    const uint8_t* scb = &sm.sc[sb][sub * 8 + c * 4];
+    const uint8_t* scb = &sm.sc[buf][hs * 8 + c * 4];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[par][i] = *(const u32x4*)(wb + i * 2048);
+      wraw[par][i] = *(const u32x4*)(wb + i * 4096);
       wsr[par][i] = *(const uint16_t*)(scb + wsw + i * 512);
     }
 #pragma unroll
     for (int g = 0; g < FM; ++g) {
-      xraw[par][g] = *(const u32x4*)(xb + g * 2048);
+      xraw[par][g] = *(const u32x4*)(xb + g * 4096);
       xsr[par][g] = *(const uint16_t*)(scb + xsw + g * 512);
     }
   };
@@ -416,50 +414,45 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
     for (int g = 0; g < FM; ++g) xo[g] = decode8<true>(xraw[par][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
   };
 
-  // prologue: scales of pairs 0 and 1, codes of stages 0, 1 and 2
-  issue_scale(0, 0, 0);
-  issue_scale(0, 1, 0);
-  issue_scale(npair > 1 ? 1 : 0, 0, 1);
-  issue_scale(npair > 1 ? 1 : 0, 1, 1);
+  // prologue: double stages 0 and 1 (a double stage past the last reloads the last into
+  // the free buffer); wait for 0 (1 may stay in flight), read its first chunk
 #pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, 0, 0, 0, 0, 0);
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 1 ? 1 : nk - 1, 1, 0, 0, 0);
-#pragma unroll
-  for (int j = 0; j < kPaW + kPwW; ++j) issue(j, nk > 2 ? 2 : nk - 1, 2, 0, 0, 0);
-  // stages 0 and 1 (stage 0 reads stage 1's first chunk ahead); stage 2's loads may
-  // still be in flight: the wait at the end of stage 0 covers them
-  wait_vmcnt<kPaW + kPwW>();
+  for (int j = 0; j < kLoads; ++j) issue(j, nd > 1 ? 1 : 0, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 15) | ((kLoads >> 4) << 14));
   __builtin_amdgcn_s_barrier();
-  read_chunk(0, 0, 0, 0, 0);
+  read_chunk(0, 0, 0, 0);
   decode_step(0, 0, wf[0], xf[0]);
 
   constexpr int kMfmaPerStep = FN * FM;
   constexpr int kReadsPerChunk = 2 * (FN + FM);
-  int buf = 0;
-  for (int t = 0; t < nk; ++t) {
-    const int nbuf = (buf + 1) & 3;  // stage t + 1 (complete since the end of stage t - 1)
-    const int lbuf = (buf + 3) & 3;  // stage t + 3 (its buffer held stage t - 1)
-    const int lstage = t + 3 < nk ? t + 3 : nk - 1;
-    const int pair = t >> 1;
-    const int sb = pair % 3, sbn = ((t + 1) >> 1) % 3;
-    const int spair = pair + 2 < npair ? pair + 2 : npair - 1;
-    const int sbl = (pair + 2) % 3;
+  // stage half hs (a constant) of double stage d in buffer b (a constant)
+  auto stage = [&](int d, const int b, const int hs) {
+    const int lds_ = d + 2 < nd ? d + 2 : nd - 1;  // double stage loaded into b at the end
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;
-      const int chunk = st >> 2, j = st & 3;
+      const int j = st & 3;
+      if (st == 0) read_chunk(1, b, hs, 1);  // this stage's second chunk
+      if (st == 4) {
+        if (hs == 0) {
+          read_chunk(0, b, 1, 0);  // stage 2d+1's first chunk, same buffer
+        } else {
+          // vmcnt(0) and lgkmcnt(0): double stage d+1 loaded, this wave's reads of b done
+          __builtin_amdgcn_s_waitcnt(0x0070);
+          __builtin_amdgcn_s_barrier();
+          read_chunk(0, b ^ 1, 0, 0);  // double stage d+1's first chunk
+        }
+      }
+      const bool loads = hs == 1 && st >= 4;
+      if (loads) {
 #pragma unroll
-      for (int l = 0; l < kLoadsPerStep; ++l)
-        if (st * kLoadsPerStep + l < kLoadsPerWave) issue(st * kLoadsPerStep + l, lstage, lbuf, t, spair, sbl);
-      const bool reads = j == 0;
-      if (reads) {  // next chunk: the second of this stage, then the first of the next
-        if (chunk == 0) read_chunk(1, buf, 1, sb, t & 1);
-        else read_chunk(0, nbuf, 0, sbn, (t + 1) & 1);
+        for (int l = 0; l < kLoadsPerStep; ++l)
+          if ((st - 4) * kLoadsPerStep + l < kLoads) issue((st - 4) * kLoadsPerStep + l, lds_, b);
       }
       // decode of the next k-step (the first k-step of the next stage after the last)
-      if (st + 1 < kSteps) decode_step((st + 1) >> 2 & 1, (st + 1) & 3, wf[cur ^ 1], xf[cur ^ 1]);
-      else decode_step(0, 0, wf[cur ^ 1], xf[cur ^ 1]);
+      decode_step(((st + 1) >> 2) & 1, (st + 1) & 3, wf[cur ^ 1], xf[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -468,19 +461,26 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
 #pragma unroll
       for (int q = 0; q < kMfmaPerStep; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        if (reads && q < kReadsPerChunk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        if (q < kLoadsPerStep && st * kLoadsPerStep + q < kLoadsPerWave)
+        if (j == 0 && q < kReadsPerChunk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (loads && q < kLoadsPerStep && (st - 4) * kLoadsPerStep + q < kLoads)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS
         __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_GEMM_VALU_PER_MFMA, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<kLoadsPerWave>();
-    __builtin_amdgcn_s_barrier();
-    buf = nbuf;
+  };
+  int d = 0;
+  for (; 2 * d + 4 <= nk; d += 2) {
+    stage(d, 0, 0);
+    stage(d, 0, 1);
+    stage(d + 1, 1, 0);
+    stage(d + 1, 1, 1);
   }
+  if (2 * d < nk) stage(d, 0, 0);
+  if (2 * d + 1 < nk) stage(d, 0, 1);
+  if (2 * d + 2 < nk) stage(d + 1, 1, 0);
 
-  // drain the last (unused) loads before the stage buffers stage the stores
+  // drain the last (unused) loads before the code buffers stage the stores
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");

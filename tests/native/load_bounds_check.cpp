@@ -232,12 +232,9 @@ int main(int argc, char** argv) {
     const int64_t Ks[] = {128, 384, 640, 3072};
     for (int64_t R : rows_list)
       for (int64_t K : Ks)
-        for (int tile : {288, 192, 256, 128, 64}) {
-          code_pieces(st, "nvfp4-codes", R, K, tile, (uint32_t)(K / 2), (int)(K / 128));
-          // the fit tile's double-stage loads (an odd stage count leaves half a segment)
-          if (tile == 288 || tile == 192)
-            row128_pieces(st, "nvfp4-codes-128", R, tile, (uint32_t)(K / 2), (int)(K / 128 + 1) / 2, true);
-        }
+        // every tile's double-stage loads (an odd stage count leaves half a segment)
+        for (int tile : {288, 192, 256, 128, 64})
+          row128_pieces(st, "nvfp4-codes-128", R, tile, (uint32_t)(K / 2), (int)(K / 128 + 1) / 2, true);
     report("nvfp4-code-pieces", st, bad);
   }
   {
