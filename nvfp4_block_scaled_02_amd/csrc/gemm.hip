@@ -1178,14 +1178,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   const int64_t t12864 = ((M + 127) / 128) * ((N + 63) / 64);
   const double c12864 = fast ? (double)passes(t12864, cus) * (nk * 16 * mfma_cycles(1.5) + 20000.0) : 1e300;
   // Split K inside the workgroup (short activations, at most 512 rows: it reads the
-  // activations once per 32 weight rows, which stops paying beyond that). Measured cost:
-  // ~6000 cycles of launch and reduction plus, per pass over the chip, 360 / 740 / 1100
-  // cycles per 128 elements of K for 32-row groups B = 1 / 2 / 4 per workgroup.
+  // activations once per 32 weight rows, which stops paying beyond that). Measured cost,
+  // in the units of the tile costs above (the 128 x 128 tile's): ~6000 cycles of launch
+  // and reduction plus, per pass over the chip, 680 / 1110 / 2000 per 128 elements of K
+  // for 32-row groups B = 1 / 2 / 4 per workgroup (M = 17, 64 and 256 at K = 3072,
+  // against the double-stage tiles).
   const bool split_ok = aligned && K % 32 == 0 && fits32;
   const SplitShape sh = splitk_shape(M);
   const int64_t wsplit = ((N + 31) / 32) * ((M + 32 * sh.b - 1) / (32 * sh.b));
   const double csplit = 6000.0 + (double)passes(wsplit, cus) * ((double)K / 128.0) *
-                                     (sh.b == 1 ? 360.0 : sh.b == 2 ? 740.0 : 1100.0);
+                                     (sh.b == 1 ? 680.0 : sh.b == 2 ? 1110.0 : 2000.0);
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
   if (fast || fit_ok) {

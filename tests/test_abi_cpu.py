@@ -108,7 +108,7 @@ def test_gemm_validation(lib):
 
 def test_gemm_plan_routes_shapes(lib):
     """The planner (host only) sends the FLUX activations (4608 rows) to the 288 x 192
-    tile, short activations to split-K, and shapes whose tile count fits 256-tile passes
+    tile, short activations (at most 64 rows, or a few rows of wide weights) to split-K, and shapes whose tile count fits 256-tile passes
     better to the 256 x 256 tile; K % 128 != 0 needs the register-staged kernel."""
     def plan(M, N, K, cus=0):
         k = ctypes.c_int(-1)
@@ -119,11 +119,14 @@ def test_gemm_plan_routes_shapes(lib):
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
                     (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
-    for M in (1, 17, 256):
+    for M in (1, 17, 64):
         assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    for M in (128, 256):   # the 128 x 64 tile overtakes split-K beyond 64 rows
+        assert plan(M, 3072, 3072) == (L.SUCCESS, T12864), M
     # wide weights with few rows: split-K's workgroups still fill the chip
-    for M, N in [(1, 18432), (17, 18432), (64, 18432)]:
+    for M, N in [(1, 18432), (17, 18432)]:
         assert plan(M, N, 3072) == (L.SUCCESS, SPLIT), (M, N)
+    assert plan(64, 18432, 3072) == (L.SUCCESS, T128SQ)
     assert plan(128, 12288, 3072) == (L.SUCCESS, T12864)
     assert plan(256, 12288, 3072) == (L.SUCCESS, T128SQ)
     assert plan(512, 12288, 3072) == (L.SUCCESS, T128)
