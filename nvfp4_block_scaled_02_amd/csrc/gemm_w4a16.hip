@@ -515,33 +515,36 @@ __global__ void __launch_bounds__(256) gemm_w4a16_fit_kernel(W4A16Problem p) {
 // groups and seven activation groups, 14 MFMAs per k-step as in the 288 x 192 tile, but
 // every weight group is decoded by one wave only (the 2 x 2 layouts decode each weight
 // group in both wave rows), and a stage moves 13% fewer bytes per product. 4608 rows make
-// 21 tile rows (the last one 128 rows); every FLUX width is a multiple of 256. The 128 x 128
-// and 64 x 128 forms (one weight group per wave) serve short and medium activations.
+// 21 tile rows (the last one 128 rows); every FLUX width is a multiple of 256. The smaller
+// forms (128 x 256, 96 x 256, 128 x 128, 64 x 128) serve short and medium activations.
 //
-// Loads. The direct-to-LDS path costs about the same per 64-byte row segment an
-// instruction touches, whatever the bytes used (measured across these tile shapes), so
-// the weights' scales, 4 bytes per row and stage, are loaded 16 bytes per row for four
-// stages at once (64 rows per load) into two quad buffers; activations take 8 rows x 128
-// bytes per load, weight codes 32 rows x 32 bytes. Four code stage buffers; stage t+3's
-// loads are issued during stage t.
+// Loads. Direct-to-LDS loads cost by the cache lines they touch, so every load reads whole
+// row segments: activations 8 rows x 128 bytes (a stage of one row: a whole line), weight
+// codes 16 rows x 64 bytes (two stages of one row), the weights' scales 64 rows x 16 bytes
+// (four stages: 4 bytes per row and stage). Loads go by double stage (128 elements of K):
+// two double-stage buffers for the codes (each holding its two stages' activations and
+// the weight rows' 64 bytes, 16-byte chunks swizzled by chunk_swz), two quad buffers for
+// the scales. A double stage's byte offset rides in the per-lane offset, so when the
+// stage count is odd the unused half of the last double stage is range-checked (zero past
+// the operand's end).
+//
+// Pipeline over double stages d (stages 2d, 2d+1, buffers d & 1): each k-step reads and
+// decodes the next k-step's fragments under its MFMAs; stage 2d's last k-step reads stage
+// 2d+1's weights and first activation fragments (same buffer); in stage 2d+1's last
+// k-step the wave first waits for all its loads (double stage d+1's, issued a double
+// stage earlier) with its LDS reads landed and meets the workgroup at the double stage's
+// one barrier, then reads double stage d+1's first fragments and issues double stage
+// d+2's loads into buffer d & 1, whose reads all ended before the barrier.
 template <int BM, int BN>
 struct alignas(16) W4A16WideSmem {
-  uint8_t x[4][BM * 128];
-  uint8_t w[4][BN * 32];
+  uint8_t x[2][2][BM * 128];  // [double stage buffer][stage of the pair][rows]
+  uint8_t w[2][BN * 64];
   uint8_t ws[2][BN * 16];
 };
 
 #ifndef NVFP4_W4A16_VALU_PER_MFMA
 #define NVFP4_W4A16_VALU_PER_MFMA 4
 #endif
-
-// s_waitcnt with vmcnt(n) (n < 64: the counter's low four bits and its two high bits at
-// 15:14) and lgkmcnt(0) when kLds, expcnt left free.
-template <int n, bool kLds>
-__device__ __forceinline__ void wait_vm_wide() {
-  static_assert(n >= 0 && n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((kLds ? 0x0070 : 0x0F70) | (n & 15) | ((n >> 4) << 14));
-}
 
 // Requires K % 64 == 0, 16-byte aligned x, codes and out, 4-byte aligned scales, and
 // (M + BM) * K * 2 and (N + BN) * K / 2 below 2^31 (32-bit buffer offsets). The grid is
@@ -551,14 +554,24 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   constexpr int NW = 4;
   __shared__ W4A16WideSmem<BM, BN> sm;
   constexpr int FM = BM / 32, FN = BN / NW / 32;
-  constexpr int kPx = BM / 8, kPw = BN / 32, kPs = BN / 64;  // pieces per stage / quad
+  constexpr int kPx = 2 * (BM / 8), kPw = BN / 16, kPs = BN / 64;  // pieces per double stage / quad
   static_assert(FM * 32 == BM && FN * 32 * NW == BN && BN % 64 == 0, "tile shape");
   static_assert(kPx % NW == 0 && kPw % NW == 0 && kPs <= NW, "loads divide among waves");
   constexpr int kPxW = kPx / NW, kPwW = kPw / NW;
-  constexpr int kCode = kPxW + kPwW;  // code loads per wave and stage
-  // loads issued during a stage whose target stage (t + 3) starts a quad: one more
-  constexpr int kPerStep = (kCode + 1 + 3) / 4;  // loads placed per k-step
-  static_assert(2 * kCode + 1 < 64, "two stages of loads fit the vmcnt counter");
+  constexpr int kCode = kPxW + kPwW;              // code loads per wave and double stage
+  constexpr int kLoads = kCode + 1;               // with a quad's scale piece
+  static_assert(2 * kLoads < 64, "two double stages of loads fit the vmcnt counter");
+  constexpr int kMfma = FN * FM;
+  // A double stage's loads in two parts: the first kPartA after the barrier of the double
+  // stage two before it (spread over the MFMAs of that last k-step), the rest over the
+  // next stage (the first stage of the double stage before it). Tiles with few MFMAs per
+  // k-step (64 x 128) have short stages and issue all of them after the barrier: their
+  // second part would have too little lead (measured, 256 x 3072 x 12288: 63.3 us split,
+  // 59.8 all after the barrier).
+  constexpr int kPartA = kMfma >= 4 ? (kMfma < kCode ? kMfma : kCode) : kLoads;
+  constexpr int kPerA = (kPartA + kMfma - 1) / kMfma;
+  constexpr int kPerSlotB = kPartA >= kLoads ? 0 : (kLoads - kPartA + 4 * kMfma - 1) / (4 * kMfma);
+  static_assert(kPartA < 16, "the prologue's wait fits the vmcnt immediate");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -584,8 +597,9 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
     tile_n = r / rows;
   }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  const int nk = (int)(p.K / 64);
-  const int nquad = (nk + 3) >> 2;
+  const int nk = (int)(p.K / 64);   // stages
+  const int nd = (nk + 1) >> 1;     // double stages
+  const int nquad = (nk + 3) >> 2;  // scale quads (two double stages)
   const uint32_t xpitch = (uint32_t)(p.K * 2), pitch = (uint32_t)(p.K >> 1), spitch = (uint32_t)(p.K >> 4);
 
   // row windows [m0, M) and [n0, N) (see window_rsrc): rows past M or N read as zero
@@ -593,25 +607,25 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   const __amdgpu_buffer_rsrc_t rw = window_rsrc(p.w_packed, n0, p.N, pitch);
   const __amdgpu_buffer_rsrc_t rs = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  // Load j of this wave for target stage ts (the stage it fills; clamped to the last one
-  // for the loads past the end, which land in buffers no stage reads): activation pieces,
-  // weight pieces, then, when ts starts a quad, the scale piece of that quad (waves past
-  // the last piece repeat it: the same bytes to the same LDS place). A last quad shorter
-  // than four stages reads past its rows' ends: range-checked like every load.
-  auto issue = [&](int j, int ts) {
-    const int buf = ts & 3;
-    const int stage = ts < nk ? ts : nk - 1;
+  // Load j of this wave for double stage ds into buffer buf: activation pieces (stage
+  // half, then rows 8i .. 8i+7), weight pieces (rows 16i .. 16i+15), then, when ds starts
+  // a quad (ds even), that quad's scale piece (waves past the last piece repeat it: the
+  // same bytes to the same LDS place). Loads for a double stage past the last reload the
+  // last into a buffer no stage reads.
+  auto issue = [&](int j, int dsn, int buf) {
+    const int ds = dsn < nd ? dsn : nd - 1;
     if (j < kPxW) {
-      const int i = j * NW + wave;  // rows 8i .. 8i+7 of the tile
-      buffer_load_lds16(rx, &sm.x[buf][i * 1024], x_piece_voff(lane, 8 * i, xpitch), (uint32_t)stage * 128);
+      const int i = j * NW + wave;
+      const int half = i / (BM / 8), pi = i % (BM / 8);
+      buffer_load_lds16(rx, &sm.x[buf][half][pi * 1024],
+                        x_piece_voff(lane, 8 * pi, xpitch) + (uint32_t)(2 * ds + half) * 128, 0);
     } else if (j < kCode) {
-      const int i = (j - kPxW) * NW + wave;  // weight group i: lane (h, r) row 32i + r, half h
-      buffer_load_lds16(rw, &sm.w[buf][i * 1024], (uint32_t)(32 * i + r32) * pitch + h * 16u,
-                        (uint32_t)stage * 32);
+      const int i = (j - kPxW) * NW + wave;
+      buffer_load_lds16(rw, &sm.w[buf][i * 1024], code_piece_voff(lane, 16 * i, pitch) + (uint32_t)ds * 64, 0);
     } else {
       const int i = min(wave, kPs - 1);  // weight rows 64i .. 64i+63
-      const int quad = min(ts >> 2, nquad - 1);
-      buffer_load_lds16(rs, &sm.ws[(ts >> 2) & 1][i * 1024],
+      const int quad = min(dsn >> 1, nquad - 1);
+      buffer_load_lds16(rs, &sm.ws[(dsn >> 1) & 1][i * 1024],
                         scale_piece_voff(lane, 64 * i, spitch, (uint32_t)quad * 16), 0);
     }
   };
@@ -625,21 +639,26 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
       for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
 
   const int xs0 = 16 * ((4 * h) ^ x_swz(r32));  // k-step j: slot offset xs0 ^ (16 j)
+  // lane's 16-byte weight chunk (stage half hs: chunk 2 hs + h) within a group of 32 rows
+  const int wrow = (r32 >> 4) * 1024 + (r32 & 15) * 64;
+  const int wsw = chunk_swz(r32 & 15);
   // weight codes and scale bytes of two stages (by stage parity), fragments of two k-steps
   u32x4 wraw[2][FN];
   uint32_t wsb[2][FN];
   bf16x8_t wf[2][FN], xf[2][FM];
-  auto read_w = [&](int ws, int ts) {
+  // stage st: double stage buffer buf, stage half hs = st & 1, scale quad st >> 2
+  auto read_w = [&](int ws, int buf, int st) {
+    const int hs = st & 1;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      wraw[ws][i] = *(const u32x4*)&sm.w[ts & 3][(wave * FN + i) * 1024 + lane * 16];
-      wsb[ws][i] = *(const uint16_t*)&sm.ws[(ts >> 2) & 1][(wave * FN * 32 + i * 32 + r32) * 16 + 4 * (ts & 3) + 2 * h];
+      wraw[ws][i] = *(const u32x4*)&sm.w[buf][(wave * FN + i) * 2048 + wrow + 16 * ((2 * hs + h) ^ wsw)];
+      wsb[ws][i] = *(const uint16_t*)&sm.ws[(st >> 2) & 1][(wave * FN * 32 + i * 32 + r32) * 16 + 4 * (st & 3) + 2 * h];
     }
   };
-  auto read_x = [&](int slot, int buf, int j) {
+  auto read_x = [&](int slot, int buf, int hs, int j) {
 #pragma unroll
     for (int g = 0; g < FM; ++g) {
-      const u32x4 v = *(const u32x4*)&sm.x[buf][g * 4096 + r32 * 128 + (xs0 ^ (16 * j))];
+      const u32x4 v = *(const u32x4*)&sm.x[buf][hs][g * 4096 + r32 * 128 + (xs0 ^ (16 * j))];
       xf[slot][g] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
@@ -653,82 +672,91 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
     }
   };
 
-  // prologue: stages 0, 1 and 2 and the scales of quad 0, then stage 0's first k-step.
-  // Outstanding after it: stages 1 and 2's code loads.
+  // prologue: double stages 0 and 1 (quad 0's scales with 0); wait for 0, read stage 0's
+  // weights and first activation fragments
 #pragma unroll
-  for (int j = 0; j <= kCode; ++j) issue(j, 0);
+  for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
+  constexpr int kPartA1 = kPartA < kCode ? kPartA : kCode;  // double stage 1 has no quad
 #pragma unroll
-  for (int j = 0; j < kCode; ++j) issue(j, 1);
-#pragma unroll
-  for (int j = 0; j < kCode; ++j) issue(j, 2);
-  wait_vm_wide<2 * kCode, false>();
+  for (int j = 0; j < kPartA1; ++j) issue(j, 1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kPartA1);
   __builtin_amdgcn_s_barrier();
-  read_w(0, 0);
-  read_x(0, 0, 0);
+  read_w(0, 0, 0);
+  read_x(0, 0, 0, 0);
   decode_w(0, 0, 0);
 
-  // One stage; ph = t % 4 (a constant). Each k-step issues its share of stage t+3's loads
-  // and reads and decodes the next k-step's fragments under its MFMAs. Before the last
-  // k-step's MFMAs the wave waits for stage t+1's loads (issued during stage t-2; those of
-  // stages t+2 and t+3 may stay in flight) with its own LDS reads of stage t landed, and
-  // meets the workgroup at a barrier; then it reads stage t+1's weights and first k-step.
-  // The barrier also orders every read of stage t's buffers before stage t+4's loads reuse
-  // them (a quad buffer is reused four stages after its last read).
-  auto stage = [&](int t, const int ph) {
-    const int ws = ph & 1;
-    const int buf = t & 3;
-    const bool quad_load = ((ph + 3) & 3) == 0;  // stage t + 3 starts a quad
-    const int nl = kCode + (quad_load ? 1 : 0);
-    // loads of stages t+2 (issued during t-1) and t+3 (issued during t)
-    const bool quad_prev = ((ph + 2) & 3) == 0;
-    const bool more = t + 1 < nk;
+  // stage half hs (a constant) of double stage d in buffer bb = d & 1 (a constant); ws = hs
+  auto stage = [&](int d, const int bb, const int hs) {
+    const int st = 2 * d + hs;
+    // loads of this stage: part A of double stage d+2 (odd stage, after the barrier) or
+    // part B of double stage d+1 (even stage); a double stage of even index starts a quad
+    const int lds_ = hs == 1 ? d + 2 : d + 1;
+    const int lbuf = hs == 1 ? bb : bb ^ 1;
+    const int nl = (hs == 1 ? bb == 0 : bb == 1) ? kLoads : kCode;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cur = j & 1;
-#pragma unroll
-      for (int l = 0; l < kPerStep; ++l)
-        if (j * kPerStep + l < nl) issue(j * kPerStep + l, t + 3);
+      const bool loads = hs == 0 || j == 3;
       if (j < 3) {
-        read_x(cur ^ 1, buf, j + 1);
-        decode_w(cur ^ 1, ws, j + 1);
+        read_x(cur ^ 1, bb, hs, j + 1);
+        decode_w(cur ^ 1, hs, j + 1);
+      } else if (hs == 0) {
+        read_w(1, bb, st + 1);  // stage 2d+1, same buffer
+        read_x(0, bb, 1, 0);
+        decode_w(0, 1, 0);
       } else {
-        if (quad_load || quad_prev) wait_vm_wide<2 * kCode + 1, true>();
-        else wait_vm_wide<2 * kCode, true>();
+        // vmcnt(0) and lgkmcnt(0): double stage d+1 loaded, this wave's reads of bb done
+        __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
-        if (more) {
-          read_w(ws ^ 1, t + 1);
-          read_x(0, (t + 1) & 3, 0);
-          decode_w(0, ws ^ 1, 0);
-        }
+        read_w(0, bb ^ 1, st + 1);  // double stage d+1's first stage
+        read_x(0, bb ^ 1, 0, 0);
+        decode_w(0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int g = 0; g < FM; ++g)
           acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][g], acc[i][g], 0, 0, 0);
-      // order: one MFMA, then an LDS read, a global->LDS load and VALU work, so the
-      // matrix pipe never waits behind a burst; on the last k-step the decode starts
-      // after four MFMAs, once the next stage's weight reads have landed
+      // order: one MFMA, then an LDS read, global->LDS loads and VALU work; after the
+      // barrier the decode starts once the reads have had four MFMAs to land
 #pragma unroll
-      for (int qq = 0; qq < FN * FM; ++qq) {
+      for (int qq = 0; qq < kMfma; ++qq) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         if (qq < FM + 2 * FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        if (qq < kPerStep && j * kPerStep + qq < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (loads && hs == 1) {
+#pragma unroll
+          for (int l = 0; l < kPerA; ++l) {
+            const int idx = qq * kPerA + l;
+            if (idx < kPartA && idx < nl) {
+              issue(idx, lds_, lbuf);
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+          }
+        } else if (loads && kPerSlotB > 0) {
+#pragma unroll
+          for (int l = 0; l < kPerSlotB; ++l) {
+            const int idx = kPartA + (j * kMfma + qq) * kPerSlotB + l;
+            if (idx < nl) {
+              issue(idx, lds_, lbuf);
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+          }
+        }
         if (j < 3 || qq >= 4) __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_W4A16_VALU_PER_MFMA, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  int t = 0;
-  for (; t + 4 <= nk; t += 4) {
-    stage(t, 0);
-    stage(t + 1, 1);
-    stage(t + 2, 2);
-    stage(t + 3, 3);
+  int d = 0;
+  for (; 2 * d + 4 <= nk; d += 2) {
+    stage(d, 0, 0);
+    stage(d, 0, 1);
+    stage(d + 1, 1, 0);
+    stage(d + 1, 1, 1);
   }
-  if (t < nk) stage(t, 0);
-  if (t + 1 < nk) stage(t + 1, 1);
-  if (t + 2 < nk) stage(t + 2, 2);
+  if (2 * d < nk) stage(d, 0, 0);
+  if (2 * d + 1 < nk) stage(d, 0, 1);
+  if (2 * d + 2 < nk) stage(d + 1, 1, 0);
 
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
@@ -740,7 +768,7 @@ __global__ void __launch_bounds__(256) gemm_w4a16_wide_kernel(W4A16Problem p) {
   gq.alpha = p.alpha;
   static_assert(NW * 32 * kStoreRowPad(FN) * 2 <= sizeof(sm.x), "store staging fits");
   store_tile_lds<FM, FN>(acc, gq, Alpha{gq.alpha, 0}, (int64_t)m0, (int64_t)n0 + wave * FN * 32,
-                         lane, (uint16_t*)&sm.x[0][0] + wave * 32 * kStoreRowPad(FN));
+                         lane, (uint16_t*)&sm.x[0][0][0] + wave * 32 * kStoreRowPad(FN));
 }
 
 }  // namespace

@@ -64,19 +64,21 @@ void for_tiles(int64_t rows, int tile, const std::function<void(int64_t)>& f) {
   for (int64_t r0 = 0; r0 < rows; r0 += tile) f(r0);
 }
 
-// Direct-to-LDS code pieces (NVFP4 fit / 256 / 128 tiles: pitch K/2; MXFP8: pitch K):
-// 16 rows x 64 bytes per piece, scalar offset stage * 64.
+// Direct-to-LDS code pieces of 16 rows x 64 bytes at byte seg * 64 of the row: MXFP8's
+// 256 x 256 tile (pitch K, scalar offset), or, with seg_in_voff, the W4A16 weight codes of
+// a double stage (pitch K/2, the offset in the per-lane offset).
 void code_pieces(Stats& st, const char* fam, int64_t rows, int64_t K, int tile, uint32_t pitch,
-                 int nstage) {
+                 int nstage, bool seg_in_voff = false) {
   for_tiles(rows, tile, [&](int64_t r0) {
     for (int i = 0; i < tile / 16; ++i)
       for (int lane = 0; lane < 64; ++lane)
         for (int stage = 0; stage < nstage; ++stage) {
-          const uint32_t voff = code_piece_voff(lane, 16 * i, pitch);
+          const uint32_t so = (uint32_t)stage * 64;
+          const uint32_t voff = code_piece_voff(lane, 16 * i, pitch) + (seg_in_voff ? so : 0);
           const int lr = lane >> 2;
           const int chunk = (lane & 3) ^ chunk_swz(lr);
-          check_load(st, fam, rows, pitch, r0, voff, (uint32_t)stage * 64, 16, r0 + 16 * i + lr,
-                     (int64_t)stage * 64 + 16 * chunk);
+          check_load(st, fam, rows, pitch, r0, voff, seg_in_voff ? 0 : so, 16, r0 + 16 * i + lr,
+                     (int64_t)so + 16 * chunk);
         }
   });
   (void)K;
@@ -151,11 +153,10 @@ void splitk(Stats& st, int64_t rows, int64_t K, int ngrp) {
   });
 }
 
-// W4A16 tiled kernels: activation pieces of 8 rows x 128 bytes (xpitch 2K, scalar offset
-// stage * 128), weight groups of 32 rows x 32 bytes (stage * 32); scale pieces of 64 rows
-// x 4 bytes (stage * 4) for the 256 x 256 and 288 x 192 tiles, or (quad_scales, the tiles
-// with their waves along N) 64 rows x 16 bytes for four stages at byte 16 * quad; K % 64 == 0.
-void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN, bool quad_scales = false) {
+// W4A16 256 x 256 and 288 x 192 kernels: activation pieces of 8 rows x 128 bytes (xpitch
+// 2K, scalar offset stage * 128), weight groups of 32 rows x 32 bytes (stage * 32), scale
+// pieces of 64 rows x 4 bytes (stage * 4); K % 64 == 0.
+void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN) {
   const uint32_t xpitch = (uint32_t)(2 * K), pitch = (uint32_t)(K / 2), spitch = (uint32_t)(K / 16);
   const int nk = (int)(K / 64);
   for_tiles(M, BM, [&](int64_t m0) {
@@ -175,13 +176,11 @@ void w4a16_tiled(Stats& st, int64_t M, int64_t N, int64_t K, int BM, int BN, boo
         for (int i = 0; i < BN / 32; ++i)
           check_load(st, "w4a16-w", N, pitch, n0, (uint32_t)(32 * i + r32) * pitch + h * 16u,
                      (uint32_t)stage * 32, 16, n0 + 32 * i + r32, (int64_t)stage * 32 + 16 * h);
-        if (!quad_scales)
-          for (int i = 0; i < (BN + 63) / 64; ++i)
-            check_load(st, "w4a16-s", N, spitch, n0, (uint32_t)(64 * i + lane) * spitch,
-                       (uint32_t)stage * 4, 4, n0 + 64 * i + lane, (int64_t)stage * 4);
+        for (int i = 0; i < (BN + 63) / 64; ++i)
+          check_load(st, "w4a16-s", N, spitch, n0, (uint32_t)(64 * i + lane) * spitch,
+                     (uint32_t)stage * 4, 4, n0 + 64 * i + lane, (int64_t)stage * 4);
       }
   });
-  if (quad_scales) scale_pieces(st, "w4a16-quad-s", N, BN, BN, spitch, (nk + 3) / 4);
 }
 
 // W4A16 split-K: window of 32 B activation rows at m0 and 32 weight rows at n0; lane
@@ -277,9 +276,17 @@ int main(int argc, char** argv) {
         for (int64_t K : Ks) {
           w4a16_tiled(st, M, N, K, 256, 256);
           w4a16_tiled(st, M, N, K, 288, 192);
-          w4a16_tiled(st, M, N, K, 224, 256, true);
-          w4a16_tiled(st, M, N, K, 128, 128, true);
-          w4a16_tiled(st, M, N, K, 64, 128, true);
+          // the tiles along N: activations by stage, weight codes and scales by double
+          // stage and quad, offsets in the per-lane offset
+          for (int bm : {224, 128, 96, 64}) {
+            const int nk = (int)(K / 64), nd = (nk + 1) / 2;
+            row128_pieces(st, "w4a16-x", M, bm, (uint32_t)(2 * K), 2 * nd, true);
+          }
+          for (int bn : {256, 128}) {
+            const int nk = (int)(K / 64), nd = (nk + 1) / 2;
+            code_pieces(st, "w4a16-w", N, K, bn, (uint32_t)(K / 2), nd, true);
+            scale_pieces(st, "w4a16-quad-s", N, bn, bn, (uint32_t)(K / 16), (nk + 3) / 4);
+          }
         }
     report("w4a16-tiled", st, bad);
   }
