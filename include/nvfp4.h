@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 /* Status codes. All argument validation happens before any HIP call. */
 typedef enum nvfp4_status {
@@ -133,8 +133,10 @@ typedef enum {
                              hundred to a few thousand rows */
   NVFP4_GEMM_TILE128X128 = 5, /* 128 x 128 output tiles (K % 128 == 0): more tiles, where
                                  the larger ones would leave compute units idle */
-  NVFP4_GEMM_TILE128X64 = 6    /* 128 x 64 output tiles (K % 128 == 0): more still, for a few
+  NVFP4_GEMM_TILE128X64 = 6,   /* 128 x 64 output tiles (K % 128 == 0): more still, for a few
                                  hundred rows */
+  NVFP4_GEMM_WSPLIT64 = 7      /* 64 x 64 output tiles whose four waves split K (K % 512 == 0):
+                                 a few hundred activation rows against a narrow weight */
 } nvfp4_gemm_kernel;
 
 /*

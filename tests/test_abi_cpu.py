@@ -108,21 +108,30 @@ def test_gemm_validation(lib):
 
 def test_gemm_plan_routes_shapes(lib):
     """The planner (host only) sends the FLUX activations (4608 rows) to the 288 x 192
-    tile, short activations (at most 64 rows, or a few rows of wide weights) to split-K, and shapes whose tile count fits 256-tile passes
-    better to the 256 x 256 tile; K % 128 != 0 needs the register-staged kernel."""
+    tile, short activations (at most 32 rows, or a few rows of wide weights) to split-K, a
+    few hundred rows whose 64 x 64 tiles fit one pass to the kernel whose waves split K,
+    and shapes whose tile count fits 256-tile passes better to the 256 x 256 tile;
+    K % 128 != 0 needs the register-staged kernel."""
     def plan(M, N, K, cus=0):
         k = ctypes.c_int(-1)
         st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864 = 1, 0, 2, 3, 4, 5, 6
+    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864, WS64 = 1, 0, 2, 3, 4, 5, 6, 7
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
                     (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
-    for M in (1, 17, 64):
+    for M in (1, 17, 32):
         assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
-    for M in (128, 256):   # the 128 x 64 tile overtakes split-K beyond 64 rows
-        assert plan(M, 3072, 3072) == (L.SUCCESS, T12864), M
+    # beyond 32 rows, while its 64 x 64 tiles fit one pass over the compute units, the
+    # kernel whose waves split K
+    for M in (64, 128, 256, 320):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, WS64), M
+    for M in (64, 256):
+        assert plan(M, 3072, 12288) == (L.SUCCESS, WS64), M
+    assert plan(64, 12288, 3072) == (L.SUCCESS, WS64)
+    assert plan(256, 3072, 3072, 128) == (L.SUCCESS, T12864)   # two passes on 128 units
+    assert plan(256, 3072, 3000) != (L.SUCCESS, WS64)            # K % 512 != 0
     # wide weights with few rows: split-K's workgroups still fill the chip
     for M, N in [(1, 18432), (17, 18432)]:
         assert plan(M, N, 3072) == (L.SUCCESS, SPLIT), (M, N)
@@ -134,7 +143,7 @@ def test_gemm_plan_routes_shapes(lib):
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128), M
     for M in (800, 1000):   # about a thousand rows: 128 x 128 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128SQ), M
-    for M in (300, 512, 600):   # a few hundred rows: 128 x 64 tiles
+    for M in (384, 512, 600):   # a few hundred rows past one pass of 64 x 64: 128 x 64 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T12864), M
     assert plan(2600, 1650, 128) == (L.SUCCESS, T128)
     assert plan(4096, 4096, 128) == (L.SUCCESS, TILE)

@@ -78,6 +78,11 @@ def test_gemm_small_shapes_in_full(M, N, K):
     (1000, 2900, 640, "tile128x128"),
     # 128 x 64 tiles: a few hundred rows
     (513, 1000, 640, "tile128x64"), (777, 385, 1152, "tile128x64"), (600, 700, 256, "tile128x64"),
+    # 64 x 64 tiles whose waves split K: 1 to 7 sets of four stages (each way the last
+    # sets are run), ragged rows and columns
+    (700, 90, 512, "wsplit64"), (65, 1000, 1024, "wsplit64"), (130, 777, 1536, "wsplit64"),
+    (200, 64, 2048, "wsplit64"), (257, 1500, 2560, "wsplit64"), (100, 500, 3072, "wsplit64"),
+    (320, 3072, 3584, "wsplit64"),
     (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])
@@ -132,6 +137,7 @@ _EXTREME_PAIRS = [
 @pytest.mark.parametrize("pair", range(len(_EXTREME_PAIRS)))
 @pytest.mark.parametrize("M,N,K,kernel", [
     (64, 128, 128, "splitk"), (600, 700, 256, "tile128x64"), (1500, 2500, 128, "tile128x128"),
+    (130, 777, 1536, "wsplit64"),
     (2600, 1650, 384, "tile128"), (2600, 3000, 128, "fit"), (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])
@@ -167,7 +173,7 @@ def _sample_rows(M, rng, n=48):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["tiny", "attn_out", "mlp_up_static", "odd_m17", "odd_m1000"])
+@pytest.mark.parametrize("name", ["tiny", "attn_out", "mlp_up_static", "odd_m17", "odd_m256", "odd_m1000"])
 def test_linear_matches_quantize_then_gemm(name):
     wl = make(name)
     d = wl.generate()

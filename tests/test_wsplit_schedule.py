@@ -1,0 +1,110 @@
+"""The set schedule of the 64 x 64 GEMM whose waves split K (``gemm_wsplit_kernel`` in
+``csrc/gemm.hip``), checked on the host for every number of sets from 1 to 12.
+
+The kernel loads a set (four stages of K) into one of two LDS buffer pairs while the waves
+compute the previous one. All four waves run the same sequence of loads, waits, barriers
+and LDS reads, so the schedule is modelled as one event list in which a barrier is a point
+every wave reaches; the checks are the ones the kernel's correctness rests on:
+
+* every set is loaded once, into the pair its compute reads;
+* a pair is read for a set only after that set's loads were waited for (each wave waits
+  for its own loads) and a barrier followed, and before anything else is loaded into it;
+* loads into a pair start only after a barrier that follows the last read of what the pair
+  held before;
+* the epilogue reuses the LDS only after a barrier that follows every read and every
+  wait for the loads.
+"""
+import pytest
+
+
+def schedule(nset):
+    """The kernel's event list: ("load", set, pair), ("wait",), ("barrier",),
+    ("read", set, pair), ("reduce",)."""
+    ev = []
+    ev.append(("load", 0, 0))
+    if nset > 1:
+        ev.append(("load", 1, 1))
+        ev.append(("wait", 0))       # vmcnt(kLoads): set 0 landed, set 1 may be in flight
+    else:
+        ev.append(("wait", None))    # vmcnt(0)
+    ev.append(("barrier",))
+    ev.append(("read", 0, 0))        # set 0's first chunk
+
+    def run_set(t, pr, loads, last):
+        ev.append(("read", t, pr))   # k-step 0: the stage's second chunk
+        if not last:                 # k-step 4
+            ev.append(("wait", None))
+            ev.append(("barrier",))
+            ev.append(("read", t + 1, pr ^ 1))
+        if loads:                    # k-steps 4 .. 7
+            ev.append(("load", t + 2, pr))
+
+    t = 0
+    while t + 4 <= nset:
+        run_set(t, 0, True, False)
+        run_set(t + 1, 1, True, False)
+        t += 2
+    rest = nset - t
+    if rest == 3:
+        run_set(t, 0, True, False)
+        run_set(t + 1, 1, False, False)
+        run_set(t + 2, 0, False, True)
+    elif rest == 2:
+        run_set(t, 0, False, False)
+        run_set(t + 1, 1, False, True)
+    else:
+        assert rest == 1
+        run_set(t, 0, False, True)
+    ev.append(("wait", None))
+    ev.append(("barrier",))
+    ev.append(("reduce",))
+    return ev
+
+
+@pytest.mark.parametrize("nset", range(1, 13))
+def test_wsplit_set_schedule(nset):
+    ev = schedule(nset)
+    content = {0: None, 1: None}          # set last loaded into each pair
+    outstanding = []                      # loads issued and not yet waited for, in order
+    landed_unsynced = set()               # sets waited for by the waves, no barrier since
+    visible = set()                       # sets every wave may read
+    last_read = {0: -2, 1: -2}            # event index of the last read of each pair (none yet)
+    last_barrier = -1
+    loaded = []
+    reads = {}
+    for i, e in enumerate(ev):
+        kind = e[0]
+        if kind == "load":
+            _, s, p = e
+            assert s < nset, f"set {s} past the end is loaded"
+            assert last_read[p] < last_barrier, f"set {s} loaded into pair {p} before a barrier after its last read"
+            content[p] = s
+            visible.discard(s)
+            outstanding.append(s)
+            loaded.append(s)
+        elif kind == "wait":
+            if e[1] is None:
+                landed_unsynced.update(outstanding)
+                outstanding = []
+            else:
+                # vmcnt(kLoads): all but the most recent set's loads have landed
+                landed_unsynced.update(outstanding[:-1])
+                outstanding = outstanding[-1:]
+                assert e[1] in landed_unsynced
+        elif kind == "barrier":
+            visible |= landed_unsynced
+            landed_unsynced = set()
+            last_barrier = i
+        elif kind == "read":
+            _, s, p = e
+            if s >= nset:
+                continue
+            assert content[p] == s, f"set {s} read from pair {p} holding set {content[p]}"
+            assert s in visible, f"set {s} read before its loads were waited for and synchronized"
+            last_read[p] = i
+            reads[s] = reads.get(s, 0) + 1
+        elif kind == "reduce":
+            assert not outstanding, "loads in flight when the LDS is reused"
+            assert max(last_read.values()) < last_barrier, "LDS reused before a barrier after the last read"
+    assert sorted(loaded) == list(range(nset)), f"sets loaded: {sorted(loaded)}"
+    assert all(reads.get(s) == 2 for s in range(nset)), f"chunk reads per set: {reads}"
