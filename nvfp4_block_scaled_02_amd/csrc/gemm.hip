@@ -14,19 +14,18 @@
 // bits), so f16 (2.5 PFLOP/s dense) is the fastest exact MFMA type.
 //
 // Structure:
-//  * Packed 4-bit tiles and scale bytes stream from HBM into LDS (four stage buffers in
-//    the direct-to-LDS kernels, two in the register-staged one); decode happens in
-//    registers right before the MFMA, so LDS holds 4-bit data and its traffic stays 4x
-//    below an f16-staged design.
+//  * Packed 4-bit tiles and scale bytes stream from HBM into LDS (the direct-to-LDS
+//    kernels load two stages of K, 256 elements or one 128-byte line of codes per row, at
+//    a time into double-stage buffers; the register-staged kernel has two stage buffers);
+//    decode happens in registers right before the MFMA, so LDS holds 4-bit data and its
+//    traffic stays 4x below an f16-staged design.
 //  * LDS layout of a packed tile: a lane reads its operand fragment for a 64-element
 //    chunk (row r, bytes [16h, 16h+16) of the chunk) with one 16-byte LDS load, free of
-//    bank conflicts. The 288 x 192 kernel keeps each row's 128 bytes of a double stage
-//    together in 1 KiB pieces of 8 rows (16-byte chunks swizzled by x_swz), because its
-//    loads read whole 128-byte lines; the other direct-to-LDS kernels (256 x 256,
-//    128 x 192, 128 x 128 and 128 x 64 tiles) keep a row's 64 bytes of a stage in 1 KiB
-//    pieces of 16 rows (chunk_swz), their loads reading 64-byte row segments; the
-//    register-staged kernel stores 64 slots of 16 bytes per 32-row group and chunk in
-//    MFMA lane order.
+//    bank conflicts. The direct-to-LDS kernels (288 x 192, 256 x 256, 128 x 192,
+//    128 x 128, 128 x 64, and the 64 x 64 tile whose waves split K) keep each row's 128
+//    bytes of a double stage together in 1 KiB pieces of 8 rows (16-byte chunks swizzled
+//    by x_swz), because their loads read whole 128-byte lines; the register-staged kernel
+//    stores 64 slots of 16 bytes per 32-row group and chunk in MFMA lane order.
 //  * K mapping: lane half h of a fragment feeds the MFMA's K slots [8h, 8h+8) with
 //    elements 32h + 8j .. 32h + 8j + 7 of the chunk on k-step j (j = 0..3). Both
 //    operands use the same mapping, so each product pairs equal k; each lane's 8
@@ -39,12 +38,14 @@
 //    lane ends up holding 4 consecutive output columns of one row.
 //  * Epilogue: fp32 accumulator * a_global * w_global (one fp32 multiply; split_alpha
 //    adds an exact power-of-two ldexp for scale pairs whose product leaves the normal
-//    binary32 range), round to nearest even bf16. The direct-to-LDS kernels pass each
-//    32-row group of a wave's blocks through LDS and store 16-byte row pieces; the
-//    others store each lane's 8 bytes directly.
+//    binary32 range), round to nearest even bf16. The tiled direct-to-LDS kernels pass
+//    each 32-row group of a wave's blocks through LDS and store 16-byte row pieces; the
+//    others (and the 64 x 64 tile, after adding its partial tiles) store each lane's 8
+//    bytes directly.
 //  * Short activations (split-K kernel): K is split over the waves of a workgroup and
 //    the partial sums meet in LDS; nvfp4_linear's fused form quantizes the activations
-//    into LDS first.
+//    into LDS first. A few hundred rows: 64 x 64 tiles whose four waves each compute the
+//    whole tile over a quarter of K, their partial tiles added in LDS.
 #include "gemm_common.hpp"
 #include "quant_common.hpp"
 
