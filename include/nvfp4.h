@@ -135,8 +135,10 @@ typedef enum {
                                  the larger ones would leave compute units idle */
   NVFP4_GEMM_TILE128X64 = 6,   /* 128 x 64 output tiles (K % 128 == 0): more still, for a few
                                  hundred rows */
-  NVFP4_GEMM_WSPLIT64 = 7      /* 64 x 64 output tiles whose four waves split K (K % 512 == 0):
+  NVFP4_GEMM_WSPLIT64 = 7,     /* 64 x 64 output tiles whose four waves split K (K % 512 == 0):
                                  a few hundred activation rows against a narrow weight */
+  NVFP4_GEMM_WSPLIT128 = 8     /* 128 x 128 output tiles, two row bands of two waves that
+                                 split K (K % 256 == 0): about a thousand rows, long K */
 } nvfp4_gemm_kernel;
 
 /*

@@ -495,53 +495,66 @@ __global__ void __launch_bounds__(256) gemm_dma_kernel(GemmProblem p) {
 // A few hundred activation rows fill the chip only with small tiles (64 or 128 rows);
 // shared 2 x 2 among the waves those give each wave one or two blocks per operand, 1 to 1.5
 // decoded fragments per MFMA, and the decode instead of the matrix pipe sets the pace.
-// Here every wave computes the whole BM x BN tile (FM x FN blocks: one fragment per MFMA
-// at 64 x 64) over every fourth stage of K: a set is four stages (two double stages) and wave w
-// takes stage 4t + w of set t. Loads and LDS image are the 256 x 256 kernel's (8-row x
-// 128-byte code pieces and 64-row x 16-byte scale pieces per double stage); a set fills a
-// pair of double-stage buffers and two pairs alternate. In each set a wave reads its
-// stage's second chunk at once; at the fifth k-step it waits for the next set's loads (its
-// LDS reads of this set are done by then), meets the workgroup at a barrier, reads the
-// next set's first chunk and issues the loads of the set after that into the pair every
-// wave has finished reading. At the end the four partial tiles meet in LDS and are added
-// in wave order (the same sums on every run). Built for 64 x 64 tiles, whose four partial
-// tiles fit the LDS at once.
-template <int BM, int BN>
-struct alignas(16) GemmSmemWsplit {
-  uint8_t x[4][BM * 128];
-  uint8_t w[4][BN * 128];
-  uint8_t sc[4][(BM + BN) * 16];
+// Here the waves split K as well as the tile: KS waves share each of the 4 / KS row bands
+// of the BM x BN tile (a wave computes its whole band, RM x BN, on every KS-th stage), so
+// a wave keeps more blocks per decoded fragment on a tile as small as before: 64 x 64 with
+// KS = 4 (2 x 2 blocks per wave, one fragment per MFMA), 128 x 128 with KS = 2 (2 x 4
+// blocks, 0.75). A set is KS stages (KS / 2 double stages) and wave w takes stage
+// KS t + w % KS of set t. Loads and LDS image are the 256 x 256 kernel's (8-row x 128-byte
+// code pieces and 64-row x 16-byte scale pieces per double stage); a set fills a group
+// of double-stage buffers and two groups alternate. In each set a wave reads its stage's
+// second chunk at once; at the fifth k-step it waits for the next set's loads (its LDS
+// reads of this set are done by then), meets the workgroup at a barrier, reads the next
+// set's first chunk and issues the loads of the set after that into the group every wave
+// has finished reading. At the end the KS partial sums of every block meet in LDS (the
+// pipeline's buffers, grown to hold all of them at once where needed) and are added in
+// wave order (the same sums on every run).
+template <int BM, int BN, int KS>
+union alignas(16) GemmSmemWsplit {
+  struct {
+    uint8_t x[KS][BM * 128];
+    uint8_t w[KS][BN * 128];
+    uint8_t sc[KS][(BM + BN) * 16];
+  } pipe;
+  // the four waves' partial blocks (32 x 32 fp32 each) at the end
+  float red[4][(BM / (4 / KS) / 32) * (BN / 32)][64 * 16];
 };
 
-// Requires K % 512 == 0 (whole sets), 16-byte aligned packed operands, 4-byte aligned
-// scales, and (rows + one tile) x K/2 below 2^31 for both operands.
-template <int BM, int BN, bool kExp>
+// Requires K % (128 KS) == 0 (whole sets), 16-byte aligned packed operands, 4-byte
+// aligned scales, and (rows + one tile) x K/2 below 2^31 for both operands.
+template <int BM, int BN, int KS, bool kExp>
 __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   constexpr int NW = 4;
-  constexpr int FM = BM / 32, FN = BN / 32;
+  static_assert(KS == 2 || KS == 4, "two or four waves per row band");
+  constexpr int WM = NW / KS;         // row bands
+  constexpr int RM = BM / WM;         // rows per band
+  constexpr int FM = RM / 32, FN = BN / 32;
+  constexpr int DS = KS / 2;          // double stages per set
   constexpr int kSteps = 8;  // 16-element k-steps per stage (two chunks of 4)
   constexpr int kPx = BM / 8, kPw = BN / 8;  // 1 KiB code pieces per double stage
-  static_assert((kPx + kPw) % NW == 0, "code pieces divide among waves");
+  static_assert(RM % 32 == 0 && (kPx + kPw) % NW == 0, "whole blocks; code pieces divide among waves");
   constexpr int kCode = (kPx + kPw) / NW;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 64-row scale pieces");
   constexpr int kSp = (BM + BN) / 64;          // scale pieces per double stage
   constexpr int kScale = (kSp + NW - 1) / NW;  // per wave (the last piece repeated)
   constexpr int kLoadsDs = kCode + kScale;     // per wave and double stage
-  constexpr int kLoads = 2 * kLoadsDs;         // per wave and set
+  constexpr int kLoads = DS * kLoadsDs;        // per wave and set
   static_assert(kLoads < 64, "a set of loads fits the vmcnt counter");
   constexpr int kLoadsPerStep = (kLoads + 3) / 4;  // over a set's last 4 k-steps
   constexpr int kMfmaPerStep = FN * FM;
   constexpr int kReadsPerChunk = 2 * (FN + FM);
   constexpr int kReadsPerMfma = (kReadsPerChunk + kMfmaPerStep - 1) / kMfmaPerStep;
   constexpr int kValuPerMfma = (8 * (FN + FM) + kMfmaPerStep - 1) / kMfmaPerStep;
-  __shared__ GemmSmemWsplit<BM, BN> sm;
+  __shared__ GemmSmemWsplit<BM, BN, KS> sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int r32 = lane & 31;
-  const int wq = wave >> 1;   // the wave's double stage within a set
-  const int whs = wave & 1;   // and stage within it
+  const int wm = wave / KS;   // the wave's row band
+  const int wk = wave % KS;   // and stage within a set
+  const int wq = wk >> 1;     // its double stage within the set
+  const int whs = wk & 1;     // and stage within that
 
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   const int tiles_m = (int)((p.M + BM - 1) / BM);
@@ -549,7 +562,7 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   tile_order(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int n0 = tile_n * BN;
-  const int nset = (int)(p.K / 512);
+  const int nset = (int)(p.K / (128 * KS));
   const uint32_t pitch = (uint32_t)(p.K >> 1);
   const uint32_t spitch = (uint32_t)(p.K >> 4);
 
@@ -559,26 +572,26 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, m0, p.M, spitch);
   const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
 
-  // load j (0 .. kLoads - 1) of this wave for set t into buffer pair pr: per double stage
-  // 2t + j / kLoadsDs, code pieces (activation rows 8i .. 8i+7, then weight rows), then
-  // scale pieces (64 rows x 16 bytes, activation rows first; slots past the last piece
-  // repeat it, writing the same bytes to the same place)
-  auto issue = [&](int j, int t, int pr) {
+  // load j (0 .. kLoads - 1) of this wave for set t into buffer group grp: per double
+  // stage DS t + j / kLoadsDs, code pieces (activation rows 8i .. 8i+7, then weight rows),
+  // then scale pieces (64 rows x 16 bytes, activation rows first; slots past the last
+  // piece repeat it, writing the same bytes to the same place)
+  auto issue = [&](int j, int t, int grp) {
     const int half = j / kLoadsDs;
     const int jj = j - half * kLoadsDs;
-    const int ds = 2 * t + half;
-    const int buf = 2 * pr + half;
+    const int ds = DS * t + half;
+    const int buf = DS * grp + half;
     if (jj < kCode) {
       const int i = jj * NW + wave;
       const bool isx = i < kPx;
       const int prow = 8 * (isx ? i : i - kPx);
-      buffer_load_lds16(isx ? rxp : rwp, isx ? &sm.x[buf][i * 1024] : &sm.w[buf][(i - kPx) * 1024],
+      buffer_load_lds16(isx ? rxp : rwp, isx ? &sm.pipe.x[buf][i * 1024] : &sm.pipe.w[buf][(i - kPx) * 1024],
                         x_piece_voff(lane, prow, pitch) + (uint32_t)ds * 128, 0);
     } else {
       const int i = min((jj - kCode) * NW + wave, kSp - 1);
       const bool isx = i < BM / 64;
       const int prow = isx ? 64 * i : 64 * (i - BM / 64);
-      buffer_load_lds16(isx ? rxs : rws, &sm.sc[buf][i * 1024],
+      buffer_load_lds16(isx ? rxs : rws, &sm.pipe.sc[buf][i * 1024],
                         scale_piece_voff(lane, prow, spitch, (uint32_t)ds * 16), 0);
     }
   };
@@ -594,19 +607,20 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   // fragments of two chunks and decoded operands of two k-steps
   const int rbase = (r32 >> 3) * 1024 + (r32 & 7) * 128;  // lane's row in a 32-row group
   const int sw = x_swz(r32);
+  const int xfrag = wm * FM * 4096;
   const int wsw = (BM + r32) * 16 + 2 * h;
-  const int xsw = r32 * 16 + 2 * h;
+  const int xsw = (wm * RM + r32) * 16 + 2 * h;
   u32x4 wraw[2][FN], xraw[2][FM];
   uint32_t wsr[2][FN], xsr[2][FM];
   half2_t wsc[FN], xsc[FM];
   half8_t wf[2][FN], xf[2][FM];
-  // chunk c of this wave's stage of the set in buffer pair pr, as chunk par
-  auto read_chunk = [&](int par, int pr, int c) {
-    const int buf = 2 * pr + wq;
+  // chunk c of this wave's stage of the set in buffer group grp, as chunk par
+  auto read_chunk = [&](int par, int grp, int c) {
+    const int buf = DS * grp + wq;
     const int fr = rbase + 16 * ((2 * (2 * whs + c) + h) ^ sw);
-    const uint8_t* wb = &sm.w[buf][fr];
-    const uint8_t* xb = &sm.x[buf][fr];
-    const uint8_t* scb = &sm.sc[buf][whs * 8 + c * 4];
+    const uint8_t* wb = &sm.pipe.w[buf][fr];
+    const uint8_t* xb = &sm.pipe.x[buf][xfrag + fr];
+    const uint8_t* scb = &sm.pipe.sc[buf][whs * 8 + c * 4];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       wraw[par][i] = *(const u32x4*)(wb + i * 4096);
@@ -631,7 +645,7 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
     for (int g = 0; g < FM; ++g) xo[g] = decode8<true>(xraw[par][g][j], j < 2 ? xsc[g].xx : xsc[g].yy);
   };
 
-  // prologue: sets 0 and 1 into pairs 0 and 1; wait for set 0, read its first chunk
+  // prologue: sets 0 and 1 into groups 0 and 1; wait for set 0, read its first chunk
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) issue(j, 0, 0);
   if (nset > 1) {
@@ -645,25 +659,25 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   read_chunk(0, 0, 0);
   decode_step(0, 0, wf[0], xf[0]);
 
-  // set t in buffer pair pr (a constant); loads: issue set t + 2 into pr (a constant);
+  // set t in buffer group grp (a constant); loads: issue set t + 2 into grp (a constant);
   // last: no set follows (a constant)
-  auto set = [&](int t, const int pr, const bool loads, const bool last) {
+  auto set = [&](int t, const int grp, const bool loads, const bool last) {
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const int cur = st & 1;
       const int j = st & 3;
-      if (st == 0) read_chunk(1, pr, 1);  // this stage's second chunk
+      if (st == 0) read_chunk(1, grp, 1);  // this stage's second chunk
       if (st == 4 && !last) {
-        // vmcnt(0) and lgkmcnt(0): set t + 1 loaded, this wave's reads of pair pr done
+        // vmcnt(0) and lgkmcnt(0): set t + 1 loaded, this wave's reads of group grp done
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
-        read_chunk(0, pr ^ 1, 0);  // set t + 1's first chunk
+        read_chunk(0, grp ^ 1, 0);  // set t + 1's first chunk
       }
       const bool ld = loads && st >= 4;
       if (ld) {
 #pragma unroll
         for (int l = 0; l < kLoadsPerStep; ++l)
-          if ((st - 4) * kLoadsPerStep + l < kLoads) issue((st - 4) * kLoadsPerStep + l, t + 2, pr);
+          if ((st - 4) * kLoadsPerStep + l < kLoads) issue((st - 4) * kLoadsPerStep + l, t + 2, grp);
       }
       // decode of the next k-step (the first k-step of the next set after the last)
       if (!(last && st + 1 == kSteps)) decode_step(((st + 1) >> 2) & 1, (st + 1) & 3, wf[cur ^ 1], xf[cur ^ 1]);
@@ -702,38 +716,38 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
     set(t, 0, false, true);
   }
 
-  // the four partial tiles meet in LDS (each wave writes its blocks lane-major, 16 values
-  // per lane); wave b % 4 adds the four parts of block b in wave order, scales and stores it
+  // The KS partial sums of every block meet in LDS (each wave writes all its blocks
+  // lane-major, 16 values per lane); among the KS waves of a row band, wave wk adds the
+  // parts of every KS-th block in wave order, scales and stores it.
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   typedef float floatx4 __attribute__((ext_vector_type(4)));
-  float* red = (float*)&sm;
-  static_assert(NW * FN * FM * 64 * 16 * sizeof(float) <= sizeof(sm), "partial tiles fit");
+  constexpr int NB = FN * FM;  // blocks per wave
+  static_assert(sizeof(sm.red[0]) == NB * 64 * 16 * sizeof(float), "partial blocks");
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int g = 0; g < FM; ++g)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4)
-        *(floatx4*)&red[((wave * FN * FM + i * FM + g) * 64 + lane) * 16 + 4 * v4] =
-            floatx4{acc[i][g][4 * v4], acc[i][g][4 * v4 + 1], acc[i][g][4 * v4 + 2], acc[i][g][4 * v4 + 3]};
+    for (int v4 = 0; v4 < 4; ++v4)
+      *(floatx4*)&sm.red[wave][b][lane * 16 + 4 * v4] =
+          floatx4{acc[b / FM][b % FM][4 * v4], acc[b / FM][b % FM][4 * v4 + 1],
+                  acc[b / FM][b % FM][4 * v4 + 2], acc[b / FM][b % FM][4 * v4 + 3]};
   __syncthreads();
   const Alpha alpha = gemm_alpha(p);
 #pragma unroll
-  for (int blk = 0; blk < FN * FM; ++blk) {
-    if (blk % NW != wave) continue;
-    const int i = blk / FM, g = blk % FM;
+  for (int b = 0; b < NB; ++b) {
+    if (b % KS != wk) continue;
     floatx16 tot[1][1];
 #pragma unroll
-    for (int src = 0; src < NW; ++src)
+    for (int src = 0; src < KS; ++src)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const floatx4 part = *(const floatx4*)&red[((src * FN * FM + blk) * 64 + lane) * 16 + 4 * v4];
+        const floatx4 part = *(const floatx4*)&sm.red[wm * KS + src][b][lane * 16 + 4 * v4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           tot[0][0][4 * v4 + e] = src == 0 ? part[e] : tot[0][0][4 * v4 + e] + part[e];
       }
-    store_tile<1, 1, kExp>(tot, p, alpha, (int64_t)m0 + g * 32, (int64_t)n0 + i * 32, lane);
+    store_tile<1, 1, kExp>(tot, p, alpha, (int64_t)m0 + wm * RM + (b % FM) * 32,
+                           (int64_t)n0 + (b / FM) * 32, lane);
   }
 }
 
@@ -1444,6 +1458,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   const bool ws_ok = aligned && K % 512 == 0 && fits_i31(M + 64, K / 2) && fits_i31(N + 64, K / 2) &&
                      t64 <= cus;
   const double cws = ws_ok ? (double)nk * 624.0 + 15200.0 : 1e300;
+  // 128 x 128 tiles, two row bands of two waves splitting K: 0.75 fragments per MFMA
+  // against the 128 x 128 tile's 1, for a larger reduction at the end; one pass only.
+  // Measured at 1000 x 3072 (K = 3072, 6144, 12288): 22.9 / 37.5 / 68.9 us against the
+  // 128 x 128 tile's 21.9 / 40.7 / 77.1 (here 1620 per stage plus 31 400).
+  const bool ws2_ok = aligned && K % 256 == 0 && fits_i31(M + 128, K / 2) && fits_i31(N + 128, K / 2) &&
+                      t128sq <= cus;
+  const double cws2 = ws2_ok ? (double)nk * 1620.0 + 31400.0 : 1e300;
   plan.kernel = fast ? NVFP4_GEMM_TILE256 : NVFP4_GEMM_GENERIC;
   plan.split = splitk_shape(M);
   if (fast || fit_ok) {
@@ -1453,6 +1474,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
     if (fast && c128sq < best) { plan.kernel = NVFP4_GEMM_TILE128X128; best = c128sq; }
     if (fast && c12864 < best) { plan.kernel = NVFP4_GEMM_TILE128X64; best = c12864; }
     if (cws < best) { plan.kernel = NVFP4_GEMM_WSPLIT64; best = cws; }
+    if (cws2 < best) { plan.kernel = NVFP4_GEMM_WSPLIT128; best = cws2; }
     if (split_ok && M <= 512 && csplit < best) plan.kernel = NVFP4_GEMM_SPLITK;
   } else if (split_ok && M <= 512 && tfit * 4 <= cus) {
     // against the register-staged kernel (K % 128 != 0): few tiles only
@@ -1461,14 +1483,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   return plan;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int KS>
 hipError_t launch_wsplit(const GemmProblem& p, hipStream_t stream) {
   const int64_t t = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (t > 0x7FFFFFFF || p.K % 512 != 0) return hipErrorInvalidValue;
+  if (t > 0x7FFFFFFF || p.K % (128 * KS) != 0) return hipErrorInvalidValue;
   if (alpha_needs_exp(p))
-    hipLaunchKernelGGL((gemm_wsplit_kernel<BM, BN, true>), dim3((unsigned)t), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_wsplit_kernel<BM, BN, KS, true>), dim3((unsigned)t), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_wsplit_kernel<BM, BN, false>), dim3((unsigned)t), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_wsplit_kernel<BM, BN, KS, false>), dim3((unsigned)t), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1524,7 +1546,9 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
       return hipGetLastError();
     }
     case NVFP4_GEMM_WSPLIT64:
-      return launch_wsplit<64, 64>(p, stream);
+      return launch_wsplit<64, 64, 4>(p, stream);
+    case NVFP4_GEMM_WSPLIT128:
+      return launch_wsplit<128, 128, 2>(p, stream);
     default:
       return launch_tile<kTileBM, kTileBN, kTileKC, NVFP4_GEMM_WM, NVFP4_GEMM_WN>(
           p, stream, plan.kernel == NVFP4_GEMM_TILE256);

@@ -117,7 +117,7 @@ def test_gemm_plan_routes_shapes(lib):
         st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864, WS64 = 1, 0, 2, 3, 4, 5, 6, 7
+    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864, WS64, WS128 = 1, 0, 2, 3, 4, 5, 6, 7, 8
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
                     (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
@@ -143,6 +143,10 @@ def test_gemm_plan_routes_shapes(lib):
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128), M
     for M in (800, 1000):   # about a thousand rows: 128 x 128 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T128SQ), M
+    # ... whose two row bands split K once K is long enough to pay for the reduction
+    for K in (6144, 12288):
+        assert plan(1000, 3072, K) == (L.SUCCESS, WS128), K
+    assert plan(640, 3072, 12288) == (L.SUCCESS, T12864)   # one pass of 128 x 64 tiles
     for M in (384, 512, 600):   # a few hundred rows past one pass of 64 x 64: 128 x 64 tiles
         assert plan(M, 3072, 3072) == (L.SUCCESS, T12864), M
     assert plan(2600, 1650, 128) == (L.SUCCESS, T128)

@@ -83,6 +83,8 @@ def test_gemm_small_shapes_in_full(M, N, K):
     (700, 90, 512, "wsplit64"), (65, 1000, 1024, "wsplit64"), (130, 777, 1536, "wsplit64"),
     (200, 64, 2048, "wsplit64"), (257, 1500, 2560, "wsplit64"), (100, 500, 3072, "wsplit64"),
     (320, 3072, 3584, "wsplit64"),
+    # 128 x 128 tiles, two row bands of two waves splitting K: 17, 18 and 21 sets
+    (1023, 2049, 4352, "wsplit128"), (1000, 2100, 4608, "wsplit128"), (900, 2600, 5376, "wsplit128"),
     (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])
@@ -137,7 +139,7 @@ _EXTREME_PAIRS = [
 @pytest.mark.parametrize("pair", range(len(_EXTREME_PAIRS)))
 @pytest.mark.parametrize("M,N,K,kernel", [
     (64, 128, 128, "splitk"), (600, 700, 256, "tile128x64"), (1500, 2500, 128, "tile128x128"),
-    (130, 777, 1536, "wsplit64"),
+    (130, 777, 1536, "wsplit64"), (1023, 2049, 4352, "wsplit128"),
     (2600, 1650, 384, "tile128"), (2600, 3000, 128, "fit"), (4096, 4096, 128, "tile256"),
     (600, 700, 208, "generic"),
 ])

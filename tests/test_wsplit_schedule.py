@@ -1,15 +1,16 @@
-"""The set schedule of the 64 x 64 GEMM whose waves split K (``gemm_wsplit_kernel`` in
-``csrc/gemm.hip``), checked on the host for every number of sets from 1 to 12.
+"""The set schedule of the GEMM whose waves split K (``gemm_wsplit_kernel`` in
+``csrc/gemm.hip``, both its 64 x 64 and 128 x 128 forms), checked on the host for every
+number of sets from 1 to 12.
 
-The kernel loads a set (four stages of K) into one of two LDS buffer pairs while the waves
+The kernel loads a set (KS stages of K) into one of two LDS buffer groups while the waves
 compute the previous one. All four waves run the same sequence of loads, waits, barriers
 and LDS reads, so the schedule is modelled as one event list in which a barrier is a point
 every wave reaches; the checks are the ones the kernel's correctness rests on:
 
-* every set is loaded once, into the pair its compute reads;
-* a pair is read for a set only after that set's loads were waited for (each wave waits
+* every set is loaded once, into the group its compute reads;
+* a group is read for a set only after that set's loads were waited for (each wave waits
   for its own loads) and a barrier followed, and before anything else is loaded into it;
-* loads into a pair start only after a barrier that follows the last read of what the pair
+* loads into a group start only after a barrier that follows the last read of what the group
   held before;
 * the epilogue reuses the LDS only after a barrier that follows every read and every
   wait for the loads.
@@ -18,8 +19,8 @@ import pytest
 
 
 def schedule(nset):
-    """The kernel's event list: ("load", set, pair), ("wait",), ("barrier",),
-    ("read", set, pair), ("reduce",)."""
+    """The kernel's event list: ("load", set, group), ("wait",), ("barrier",),
+    ("read", set, group), ("reduce",)."""
     ev = []
     ev.append(("load", 0, 0))
     if nset > 1:
@@ -64,11 +65,11 @@ def schedule(nset):
 @pytest.mark.parametrize("nset", range(1, 13))
 def test_wsplit_set_schedule(nset):
     ev = schedule(nset)
-    content = {0: None, 1: None}          # set last loaded into each pair
+    content = {0: None, 1: None}          # set last loaded into each group
     outstanding = []                      # loads issued and not yet waited for, in order
     landed_unsynced = set()               # sets waited for by the waves, no barrier since
     visible = set()                       # sets every wave may read
-    last_read = {0: -2, 1: -2}            # event index of the last read of each pair (none yet)
+    last_read = {0: -2, 1: -2}            # event index of the last read of each group (none yet)
     last_barrier = -1
     loaded = []
     reads = {}
@@ -77,7 +78,7 @@ def test_wsplit_set_schedule(nset):
         if kind == "load":
             _, s, p = e
             assert s < nset, f"set {s} past the end is loaded"
-            assert last_read[p] < last_barrier, f"set {s} loaded into pair {p} before a barrier after its last read"
+            assert last_read[p] < last_barrier, f"set {s} loaded into group {p} before a barrier after its last read"
             content[p] = s
             visible.discard(s)
             outstanding.append(s)
@@ -99,7 +100,7 @@ def test_wsplit_set_schedule(nset):
             _, s, p = e
             if s >= nset:
                 continue
-            assert content[p] == s, f"set {s} read from pair {p} holding set {content[p]}"
+            assert content[p] == s, f"set {s} read from group {p} holding set {content[p]}"
             assert s in visible, f"set {s} read before its loads were waited for and synchronized"
             last_read[p] = i
             reads[s] = reads.get(s, 0) + 1
