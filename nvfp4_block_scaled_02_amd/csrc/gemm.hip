@@ -716,9 +716,10 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
     set(t, 0, false, true);
   }
 
-  // The KS partial sums of every block meet in LDS (each wave writes all its blocks
-  // lane-major, 16 values per lane); among the KS waves of a row band, wave wk adds the
-  // parts of every KS-th block in wave order, scales and stores it.
+  // The KS partial sums of every block meet in LDS (each wave writes all its blocks, four
+  // values per lane and 16-byte access, consecutive lanes side by side); among the KS
+  // waves of a row band, wave wk adds the parts of every KS-th block in wave order,
+  // scales and stores it.
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -728,7 +729,7 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4)
-      *(floatx4*)&sm.red[wave][b][lane * 16 + 4 * v4] =
+      *(floatx4*)&sm.red[wave][b][(v4 * 64 + lane) * 4] =
           floatx4{acc[b / FM][b % FM][4 * v4], acc[b / FM][b % FM][4 * v4 + 1],
                   acc[b / FM][b % FM][4 * v4 + 2], acc[b / FM][b % FM][4 * v4 + 3]};
   __syncthreads();
@@ -741,7 +742,7 @@ __global__ void __launch_bounds__(256) gemm_wsplit_kernel(GemmProblem p) {
     for (int src = 0; src < KS; ++src)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const floatx4 part = *(const floatx4*)&sm.red[wm * KS + src][b][lane * 16 + 4 * v4];
+        const floatx4 part = *(const floatx4*)&sm.red[wm * KS + src][b][(v4 * 64 + lane) * 4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           tot[0][0][4 * v4 + e] = src == 0 ? part[e] : tot[0][0][4 * v4 + e] + part[e];
