@@ -62,9 +62,8 @@ def schedule(nset):
     return ev
 
 
-@pytest.mark.parametrize("nset", range(1, 13))
-def test_wsplit_set_schedule(nset):
-    ev = schedule(nset)
+def check(ev, nset):
+    """Raise AssertionError where the event list breaks one of the rules above."""
     content = {0: None, 1: None}          # set last loaded into each group
     outstanding = []                      # loads issued and not yet waited for, in order
     landed_unsynced = set()               # sets waited for by the waves, no barrier since
@@ -109,3 +108,32 @@ def test_wsplit_set_schedule(nset):
             assert max(last_read.values()) < last_barrier, "LDS reused before a barrier after the last read"
     assert sorted(loaded) == list(range(nset)), f"sets loaded: {sorted(loaded)}"
     assert all(reads.get(s) == 2 for s in range(nset)), f"chunk reads per set: {reads}"
+
+
+@pytest.mark.parametrize("nset", range(1, 13))
+def test_wsplit_set_schedule(nset):
+    check(schedule(nset), nset)
+
+
+def _mutations(ev):
+    """Event lists with one plausible mistake each: a load into the other buffer group, a
+    dropped wait before a barrier (the final one aside: no load is in flight there), a
+    read moved ahead of the barrier it follows."""
+    out = []
+    for i, e in enumerate(ev):
+        if e[0] == "load" and e[1] >= 2:
+            out.append(ev[:i] + [("load", e[1], e[2] ^ 1)] + ev[i + 1:])
+        if e[0] == "wait" and ev[i + 1][0] == "barrier" and 5 < i < len(ev) - 3:
+            out.append(ev[:i] + ev[i + 1:])
+        if e[0] == "barrier" and i + 1 < len(ev) and ev[i + 1][0] == "read" and i > 5:
+            out.append(ev[:i - 1] + [ev[i + 1], ev[i - 1], e] + ev[i + 2:])
+    return out
+
+
+@pytest.mark.parametrize("nset", [3, 6, 7])
+def test_wsplit_schedule_check_catches_mistakes(nset):
+    muts = _mutations(schedule(nset))
+    assert len(muts) >= 3
+    for m in muts:
+        with pytest.raises(AssertionError):
+            check(m, nset)
