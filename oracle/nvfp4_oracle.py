@@ -317,7 +317,8 @@ def check_gemm(out_bf16_bits: np.ndarray, ref: np.ndarray, absref: np.ndarray):
     err = np.abs(out - ref)
     bad = ~(err <= tol)  # NaN counts as bad
     ratio = np.where(tol > 0, err / tol, np.inf)
-    worst = float(np.nanmax(ratio)) if ratio.size else 0.0
+    ratio = np.where(np.isnan(ratio), np.inf, ratio)  # a NaN output is as bad as can be
+    worst = float(np.max(ratio)) if ratio.size else 0.0
     return (not bool(bad.any())), worst, int(bad.sum())
 
 
