@@ -85,7 +85,9 @@ def test_gemm_small_shapes_in_full(M, N, K):
     (320, 3072, 3584, "wsplit64"),
     # 128 x 128 tiles, two row bands of two waves splitting K: 17, 18 and 21 sets
     (1023, 2049, 4352, "wsplit128"), (1000, 2100, 4608, "wsplit128"), (900, 2600, 5376, "wsplit128"),
-    (4096, 4096, 128, "tile256"),
+    # 256 x 256 tiles: one double stage, and nine (an odd count: the last double stage's
+    # second half is the loop's tail)
+    (4096, 4096, 128, "tile256"), (4096, 4096, 1152, "tile256"),
     (600, 700, 208, "generic"),
 ])
 def test_gemm_tiled_kernels_in_full(M, N, K, kernel):

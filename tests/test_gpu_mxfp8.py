@@ -89,8 +89,9 @@ def _gemm_dev(ac, as_, wc, ws, guard=True):
     # 288 x 192 tiles with ragged edges and several 8-stage scale groups (K = 1152)
     (600, 400, 1152), (289, 193, 640),
     # 4096 x 4096: 256 x 256 tiles need one pass over 256 compute units, 288 x 192 two,
-    # so this one runs on the 256 x 256 kernel
-    (4096, 4096, 128),
+    # so these run on the 256 x 256 kernel: two stages, and 18 (two whole 8-stage scale
+    # groups and a partial third)
+    (4096, 4096, 128), (4096, 4096, 1152),
 ])
 def test_gemm_small_shapes_in_full(M, N, K):
     rng = np.random.default_rng(M * 11 + N * 5 + K)

@@ -46,8 +46,10 @@ def _check(got, x, wp, ws, wgs, label):
     (2017, 2305, 1088, "wide96x256"), (2304, 2048, 640, "wide96x256"),
     (2017, 3000, 320, "wide128x256"),
     (3001, 2999, 192, "wide"), (3300, 2600, 320, "wide"),
-    # the 288 x 192 tile (one pass where the others need two) and the 256 x 256 tile
+    # the 288 x 192 tile (one pass where the others need two) and the 256 x 256 tile, each
+    # with one stage and with 17 or 18 (whole quads of scale stages and a partial last one)
     (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256"),
+    (4288, 3088, 1088, "fit"), (4096, 4096, 1152, "tile256"),
 ])
 def test_w4a16_small_shapes_in_full(M, N, K, kernel):
     assert nv.gemm_w4a16_plan(M, N, K) == kernel
