@@ -20,10 +20,12 @@ settle phase runs by wall time, whatever --warmup says):
    device-to-device copy moving the same bytes (the copy ceiling);
 6. context rows: the fused linear (quantize + GEMM) and the GEMM alone for every
    M = 4608 FLUX linear and the 4-image batch, hipBLASLt bf16 at the metric's shape, the
-   MXFP8, rowwise FP8 and W4A16 paths, and short activations;
+   MXFP8, rowwise FP8 and W4A16 paths, and short activations (for 1 and 17 rows also on
+   rotated weights, read from HBM);
 7. the CPU oracle timed on a bounded sample.
 
-The GFX clock is sampled (amdsmi, its own thread) throughout and reported per leg.
+The GFX clock is sampled (amdsmi, its own thread) throughout and reported per leg; the
+memory clock is read once at the end.
 
     python bench.py [--steps K] [--warmup W] [--workload attn_out] [--gpus 1]
                     [--no-context] [--no-cpu-baseline]
@@ -114,6 +116,7 @@ class ClockSampler:
         self._stop = threading.Event()
         self._thread = None
         self._read = None
+        self._read_mem = None
         try:
             self._setup()
         except Exception as e:  # no amdsmi, no permission, no device: report, never fail
@@ -154,6 +157,11 @@ class ClockSampler:
             c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX).get("clk")
             return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
 
+        def mem_clock():
+            c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.MEM).get("clk")
+            return float(c) if isinstance(c, (int, float)) and 0 < c < 100000 else None
+
+        self._read_mem = mem_clock
         for name, fn in (("amdsmi gpu_metrics current_gfxclk(s)", from_metrics),
                          ("amdsmi clock_info GFX", from_clock_info)):
             try:
@@ -186,6 +194,13 @@ class ClockSampler:
         self._stop.set()
         if self._thread is not None:
             self._thread.join(timeout=1.0)
+
+    def memory_clock_mhz(self):
+        """One reading of the memory clock (MHz), or None where it cannot be read."""
+        try:
+            return self._read_mem() if self._read_mem is not None else None
+        except Exception:
+            return None
 
     def window(self, t0: float, t1: float):
         v = [c for t, c in self.samples if t0 <= t <= t1]
@@ -340,12 +355,14 @@ def bandwidth_legs(nv, lib, timer, sp, rotate_mb, n_min, gen):
     return out
 
 
-def context_legs(nv, lib, timer, stream, n):
+def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
     """Context rows (not the metric). The fused linear (quantize + GEMM: nvfp4_linear) and
     the GEMM alone on every M = 4608 FLUX linear and the 4-image batch, on the seeded
     workload tensors (the static-scale MLP up-projection keeps its offline scale);
     hipBLASLt bf16, MXFP8, rowwise FP8 and W4A16 at the metric's shape; short activations
-    (weights dominate the bytes). All operands resident (warm)."""
+    (weights dominate the bytes). All operands resident (warm), except the rows for 1 and
+    17 activation rows, which also cycle through copies of the weights totalling
+    `rotate_weights_mb` (HBM-bound: the weights' bytes are the work)."""
     import numpy as np
     import torch
 
@@ -448,12 +465,35 @@ def context_legs(nv, lib, timer, stream, n):
               P(work), ctypes.c_size_t(nb), sp)
         msl, _ = timer.launches(lambda: lib.nvfp4_linear(*al), n, warm)
         wbytes = N * (K // 2 + K // 16)
-        out["short_activations"][f"M={M}"] = {
+        row = {
             "N": N, "K": K, "kernel": nv.gemm_plan(M, N, K), "w4a4_avg_ms": round(ms, 5),
             "w4a4_weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
             "linear": nv.linear_plan(M, N, K), "linear_avg_ms": round(msl, 5),
             "w4a16_kernel": nv.gemm_w4a16_plan(M, N, K), "w4a16_avg_ms": round(ms16, 5),
             "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+        if M <= 17:
+            # HBM-bound on the weights: cycle through copies of the quantized weights
+            # totalling beyond the 256 MB Infinity Cache, so each launch reads them from HBM
+            n_rot = max(2, -(-rotate_weights_mb * 2**20 // wbytes))
+            sets = [(wp.clone(), ws.clone()) for _ in range(n_rot)]
+            args_r = [(P(ap), P(as_), ctypes.c_float(ags), P(a), P(b), ctypes.c_float(wgs), M, N, K,
+                       P(y), sp) for a, b in sets]
+            it = [0]
+
+            def rot():
+                if lib.nvfp4_gemm(*args_r[it[0] % n_rot]):
+                    raise RuntimeError("gemm failed")
+                it[0] += 1
+
+            ms_r, _ = timer.launches(rot, max(n, 2 * n_rot), n_rot)
+            abytes = M * (K // 2 + K // 16) + 2 * M * N  # activation codes + bf16 output
+            row["w4a4_rotated_weights"] = {
+                "weight_sets": n_rot, "avg_ms": round(ms_r, 5),
+                "weight_GB/s": round(wbytes / (ms_r * 1e-3) / 1e9, 1),
+                "bytes_per_launch": wbytes + abytes,
+                "frac_hbm_peak": round((wbytes + abytes) / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del sets, args_r
+        out["short_activations"][f"M={M}"] = row
     return out
 
 
@@ -573,6 +613,7 @@ def main():
         "settle": settle_rec,
         "clock_timed_steps": clock.window(h0, h1),
         "clock_source": clock.source,
+        "memory_clock_mhz": clock.memory_clock_mhz(),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
