@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 /* Status codes. All argument validation happens before any HIP call. */
 typedef enum nvfp4_status {
@@ -137,8 +137,12 @@ typedef enum {
                                  hundred rows */
   NVFP4_GEMM_WSPLIT64 = 7,     /* 64 x 64 output tiles whose four waves split K (K % 512 == 0):
                                  a few hundred activation rows against a narrow weight */
-  NVFP4_GEMM_WSPLIT128 = 8     /* 128 x 128 output tiles, two row bands of two waves that
+  NVFP4_GEMM_WSPLIT128 = 8,    /* 128 x 128 output tiles, two row bands of two waves that
                                  split K (K % 256 == 0): about a thousand rows, long K */
+  NVFP4_GEMM_GEMV16 = 9        /* at most 16 activation rows, or 32 where N <= 16 x the
+                                 compute units (K % 256 == 0): 4 to 16 weight rows per
+                                 workgroup, 16 x 16 x 32 MFMAs, the weights' read spread
+                                 over every compute unit */
 } nvfp4_gemm_kernel;
 
 /*
@@ -285,10 +289,11 @@ int nvfp4_fp8r_gemm(const void* a_codes, const void* a_scales, const void* w_cod
 
 /*
  * Whether nvfp4_linear (and nvfp4_linear_devgs) run an M x N x K product as one kernel:
- * the short-activation split-K GEMM first quantizing the bf16 activations into its LDS
- * (for at most 32 rows and 16384 elements, where repeating that quantization in every
- * workgroup along N costs less than a second launch), instead of the quantize kernel
- * followed by nvfp4_gemm. num_cus as in nvfp4_gemm_plan. Host only.
+ * the short-activation GEMM that nvfp4_gemm would run (the 16-row kernel, or split-K)
+ * first quantizing the bf16 activations into its LDS (for at most 32 rows and 16384
+ * elements, where repeating that quantization in every workgroup along N costs less than
+ * a second launch), instead of the quantize kernel followed by nvfp4_gemm. num_cus as in
+ * nvfp4_gemm_plan. Host only.
  * Writes 1 (one kernel) or 0 (two) to *fused; NVFP4_ERROR_INVALID_VALUE for a null
  * pointer, NVFP4_ERROR_INVALID_SHAPE for shapes the linear rejects.
  */

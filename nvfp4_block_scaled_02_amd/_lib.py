@@ -11,7 +11,7 @@ import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnvfp4.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS = {
     0: "NVFP4_SUCCESS",

@@ -350,7 +350,7 @@ int linear_launch(const void* x, float ags, const void* wp, const void* ws, floa
   if (N > 0 && nvfp4::linear_fused(M, N, K, true, info.num_cus)) {
     const float den = 6.0f * ags;
     const nvfp4::FusedQuant fq{x, ags, den, 1.0f / den, nullptr, ap, as};
-    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream);
+    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream, info.num_cus);
     return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
   }
   e = nvfp4::launch_quantize(x, M, K, ags, ap, as, (hipStream_t)stream, info);
@@ -499,7 +499,7 @@ int nvfp4_linear_devgs(const void* x, const float* ags_device, const void* wp, c
   hipError_t e;
   if (N > 0 && nvfp4::linear_fused(M, N, K, true, info.num_cus)) {
     const nvfp4::FusedQuant fq{x, 1.0f, 6.0f, 1.0f / 6.0f, ags_device, ap, as};
-    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream);
+    e = nvfp4::launch_linear_fused(p, fq, (hipStream_t)stream, info.num_cus);
     return e == hipSuccess ? NVFP4_SUCCESS : hip_fail(e);
   }
   e = nvfp4::launch_quantize(x, M, K, 1.0f, ap, as, (hipStream_t)stream, info, ags_device);

@@ -1020,6 +1020,40 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
                           n_base, lane, wave_m * 2, wave_m * 2 + 2);
 }
 
+// Fused linear for the shortest activations: the workgroup quantizes the M x K bf16
+// activations (M * K <= kFuseElems) into LDS in the NVFP4 layout (codes xq [M][K/2], scales
+// xqs [M][K/16]) with the quantize kernel's functions, so codes and scales are bit-identical
+// to nvfp4_quantize's, and with `store` also into the caller's workspace. Half block hb
+// (8 elements) per lane, the pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one
+// wave; the workgroup's `nthreads` threads (a multiple of 64) take half blocks in turn, so
+// both lanes of a pair are always active together.
+constexpr int kFuseElems = 16384;
+__device__ __forceinline__ void quantize_to_lds(const FusedQuant& fq, int64_t M, int64_t K,
+                                                uint8_t* xq, uint8_t* xqs, bool store,
+                                                int nthreads) {
+  const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
+  const int nhalves = (int)(M * K / 8);
+  const u32x4* xv = (const u32x4*)fq.x;
+  for (int hb = threadIdx.x; hb < nhalves; hb += nthreads) {
+    float f[8];
+    unpack_bf16x8(xv[hb], f);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
+    const float o = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+    const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
+    const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
+                                                         : encode_half<false>(f, bs);
+    *(uint32_t*)&xq[4 * hb] = word;
+    if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
+    if (store && fq.ws_packed != nullptr) {
+      *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
+      if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
+    }
+  }
+}
+
 // ---- small-M path: split K inside the workgroup -----------------------------------------
 //
 // For short activations (a few to a few hundred tokens) the tiled kernels leave most of
@@ -1048,7 +1082,6 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 // The K loop then reads the activation fragments from LDS (zeros for rows past M).
 // Every workgroup along N repeats the quantization, which is why it is limited to a few
 // thousand elements per thread block.
-constexpr int kFuseElems = 16384;
 template <int A, int B, int DG, int NW, bool kFuse, bool kVecScale, bool kExp>
 __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, FusedQuant fq) {
   __shared__ float red[2][NW][16 * 64];
@@ -1191,38 +1224,15 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
     }
   };
 
-  // kFuse: quantize the M x K activations into LDS: half block hb (8 elements) per lane,
-  // the pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one wave.
-  auto quantize_to_lds = [&]() {
-    const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
-    const int nhalves = (int)(p.M * p.K / 8);
-    const u32x4* xv = (const u32x4*)fq.x;
-    for (int hb = threadIdx.x; hb < nhalves; hb += 64 * NW) {
-      float f[8];
-      unpack_bf16x8(xv[hb], f);
-      float a = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
-      const float o = __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
-      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
-      const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
-                                                           : encode_half<false>(f, bs);
-      *(uint32_t*)&xq[4 * hb] = word;
-      if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
-      if (tn == 0 && fq.ws_packed != nullptr) {
-        *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
-        if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
-      }
-    }
-    __syncthreads();
-  };
 
 #pragma unroll
   for (int s = 0; s < DG; ++s)
     if (s < ngroups) load_group(s, s);
   // (after the first weight loads, so their latency overlaps the quantization)
-  if constexpr (kFuse) quantize_to_lds();
+  if constexpr (kFuse) {
+    quantize_to_lds(fq, p.M, p.K, xq, xqs, tn == 0, 64 * NW);
+    __syncthreads();
+  }
   for (int G = 0; G < ngroups; G += DG) {
 #pragma unroll
     for (int s = 0; s < DG; ++s) {
@@ -1276,6 +1286,172 @@ __global__ void __launch_bounds__(64 * NW) gemm_splitk_kernel(GemmProblem p, Fus
         }
       }
     }
+}
+
+// ---- one to sixteen activation rows: weight rows spread over the whole chip ------------
+//
+// With a handful of activation rows the product is a read of the weights (1728 bytes per
+// weight row at K = 3072) and takes the weight bytes over the load rate the workgroups
+// reach. A compute unit loading 32 rows in 16-byte pieces, as the split-K kernel's
+// register fragments do, gets about 15 GB/s there, and 32-row workgroups leave most of the
+// chip idle at N = 3072 (96 of 256 compute units). Here a workgroup owns R <= 16 weight
+// rows (a multiple of 4 the launcher picks so that the grid covers the chip: 12 rows, 256
+// workgroups at N = 3072), its NW waves take the 256-element groups of K in turn (group g
+// to wave g % NW; a group is one 128-byte line of codes and 16 scale bytes per row), and a
+// 16 x 16 x 32 MFMA block holds the R weight rows against up to 16 activation rows.
+//
+// Lane (r, q) = (lane % 16, lane / 16) loads bytes 32q .. 32q + 31 of weight row r's line
+// (elements 64q .. 64q + 63 of the group, four E4M3 blocks) with the row's scale bytes
+// 4q .. 4q + 3, and the same of activation row r; lanes past the R weight rows or the M
+// activation rows load nothing and hold zeros. MFMA 4h + j (h = 0, 1 the 16-byte half, j
+// its 32-bit word) takes word j of half h from every lane: elements 64q + 32h + 8j .. + 7
+// for q = 0..3, a reordering of the group's positions along K taken alike for both
+// operands. The NW partial sums meet in LDS and are added in wave order.
+//
+// Requires M <= 16, K % 256 == 0, 16-byte aligned packed operands, 4-byte aligned scales,
+// and both operands below 2^31 bytes (32-bit buffer offsets).
+template <int NW, int DG, int B, bool kFuse, bool kExp>
+__global__ void __launch_bounds__(64 * NW) gemm_gemv16_kernel(GemmProblem p, int R, FusedQuant fq) {
+  typedef float floatx4 __attribute__((ext_vector_type(4)));
+  __shared__ floatx4 red[NW][B][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElems / 2 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xqs[kFuse ? kFuseElems / 16 : 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
+  const int ngt = (int)(p.K / 256);
+  const int ng = (ngt - wave + NW - 1) / NW;  // this wave's groups: wave, wave + NW, ...
+  // weight rows past N fall outside the window and read as zeros; rows of the next
+  // workgroup (r >= R) and activation rows past M are not loaded
+  const bool wlive = r < R;
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
+  const __amdgpu_buffer_rsrc_t rxp = window_rsrc(p.a_packed, 0, p.M, pitch);
+  const __amdgpu_buffer_rsrc_t rxs = window_rsrc(p.a_scales, 0, p.M, spitch);
+
+  // ring slot s: the lane's codes (two 16-byte halves) and four scale bytes of one group,
+  // for its weight row and its activation rows r and 16 + r (kFuse: activations from LDS)
+  u32x4 wc[DG][2], xc[DG][B][2];
+  uint32_t wsv[DG], xsv[DG][B];
+  auto load_x = [&](int s, int g) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int row = 16 * b + r;
+      const bool live = row < p.M;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = gemv_code_voff(row, q, h, g, pitch);
+        xc[s][b][h] = u32x4{0u, 0u, 0u, 0u};
+        if (live) {
+          if constexpr (kFuse) xc[s][b][h] = *(const u32x4*)&xq[off];
+          else xc[s][b][h] = __builtin_amdgcn_raw_buffer_load_b128(rxp, (int)off, 0, 0);
+        }
+      }
+      const uint32_t soff = gemv_scale_voff(row, q, g, spitch);
+      xsv[s][b] = 0u;
+      if (live) {
+        if constexpr (kFuse) xsv[s][b] = *(const uint32_t*)&xqs[soff];
+        else xsv[s][b] = __builtin_amdgcn_raw_buffer_load_b32(rxs, (int)soff, 0, 0);
+      }
+    }
+  };
+  auto load_w = [&](int s, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      wc[s][h] = u32x4{0u, 0u, 0u, 0u};
+      if (wlive)
+        wc[s][h] = __builtin_amdgcn_raw_buffer_load_b128(rwp, (int)gemv_code_voff(r, q, h, g, pitch), 0, 0);
+    }
+    wsv[s] = 0u;
+    if (wlive) wsv[s] = __builtin_amdgcn_raw_buffer_load_b32(rws, (int)gemv_scale_voff(r, q, g, spitch), 0, 0);
+  };
+  floatx4 acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // word j of half h spans elements 64q + 32h + 8j .. + 7: block 4q + 2h + j / 2, i.e.
+  // byte 2h + j / 2 of the lane's scale word
+  auto compute = [&](int s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half2_t ws2 = scales_to_f16<true>(wsv[s] >> (16 * h));
+      half2_t xs2[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) xs2[b] = scales_to_f16<true>(xsv[s][b] >> (16 * h));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8_t wf = decode8<true>(wc[s][h][j], j < 2 ? ws2.xx : ws2.yy);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const half8_t xf = decode8<true>(xc[s][b][h][j], j < 2 ? xs2[b].xx : xs2[b].yy);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf, acc[b], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < DG; ++s)
+    if (s < ng) load_w(s, wave + NW * s);
+  if constexpr (kFuse) {
+    // (after the first weight loads, so their latency overlaps the quantization)
+    quantize_to_lds(fq, p.M, p.K, xq, xqs, blockIdx.x == 0, 64 * NW);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int s = 0; s < DG; ++s)
+    if (s < ng) load_x(s, wave + NW * s);
+  for (int i = 0; i < ng; i += DG) {
+#pragma unroll
+    for (int s = 0; s < DG; ++s) {
+      if (i + s < ng) {
+        compute(s);
+        if (i + s + DG < ng) {
+          load_w(s, wave + NW * (i + s + DG));
+          load_x(s, wave + NW * (i + s + DG));
+        }
+      }
+    }
+  }
+
+  // lane (r, q) holds output rows 16b + r, columns n0 + 4q + {0..3} in acc[b]; wave 0
+  // adds the NW parts in wave order, scales, rounds and stores them
+#pragma unroll
+  for (int b = 0; b < B; ++b) red[wave][b][lane] = acc[b];
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t n = n0 + 4 * q;
+  if (4 * q >= R || n >= p.N) return;
+  const Alpha alpha = gemm_alpha(p);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const int64_t m = 16 * b + r;
+    if (m >= p.M) continue;
+    float tot[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tot[e] = red[0][b][lane][e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const floatx4 part = red[w][b][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[e] += part[e];
+    }
+    float sv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = apply_alpha<kExp>(tot[e], alpha);
+    const u32x2 bits = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
+    uint16_t* orow = p.out + m * p.N;
+    if ((p.N & 3) == 0 && n + 3 < p.N) {
+      *(u32x2*)&orow[n] = bits;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) orow[n + e] = (uint16_t)(bits[e >> 1] >> (16 * (e & 1)));
+    }
+  }
 }
 
 // Device-resident global scales (whose product the launch cannot see) and host pairs
@@ -1410,9 +1586,46 @@ hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s)
   return hipGetLastError();
 }
 
+// Weight rows per workgroup of the 16-row kernel: a multiple of 4 up to 16, the fewest
+// that keep the grid within one workgroup per compute unit.
+int gemv16_rows(int64_t N, int64_t cus) {
+  const int64_t r = 4 * ((N + 4 * cus - 1) / (4 * cus));
+  return (int)(r < 4 ? 4 : r > 16 ? 16 : r);
+}
+
+template <int NW, int B, bool kFuse>
+void launch_gemv16_kernel(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream,
+                          unsigned wgs, int R) {
+  if (alpha_needs_exp(p))
+    hipLaunchKernelGGL((gemm_gemv16_kernel<NW, 4, B, kFuse, true>), dim3(wgs), dim3(64 * NW), 0,
+                       stream, p, R, fq);
+  else
+    hipLaunchKernelGGL((gemm_gemv16_kernel<NW, 4, B, kFuse, false>), dim3(wgs), dim3(64 * NW), 0,
+                       stream, p, R, fq);
+}
+
+template <bool kFuse>
+hipError_t launch_gemv16(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream, int64_t cus) {
+  const int R = gemv16_rows(p.N, cus > 0 ? cus : 256);
+  const int64_t wgs = (p.N + R - 1) / R;
+  if (wgs > 0x7FFFFFFF || p.M > 32 || p.K % 256 != 0) return hipErrorInvalidValue;
+  if (kFuse && p.M * p.K > kFuseElems) return hipErrorInvalidValue;
+  // eight waves once K has eight groups (more loads in flight per compute unit); one or
+  // two 16-row activation blocks
+  const bool wide = p.K / 256 >= 8;
+  if (p.M <= 16) {
+    if (wide) launch_gemv16_kernel<8, 1, kFuse>(p, fq, stream, (unsigned)wgs, R);
+    else launch_gemv16_kernel<4, 1, kFuse>(p, fq, stream, (unsigned)wgs, R);
+  } else {
+    if (wide) launch_gemv16_kernel<8, 2, kFuse>(p, fq, stream, (unsigned)wgs, R);
+    else launch_gemv16_kernel<4, 2, kFuse>(p, fq, stream, (unsigned)wgs, R);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus, bool allow_gemv16) {
   constexpr int BM = kTileBM, BN = kTileBN, KC = kTileKC;
   constexpr int FBM = kFitBM, FBN = kFitBN;
   GemmPlan plan{};
@@ -1477,6 +1690,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
     if (cws < best) { plan.kernel = NVFP4_GEMM_WSPLIT64; best = cws; }
     if (cws2 < best) { plan.kernel = NVFP4_GEMM_WSPLIT128; best = cws2; }
     if (split_ok && M <= 512 && csplit < best) plan.kernel = NVFP4_GEMM_SPLITK;
+    // at most 16 activation rows, or up to 32 while 16-row workgroups fit one pass over the
+    // compute units (two activation blocks hold one 512-thread workgroup per compute unit,
+    // so more passes cost a whole workgroup's latency each; 17 x 18432 x 3072: 20.9 us
+    // against split-K's 13.7): the weights' read, spread over the whole chip
+    const bool gemv_rows = M <= 16 || (M <= 32 && (N + 15) / 16 <= cus);
+    if (allow_gemv16 && gemv_rows && K % 256 == 0 && fits_i31(M + 32, K / 2) && fits_i31(N + 16, K / 2))
+      plan.kernel = NVFP4_GEMM_GEMV16;
   } else if (split_ok && M <= 512 && tfit * 4 <= cus) {
     // against the register-staged kernel (K % 128 != 0): few tiles only
     plan.kernel = NVFP4_GEMM_SPLITK;
@@ -1502,6 +1722,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
   switch (plan.kernel) {
     case NVFP4_GEMM_SPLITK:
       return launch_splitk(p, stream, plan.split);
+    case NVFP4_GEMM_GEMV16:
+      return launch_gemv16<false>(p, FusedQuant{}, stream, dev.num_cus);
     case NVFP4_GEMM_FIT: {
       const int64_t tfit = ((p.M + kFitBM - 1) / kFitBM) * ((p.N + kFitBN - 1) / kFitBN);
       if (tfit > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1557,15 +1779,22 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
 }
 
 bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
+  // activations small enough to quantize in every workgroup (and to sit in its LDS), on
+  // the GEMM the product would run: the 16-row kernel, or split-K with one 32-row
+  // activation group
+  if (M > 32 || M * K > kFuseElems) return false;
   const GemmPlan g = plan_gemm(M, N, K, aligned, cus);
-  // one 32-row activation group, and activations small enough to quantize in every
-  // workgroup (and to sit in its LDS)
-  return g.kernel == NVFP4_GEMM_SPLITK && M <= 32 && M * K <= kFuseElems;
+  return g.kernel == NVFP4_GEMM_GEMV16 || g.kernel == NVFP4_GEMM_SPLITK;
 }
 
-hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream) {
+hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream,
+                               int64_t cus) {
+  if (p.M > 32 || p.M * p.K > kFuseElems) return hipErrorInvalidValue;
+  // (the entry points have checked the operands' alignment, as linear_fused assumes)
+  if (plan_gemm(p.M, p.N, p.K, true, cus).kernel == NVFP4_GEMM_GEMV16)
+    return launch_gemv16<true>(p, fq, stream, cus);
   const int64_t wgs = (p.N + 31) / 32;
-  if (p.M > 32 || p.M * p.K > kFuseElems || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.K % 64 == 0)
     launch_splitk_kernel<1, 1, 4, 4, true, true>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
   else

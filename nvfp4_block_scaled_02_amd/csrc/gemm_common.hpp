@@ -138,6 +138,18 @@ NVFP4_HD uint32_t scale_piece_voff(int lane, int prow, uint32_t spitch, uint32_t
   return (uint32_t)(prow + lane) * spitch + kbyte;
 }
 
+// Per-lane offsets of the 16-row kernel's loads (gemm_gemv16_kernel) through a row window:
+// lane (r, q) reads, of row r and 256-element group g of K (one 128-byte line of codes and
+// 16 scale bytes per row), code bytes 32q + 16h .. + 15 (half h = 0, 1) and scale bytes
+// 4q .. 4q + 3. The row is in the checked offset, and with K % 256 == 0 every load lies
+// inside its row.
+NVFP4_HD uint32_t gemv_code_voff(int r, int q, int h, int g, uint32_t pitch) {
+  return (uint32_t)r * pitch + (uint32_t)g * 128u + 32u * (uint32_t)q + 16u * (uint32_t)h;
+}
+NVFP4_HD uint32_t gemv_scale_voff(int r, int q, int g, uint32_t spitch) {
+  return (uint32_t)r * spitch + (uint32_t)g * 16u + 4u * (uint32_t)q;
+}
+
 // Swizzle of the W4A16 kernels' bf16 activation rows (128 bytes of a stage, eight 16-byte
 // chunks): chunk c of row r (r = row within its 32-row group) sits at slot c ^ x_swz(r).
 NVFP4_HD int x_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }

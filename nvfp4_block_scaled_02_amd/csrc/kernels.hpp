@@ -75,7 +75,8 @@ struct FusedQuant {
   uint8_t* ws_scales;     // [M, K/16] scales out
 };
 bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus);
-hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream);
+hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream,
+                               int64_t cus);
 
 // The kernel launch_gemm picks for a shape (values of nvfp4_gemm_kernel in nvfp4.h), and
 // the split-K workgroup shape (32a weight rows x 32b activation rows) when it splits.
@@ -84,7 +85,8 @@ struct GemmPlan {
   int kernel;
   SplitShape split;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus,
+                   bool allow_gemv16 = true);
 
 struct W4A16Problem {
   const uint16_t* x;  // bf16 [M, K]

@@ -229,7 +229,7 @@ def fp8r_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
 
 
 GEMM_KERNELS = {0: "tile256", 1: "fit", 2: "splitk", 3: "generic", 4: "tile128", 5: "tile128x128", 6: "tile128x64",
-                7: "wsplit64", 8: "wsplit128"}
+                7: "wsplit64", 8: "wsplit128", 9: "gemv16"}
 
 
 def gemm_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:

@@ -153,6 +153,29 @@ void splitk(Stats& st, int64_t rows, int64_t K, int ngrp) {
   });
 }
 
+// 16-row kernel (at most 32 activation rows): a window of rows [b R, rows) per workgroup b
+// for the weights (lanes r < R load) and [0, M) for the activations (lane r loads rows r
+// and 16 + r below M); lane (r, q) reads 16 code bytes at 128 g + 32 q + 16 h and 4 scale
+// bytes at 16 g + 4 q of group g (K % 256 == 0).
+void gemv16(Stats& st, int64_t rows, int64_t K, int R, bool weights) {
+  const uint32_t pitch = (uint32_t)(K / 2), spitch = (uint32_t)(K / 16);
+  const int ngt = (int)(K / 256);
+  const int64_t step = weights ? R : rows;
+  for (int64_t r0 = 0; r0 < rows; r0 += step)
+    for (int slot = 0; slot < (weights ? 64 : 128); ++slot) {
+      const int lane = slot & 63, r = (slot >> 6) * 16 + (lane & 15), q = lane >> 4;
+      if (weights ? r >= R : r >= rows) continue;  // lanes that load nothing
+      const int64_t row = r0 + r;
+      for (int g = 0; g < ngt; ++g) {
+        for (int h = 0; h < 2; ++h)
+          check_load(st, "gemv16-codes", rows, pitch, r0, gemv_code_voff(r, q, h, g, pitch), 0, 16,
+                     row, (int64_t)g * 128 + 32 * q + 16 * h);
+        check_load(st, "gemv16-scales", rows, spitch, r0, gemv_scale_voff(r, q, g, spitch), 0, 4, row,
+                   (int64_t)g * 16 + 4 * q);
+      }
+    }
+}
+
 // W4A16 256 x 256 and 288 x 192 kernels: activation pieces of 8 rows x 128 bytes (xpitch
 // 2K, scalar offset stage * 128), weight groups of 32 rows x 32 bytes (stage * 32), scale
 // pieces of 64 rows x 4 bytes (stage * 4); K % 64 == 0.
@@ -254,6 +277,16 @@ int main(int argc, char** argv) {
       for (int64_t K : Ks)
         for (int ngrp : {1, 2, 4}) splitk(st, R, K, ngrp);
     report("splitk", st, bad);
+  }
+  {
+    Stats st;
+    const int64_t Ks[] = {256, 768, 3072};
+    for (int64_t R : rows_list)
+      for (int64_t K : Ks) {
+        for (int wr : {4, 8, 12, 16}) gemv16(st, R, K, wr, true);
+        if (R <= 32) gemv16(st, R, K, 16, false);
+      }
+    report("gemv16", st, bad);
   }
   {
     Stats st;

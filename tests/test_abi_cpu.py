@@ -108,7 +108,8 @@ def test_gemm_validation(lib):
 
 def test_gemm_plan_routes_shapes(lib):
     """The planner (host only) sends the FLUX activations (4608 rows) to the 288 x 192
-    tile, short activations (at most 32 rows, or a few rows of wide weights) to split-K, a
+    tile, at most 32 activation rows with K % 256 == 0 to the 16-row kernel, other short
+    activations (at most 32 rows, or a few rows of wide weights) to split-K, a
     few hundred rows whose 64 x 64 tiles fit one pass to the kernel whose waves split K,
     and shapes whose tile count fits 256-tile passes better to the 256 x 256 tile;
     K % 128 != 0 needs the register-staged kernel."""
@@ -117,12 +118,20 @@ def test_gemm_plan_routes_shapes(lib):
         st = lib.nvfp4_gemm_plan(M, N, K, cus, ctypes.byref(k))
         return st, k.value
 
-    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864, WS64, WS128 = 1, 0, 2, 3, 4, 5, 6, 7, 8
+    FIT, TILE, SPLIT, GEN, T128, T128SQ, T12864, WS64, WS128, GEMV = 1, 0, 2, 3, 4, 5, 6, 7, 8, 9
     for M, N, K in [(4608, 3072, 3072), (4608, 12288, 3072), (4608, 3072, 12288),
                     (4608, 9216, 3072), (2600, 3000, 128), (1000, 12288, 3072)]:
         assert plan(M, N, K) == (L.SUCCESS, FIT), (M, N, K)
-    for M in (1, 17, 32):
-        assert plan(M, 3072, 3072) == (L.SUCCESS, SPLIT), M
+    # at most 16 rows, or 32 while 16-row workgroups fit one pass (K % 256 == 0): the
+    # weights' read spread over the chip
+    for M, N, K in [(1, 3072, 3072), (16, 3072, 3072), (17, 3072, 3072), (32, 3072, 3072),
+                    (1, 3072, 12288), (5, 12288, 256), (1, 18432, 3072), (16, 18432, 3072),
+                    (32, 4096, 3072), (16, 9216, 3072)]:
+        assert plan(M, N, K) == (L.SUCCESS, GEMV), (M, N, K)
+    assert plan(17, 18432, 3072) == (L.SUCCESS, SPLIT)
+    assert plan(32, 4112, 3072) == (L.SUCCESS, SPLIT)
+    for M, K in [(1, 3072 + 128), (17, 3072 + 128), (32, 1056)]:   # K % 256 != 0
+        assert plan(M, 3072, K) == (L.SUCCESS, SPLIT), (M, K)
     # beyond 32 rows, while its 64 x 64 tiles fit one pass over the compute units, the
     # kernel whose waves split K
     for M in (64, 128, 256, 320):
@@ -133,8 +142,6 @@ def test_gemm_plan_routes_shapes(lib):
     assert plan(256, 3072, 3072, 128) == (L.SUCCESS, T12864)   # two passes on 128 units
     assert plan(256, 3072, 3000) != (L.SUCCESS, WS64)            # K % 512 != 0
     # wide weights with few rows: split-K's workgroups still fill the chip
-    for M, N in [(1, 18432), (17, 18432)]:
-        assert plan(M, N, 3072) == (L.SUCCESS, SPLIT), (M, N)
     assert plan(64, 18432, 3072) == (L.SUCCESS, T128SQ)
     assert plan(128, 12288, 3072) == (L.SUCCESS, T12864)
     assert plan(256, 12288, 3072) == (L.SUCCESS, T128SQ)

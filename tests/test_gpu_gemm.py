@@ -89,6 +89,14 @@ def test_gemm_small_shapes_in_full(M, N, K):
     # second half is the loop's tail)
     (4096, 4096, 128, "tile256"), (4096, 4096, 1152, "tile256"),
     (600, 700, 208, "generic"),
+    # at most 32 activation rows: 4, 8, 12 and 16 weight rows per workgroup (one per
+    # compute unit at N = 1024, 2048, 3072 and beyond), four or eight waves, one to 48
+    # groups of 256 along K (a wave with none, the ring of four refilled), ragged last
+    # workgroups, one or two 16-row activation blocks
+    (1, 4, 256, "gemv16"), (5, 101, 256, "gemv16"), (16, 1000, 2816, "gemv16"),
+    (3, 2050, 12288, "gemv16"), (1, 3072, 3072, "gemv16"), (16, 3072, 3072, "gemv16"),
+    (7, 12289, 512, "gemv16"), (2, 5000, 2048, "gemv16"), (17, 3072, 3072, "gemv16"),
+    (32, 700, 768, "gemv16"), (25, 4000, 1280, "gemv16"), (20, 2050, 6144, "gemv16"),
 ])
 def test_gemm_tiled_kernels_in_full(M, N, K, kernel):
     assert nv.gemm_plan(M, N, K) == kernel
@@ -143,7 +151,7 @@ _EXTREME_PAIRS = [
     (64, 128, 128, "splitk"), (600, 700, 256, "tile128x64"), (1500, 2500, 128, "tile128x128"),
     (130, 777, 1536, "wsplit64"), (1023, 2049, 4352, "wsplit128"),
     (2600, 1650, 384, "tile128"), (2600, 3000, 128, "fit"), (4096, 4096, 128, "tile256"),
-    (600, 700, 208, "generic"),
+    (600, 700, 208, "generic"), (9, 301, 768, "gemv16"), (20, 130, 512, "gemv16"),
 ])
 def test_gemm_extreme_global_scale_pairs(M, N, K, kernel, pair):
     """Every kernel's epilogue against the oracle (whose a_gs * w_gs is exact in float64)
@@ -200,6 +208,7 @@ def test_linear_matches_quantize_then_gemm(name):
 
 
 @pytest.mark.parametrize("M,N,K,plan", [(1, 640, 256, "fused"), (17, 3072, 1024, "two_kernels"),
+                                         (16, 3072, 1280, "two_kernels"),
                                          (600, 700, 256, "two_kernels")])
 def test_linear_calibrated_scales_with_subnormal_product(M, N, K, plan):
     """nvfp4_linear on tensors of magnitude 2^-70 and 2^-60 (all positive, so the sums do

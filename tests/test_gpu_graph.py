@@ -15,7 +15,8 @@ from workloads import to_bf16_bits
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,N,K", [(4608, 3072, 3072), (300, 512, 1024), (1, 3072, 3072), (17, 640, 256)])
+@pytest.mark.parametrize("M,N,K", [(4608, 3072, 3072), (300, 512, 1024), (1, 3072, 3072), (17, 640, 256),
+                                   (17, 3072, 3072), (17, 640, 160), (64, 3072, 1056)])
 def test_linear_graph_replays_match_eager(M, N, K):
     rng = np.random.default_rng(M + N + K)
     w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
