@@ -1586,13 +1586,6 @@ hipError_t launch_splitk(const GemmProblem& p, hipStream_t stream, SplitShape s)
   return hipGetLastError();
 }
 
-// Weight rows per workgroup of the 16-row kernel: a multiple of 4 up to 16, the fewest
-// that keep the grid within one workgroup per compute unit.
-int gemv16_rows(int64_t N, int64_t cus) {
-  const int64_t r = 4 * ((N + 4 * cus - 1) / (4 * cus));
-  return (int)(r < 4 ? 4 : r > 16 ? 16 : r);
-}
-
 template <int NW, int B, bool kFuse>
 void launch_gemv16_kernel(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream,
                           unsigned wgs, int R) {

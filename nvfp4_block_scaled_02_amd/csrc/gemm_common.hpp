@@ -150,6 +150,12 @@ NVFP4_HD uint32_t gemv_scale_voff(int r, int q, int g, uint32_t spitch) {
   return (uint32_t)r * spitch + (uint32_t)g * 16u + 4u * (uint32_t)q;
 }
 
+// The W4A16 16-row kernel's bf16 activation loads: lane (r, q) reads 16 bytes k = 0..7 of
+// its 128-byte quarter of group g (elements 64q + 8k .. + 7) of activation row r.
+NVFP4_HD uint32_t gemv_x16_voff(int r, int q, int k, int g, uint32_t xpitch) {
+  return (uint32_t)r * xpitch + (uint32_t)g * 512u + 128u * (uint32_t)q + 16u * (uint32_t)k;
+}
+
 // Swizzle of the W4A16 kernels' bf16 activation rows (128 bytes of a stage, eight 16-byte
 // chunks): chunk c of row r (r = row within its 32-row group) sits at slot c ^ x_swz(r).
 NVFP4_HD int x_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }

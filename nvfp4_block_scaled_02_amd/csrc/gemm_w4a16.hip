@@ -183,6 +183,115 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
   }
 }
 
+// ---- at most 16 activation rows: weight rows spread over the whole chip ------------------
+//
+// The layout of the NVFP4 16-row kernel (gemm.hip) with bf16 activations: a workgroup owns
+// R <= 16 weight rows (gemv16_rows: 12 at N = 3072, 256 workgroups), its NW waves take the
+// 256-element groups of K in turn, and a 16 x 16 x 32 bf16 MFMA block holds the R weight
+// rows against up to 16 activation rows. Lane (r, q) loads 32 code bytes and 4 scale
+// bytes of weight row r (elements 64q .. 64q + 63 of the group) and the same 64 elements
+// of activation row r (128 bytes); word j of code half h, decoded to bf16 exactly, meets
+// activation bytes 16(4h + j) .. + 15 (the same elements 64q + 32h + 8j .. + 7) in MFMA
+// 4h + j. Lanes past the R weight rows or the M activation rows load nothing. The NW
+// partial sums meet in LDS in wave order.
+//
+// Requires M <= 16, K % 256 == 0, 16-byte aligned x, packed weights and output, 4-byte
+// aligned scales, and operands below 2^31 bytes.
+template <int NW, int DG>
+__global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem p, int R) {
+  typedef float floatx4 __attribute__((ext_vector_type(4)));
+  __shared__ floatx4 red[NW][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+  const uint32_t pitch = (uint32_t)(p.K >> 1);
+  const uint32_t spitch = (uint32_t)(p.K >> 4);
+  const uint32_t xpitch = (uint32_t)(p.K * 2);
+  const int ngt = (int)(p.K / 256);
+  const int ng = (ngt - wave + NW - 1) / NW;  // this wave's groups: wave, wave + NW, ...
+  const bool wlive = r < R;
+  const bool xlive = r < p.M;
+  const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
+  const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
+  const __amdgpu_buffer_rsrc_t rx = window_rsrc(p.x, 0, p.M, xpitch);
+
+  u32x4 wc[DG][2], xc[DG][8];
+  uint32_t wsv[DG];
+  auto load = [&](int s, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      wc[s][h] = u32x4{0u, 0u, 0u, 0u};
+      if (wlive)
+        wc[s][h] = __builtin_amdgcn_raw_buffer_load_b128(rwp, (int)gemv_code_voff(r, q, h, g, pitch), 0, 0);
+    }
+    wsv[s] = 0u;
+    if (wlive) wsv[s] = __builtin_amdgcn_raw_buffer_load_b32(rws, (int)gemv_scale_voff(r, q, g, spitch), 0, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xc[s][k] = u32x4{0u, 0u, 0u, 0u};
+      if (xlive) xc[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)gemv_x16_voff(r, q, k, g, xpitch), 0, 0);
+    }
+  };
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // word j of half h: block 4q + 2h + j / 2, byte 2h + j / 2 of the lane's scale word
+      const float2_t sf = scales_to_f32(wsv[s] >> (16 * h));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t wf = decode8_bf16(wc[s][h][j], j < 2 ? sf[0] : sf[1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8_t, xc[s][4 * h + j]),
+                                                      acc, 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < DG; ++s)
+    if (s < ng) load(s, wave + NW * s);
+  for (int i = 0; i < ng; i += DG) {
+#pragma unroll
+    for (int s = 0; s < DG; ++s) {
+      if (i + s < ng) {
+        compute(s);
+        if (i + s + DG < ng) load(s, wave + NW * (i + s + DG));
+      }
+    }
+  }
+
+  // lane (r, q) holds output row r, columns n0 + 4q + {0..3}; wave 0 adds the NW parts in
+  // wave order, scales, rounds and stores them
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t n = n0 + 4 * q;
+  if (r >= p.M || 4 * q >= R || n >= p.N) return;
+  float tot[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) tot[e] = red[0][lane][e];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    const floatx4 part = red[w][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tot[e] += part[e];
+  }
+  float sv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sv[e] = tot[e] * p.alpha;
+  const u32x2 bits = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
+  uint16_t* orow = p.out + (int64_t)r * p.N;
+  if ((p.N & 3) == 0 && n + 3 < p.N) {
+    *(u32x2*)&orow[n] = bits;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < p.N) orow[n + e] = (uint16_t)(bits[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 // ---- tiled form for long activations -------------------------------------------------
 //
 // 256 x 256 output tiles, 2 x 2 waves of 128 x 128 (4 x 4 blocks of 32 x 32), the bf16
@@ -807,6 +916,13 @@ W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bo
   // compute units times its stage cost.
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const bool fits32 = fits_i31(M + 288, 2 * K) && fits_i31(N + 256, K / 2);
+  // at most 16 rows (K % 256 == 0): the weights' read spread over the whole chip, up to
+  // three passes of 16-row workgroups (its 186 VGPRs hold one 512-thread workgroup per
+  // compute unit; measured: 1 x 12288 x 3072 10.2 us against split-K's 11.9, 8 x 18432 x
+  // 3072 20.3 against 18.9)
+  if (aligned && M <= 16 && K % 256 == 0 && (N + 15) / 16 <= 3 * cus && fits_i31(M + 16, 2 * K) &&
+      fits_i31(N + 16, K / 2))
+    return W4A16Kernel::kGemv16;
   if (K % 64 != 0 || !fits32 || !aligned || M <= 64) return W4A16Kernel::kSplitK;
   auto cost = [&](int bm, int bn, bool quad) {
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
@@ -860,6 +976,17 @@ hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const La
       const int64_t t = tiles_of(256, 256, false);
       if (t > 0x7FFFFFFF) return hipErrorInvalidValue;
       hipLaunchKernelGGL((gemm_w4a16_tile_kernel<256, 256>), dim3((unsigned)t), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+    case W4A16Kernel::kGemv16: {
+      const int R = gemv16_rows(p.N, dev.num_cus > 0 ? dev.num_cus : 256);
+      const int64_t wgs = (p.N + R - 1) / R;
+      if (wgs > 0x7FFFFFFF || p.M > 16 || p.K % 256 != 0) return hipErrorInvalidValue;
+      // eight waves once K has eight groups (more loads in flight per compute unit)
+      if (p.K / 256 >= 8)
+        hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<8, 4>), dim3((unsigned)wgs), dim3(512), 0, stream, p, R);
+      else
+        hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<4, 4>), dim3((unsigned)wgs), dim3(256), 0, stream, p, R);
       return hipGetLastError();
     }
     case W4A16Kernel::kSplitK:

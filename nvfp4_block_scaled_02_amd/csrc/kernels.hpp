@@ -88,6 +88,13 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus,
                    bool allow_gemv16 = true);
 
+// Weight rows per workgroup of the 16-row kernels (NVFP4 and W4A16): a multiple of 4 up
+// to 16, the fewest that keep the grid within one workgroup per compute unit.
+inline int gemv16_rows(int64_t N, int64_t cus) {
+  const int64_t r = 4 * ((N + 4 * cus - 1) / (4 * cus));
+  return (int)(r < 4 ? 4 : r > 16 ? 16 : r);
+}
+
 struct W4A16Problem {
   const uint16_t* x;  // bf16 [M, K]
   const uint8_t* w_packed;
@@ -98,11 +105,11 @@ struct W4A16Problem {
 };
 
 // W4A16 kernels, in the order of the plan codes: split-K (short activations), the 288 x 192
-// tile, the 256 x 256 tile, and the tiles with their waves along N: 224 x 256, 128 x 256,
-// 96 x 256, 128 x 128 and 64 x 128.
+// tile, the 256 x 256 tile, the tiles with their waves along N: 224 x 256, 128 x 256,
+// 96 x 256, 128 x 128 and 64 x 128, and the 16-row kernel (at most 16 activation rows).
 enum class W4A16Kernel {
   kSplitK = 0, kFit = 1, kTile256 = 2, kWide = 3, kWide128x256 = 4, kWide96x256 = 5,
-  kWide128x128 = 6, kWide64x128 = 7
+  kWide128x128 = 6, kWide64x128 = 7, kGemv16 = 8
 };
 W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bool aligned);
 hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const LaunchInfo& dev);

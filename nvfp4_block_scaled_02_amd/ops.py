@@ -241,7 +241,7 @@ def gemm_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:
 
 
 W4A16_KERNELS = {0: "splitk", 1: "fit", 2: "tile256", 3: "wide", 4: "wide128x256", 5: "wide96x256",
-                 6: "wide128x128", 7: "wide64x128"}
+                 6: "wide128x128", 7: "wide64x128", 8: "gemv16"}
 
 
 def gemm_w4a16_plan(M: int, N: int, K: int, num_cus: int = 0) -> str:

@@ -232,7 +232,7 @@ int main() {
           EXPECT_TRUE(s2 == OK || s2 == SHAPE);
           EXPECT_TRUE(s3 == OK || s3 == SHAPE);
           if (s1 == OK) EXPECT_TRUE(k1 >= 0 && k1 <= 9);
-          if (s2 == OK) EXPECT_TRUE(k2 >= 0 && k2 <= 7);
+          if (s2 == OK) EXPECT_TRUE(k2 >= 0 && k2 <= 8);
           if (s3 == OK) EXPECT_TRUE(f == 0 || f == 1);
           if (cus != 0) continue;
           // rejected shapes fail the same way in the entry points (accepted ones would reach

@@ -176,6 +176,20 @@ void gemv16(Stats& st, int64_t rows, int64_t K, int R, bool weights) {
     }
 }
 
+// W4A16 16-row kernel's bf16 activation loads: window [0, M), lanes r < M, 16 bytes k of
+// the lane's 128-byte quarter of group g (K % 256 == 0).
+void w4a16_gemv16_x(Stats& st, int64_t M, int64_t K) {
+  const uint32_t xpitch = (uint32_t)(2 * K);
+  for (int lane = 0; lane < 64; ++lane) {
+    const int r = lane & 15, q = lane >> 4;
+    if (r >= M) continue;
+    for (int g = 0; g < (int)(K / 256); ++g)
+      for (int k = 0; k < 8; ++k)
+        check_load(st, "w4a16-gemv16-x", M, xpitch, 0, gemv_x16_voff(r, q, k, g, xpitch), 0, 16, r,
+                   (int64_t)g * 512 + 128 * q + 16 * k);
+  }
+}
+
 // W4A16 256 x 256 and 288 x 192 kernels: activation pieces of 8 rows x 128 bytes (xpitch
 // 2K, scalar offset stage * 128), weight groups of 32 rows x 32 bytes (stage * 32), scale
 // pieces of 64 rows x 4 bytes (stage * 4); K % 64 == 0.
@@ -287,6 +301,12 @@ int main(int argc, char** argv) {
         if (R <= 32) gemv16(st, R, K, 16, false);
       }
     report("gemv16", st, bad);
+  }
+  {
+    Stats st;
+    for (int64_t M = 1; M <= 16; ++M)
+      for (int64_t K : {256, 768, 3072}) w4a16_gemv16_x(st, M, K);
+    report("w4a16-gemv16", st, bad);
   }
   {
     Stats st;

@@ -30,7 +30,7 @@ def report(tmp_path_factory):
     return r
 
 
-@pytest.mark.parametrize("family", ["nvfp4-code-pieces", "nvfp4-scale-pieces", "splitk", "gemv16", "mxfp8",
+@pytest.mark.parametrize("family", ["nvfp4-code-pieces", "nvfp4-scale-pieces", "splitk", "gemv16", "w4a16-gemv16", "mxfp8",
                                     "w4a16-tiled", "w4a16-splitk"])
 def test_no_load_leaves_its_operand(report, family):
     lines = {l.split(" loads ")[0]: l for l in report.stdout.splitlines() if " loads " in l}
