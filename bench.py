@@ -257,12 +257,19 @@ class Timer:
 
         self.torch, self.stream, self.clock = torch, stream, clock
 
-    def launches(self, fn, n: int, warm: int):
+    def launches(self, fn, n: int, warm: int, warm_seconds: float = 0.0):
         """Average ms of n back-to-back launches of fn on the stream, after `warm` untimed
-        ones; returns (ms, clock summary of the timed launches)."""
+        ones and, with warm_seconds, more untimed ones until that much wall time has passed
+        (the GPU clock takes milliseconds to rise again after memory-bound work); returns
+        (ms, clock summary of the timed launches)."""
         torch = self.torch
         for _ in range(warm):
             fn()
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < warm_seconds:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -393,9 +400,9 @@ def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         al = (P(x), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y),
               P(work), ctypes.c_size_t(nb), sp)
-        ms_l, clk_l = timer.launches(lambda: lib.nvfp4_linear(*al), n, warm)
+        ms_l, clk_l = timer.launches(lambda: lib.nvfp4_linear(*al), n, warm, warm_seconds=0.3)
         ag = (P(ap), P(as_), ctypes.c_float(ags), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
-        ms_g, clk_g = timer.launches(lambda: lib.nvfp4_gemm(*ag), n, warm)
+        ms_g, clk_g = timer.launches(lambda: lib.nvfp4_gemm(*ag), n, warm, warm_seconds=0.3)
         fl = 2.0 * M * N * K
         out["linear"][name] = {
             "M": M, "N": N, "K": K, "gemm_kernel": nv.gemm_plan(M, N, K),
@@ -408,7 +415,7 @@ def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
         if name == "attn_out":
             # hipBLASLt bf16 GEMM of the unquantized operands at the same shape
             wt = w.t().contiguous()
-            ms_b, _ = timer.launches(lambda: torch.matmul(x, wt, out=y), n, warm)
+            ms_b, _ = timer.launches(lambda: torch.matmul(x, wt, out=y), n, warm, warm_seconds=0.2)
             out["hipblaslt_bf16_matmul"] = {"shape": [M, N, K], "avg_ms": round(ms_b, 5),
                                             "TFLOP/s": round(fl / (ms_b * 1e-3) / 1e12, 1)}
             del wt
@@ -416,7 +423,7 @@ def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
             ac, asx = nv.mxfp8_quantize(x)
             wc, wsx = nv.mxfp8_quantize(w)
             a8 = (P(ac), P(asx), P(wc), P(wsx), M, N, K, P(y), sp)
-            ms8, _ = timer.launches(lambda: lib.nvfp4_mxfp8_gemm(*a8), n, warm)
+            ms8, _ = timer.launches(lambda: lib.nvfp4_mxfp8_gemm(*a8), n, warm, warm_seconds=0.2)
             q8 = (P(x), M, K, P(ac), P(asx), sp)
             msq8, _ = timer.launches(lambda: lib.nvfp4_mxfp8_quantize(*q8), n, warm)
             out["mxfp8"] = {"shape": [M, N, K], "gemm_avg_ms": round(ms8, 5),
@@ -429,7 +436,7 @@ def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
             rc, rs = nv.fp8r_quantize(x)
             wrc, wrs = nv.fp8r_quantize(w)
             ar = (P(rc), P(rs), P(wrc), P(wrs), M, N, K, P(y), sp)
-            msr, _ = timer.launches(lambda: lib.nvfp4_fp8r_gemm(*ar), n, warm)
+            msr, _ = timer.launches(lambda: lib.nvfp4_fp8r_gemm(*ar), n, warm, warm_seconds=0.2)
             qr = (P(x), M, K, P(rc), P(rs), sp)
             msqr, _ = timer.launches(lambda: lib.nvfp4_fp8r_quantize(*qr), n, warm)
             out["fp8r"] = {"shape": [M, N, K], "gemm_avg_ms": round(msr, 5),
@@ -440,7 +447,7 @@ def context_legs(nv, lib, timer, stream, n, rotate_weights_mb=512):
             del rc, rs, wrc, wrs
             # W4A16: NVFP4 weights, bf16 activations
             a16 = (P(x), P(wp), P(ws), ctypes.c_float(wgs), M, N, K, P(y), sp)
-            ms16, _ = timer.launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, warm)
+            ms16, _ = timer.launches(lambda: lib.nvfp4_gemm_w4a16(*a16), n, warm, warm_seconds=0.2)
             out["w4a16"] = {"shape": [M, N, K], "kernel": nv.gemm_w4a16_plan(M, N, K),
                             "avg_ms": round(ms16, 5), "TFLOP/s": round(fl / (ms16 * 1e-3) / 1e12, 1)}
         del x, w, wp, ws, work, ap, as_, y
@@ -653,7 +660,7 @@ def main():
                      "bf16 output",
     }
     if not args.no_context:
-        result["context"] = context_legs(nv, lib, timer, stream, max(50, args.steps // 2))
+        result["context"] = context_legs(nv, lib, timer, stream, max(200, args.steps // 2))
     clock.stop()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, ags, wgs, args.cpu_seconds)
