@@ -185,8 +185,9 @@ typedef enum {
   NVFP4_W4A16_WIDE96X256 = 5,  /* 96 x 256, */
   NVFP4_W4A16_WIDE128X128 = 6, /* 128 x 128 */
   NVFP4_W4A16_WIDE64X128 = 7, /* and 64 x 128 tiles: medium and short activations */
-  NVFP4_W4A16_GEMV16 = 8       /* at most 16 activation rows (K % 256 == 0): 4 to 16 weight
-                                  rows per workgroup on 16 x 16 x 32 bf16 MFMAs */
+  NVFP4_W4A16_GEMV16 = 8       /* at most 16 activation rows, or 32 where N <= 16 x the
+                                  compute units (K % 256 == 0): 4 to 16 weight rows per
+                                  workgroup on 16 x 16 x 32 bf16 MFMAs */
 } nvfp4_w4a16_kernel;
 
 /*

@@ -197,10 +197,10 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W4A16Problem p) {
 //
 // Requires M <= 16, K % 256 == 0, 16-byte aligned x, packed weights and output, 4-byte
 // aligned scales, and operands below 2^31 bytes.
-template <int NW, int DG>
+template <int NW, int DG, int B>
 __global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem p, int R) {
   typedef float floatx4 __attribute__((ext_vector_type(4)));
-  __shared__ floatx4 red[NW][64];
+  __shared__ floatx4 red[NW][B][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
@@ -212,12 +212,11 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem
   const int ngt = (int)(p.K / 256);
   const int ng = (ngt - wave + NW - 1) / NW;  // this wave's groups: wave, wave + NW, ...
   const bool wlive = r < R;
-  const bool xlive = r < p.M;
   const __amdgpu_buffer_rsrc_t rwp = window_rsrc(p.w_packed, n0, p.N, pitch);
   const __amdgpu_buffer_rsrc_t rws = window_rsrc(p.w_scales, n0, p.N, spitch);
   const __amdgpu_buffer_rsrc_t rx = window_rsrc(p.x, 0, p.M, xpitch);
 
-  u32x4 wc[DG][2], xc[DG][8];
+  u32x4 wc[DG][2], xc[DG][B][8];
   uint32_t wsv[DG];
   auto load = [&](int s, int g) {
 #pragma unroll
@@ -229,12 +228,17 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem
     wsv[s] = 0u;
     if (wlive) wsv[s] = __builtin_amdgcn_raw_buffer_load_b32(rws, (int)gemv_scale_voff(r, q, g, spitch), 0, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xc[s][k] = u32x4{0u, 0u, 0u, 0u};
-      if (xlive) xc[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)gemv_x16_voff(r, q, k, g, xpitch), 0, 0);
-    }
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xc[s][b][k] = u32x4{0u, 0u, 0u, 0u};
+        if (16 * b + r < p.M)
+          xc[s][b][k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)gemv_x16_voff(16 * b + r, q, k, g, xpitch), 0, 0);
+      }
   };
-  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  floatx4 acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](int s) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -243,8 +247,10 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t wf = decode8_bf16(wc[s][h][j], j < 2 ? sf[0] : sf[1]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8_t, xc[s][4 * h + j]),
-                                                      acc, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, __builtin_bit_cast(bf16x8_t, xc[s][b][4 * h + j]),
+                                                           acc[b], 0, 0, 0);
       }
     }
   };
@@ -262,33 +268,39 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4a16_gemv16_kernel(W4A16Problem
     }
   }
 
-  // lane (r, q) holds output row r, columns n0 + 4q + {0..3}; wave 0 adds the NW parts in
-  // wave order, scales, rounds and stores them
-  red[wave][lane] = acc;
+  // lane (r, q) holds output rows 16b + r, columns n0 + 4q + {0..3} in acc[b]; wave 0 adds
+  // the NW parts in wave order, scales, rounds and stores them
+#pragma unroll
+  for (int b = 0; b < B; ++b) red[wave][b][lane] = acc[b];
   __syncthreads();
   if (wave != 0) return;
   const int64_t n = n0 + 4 * q;
-  if (r >= p.M || 4 * q >= R || n >= p.N) return;
-  float tot[4];
+  if (4 * q >= R || n >= p.N) return;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) tot[e] = red[0][lane][e];
+  for (int b = 0; b < B; ++b) {
+    const int64_t m = 16 * b + r;
+    if (m >= p.M) continue;
+    float tot[4];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    const floatx4 part = red[w][lane];
+    for (int e = 0; e < 4; ++e) tot[e] = red[0][b][lane][e];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tot[e] += part[e];
-  }
-  float sv[4];
+    for (int w = 1; w < NW; ++w) {
+      const floatx4 part = red[w][b][lane];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sv[e] = tot[e] * p.alpha;
-  const u32x2 bits = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
-  uint16_t* orow = p.out + (int64_t)r * p.N;
-  if ((p.N & 3) == 0 && n + 3 < p.N) {
-    *(u32x2*)&orow[n] = bits;
-  } else {
+      for (int e = 0; e < 4; ++e) tot[e] += part[e];
+    }
+    float sv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (n + e < p.N) orow[n + e] = (uint16_t)(bits[e >> 1] >> (16 * (e & 1)));
+    for (int e = 0; e < 4; ++e) sv[e] = tot[e] * p.alpha;
+    const u32x2 bits = bf16x4_rne(sv[0], sv[1], sv[2], sv[3]);
+    uint16_t* orow = p.out + m * p.N;
+    if ((p.N & 3) == 0 && n + 3 < p.N) {
+      *(u32x2*)&orow[n] = bits;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) orow[n + e] = (uint16_t)(bits[e >> 1] >> (16 * (e & 1)));
+    }
   }
 }
 
@@ -919,9 +931,11 @@ W4A16Kernel plan_gemm_w4a16(int64_t M, int64_t N, int64_t K, int64_t num_cus, bo
   // at most 16 rows (K % 256 == 0): the weights' read spread over the whole chip, up to
   // three passes of 16-row workgroups (its 186 VGPRs hold one 512-thread workgroup per
   // compute unit; measured: 1 x 12288 x 3072 10.2 us against split-K's 11.9, 8 x 18432 x
-  // 3072 20.3 against 18.9)
-  if (aligned && M <= 16 && K % 256 == 0 && (N + 15) / 16 <= 3 * cus && fits_i31(M + 16, 2 * K) &&
-      fits_i31(N + 16, K / 2))
+  // 3072 20.3 against 18.9); 17 to 32 rows (two activation blocks, a two-deep ring) in
+  // one pass only
+  const int64_t g16 = (N + 15) / 16;
+  if (aligned && K % 256 == 0 && (M <= 16 ? g16 <= 3 * cus : (M <= 32 && g16 <= cus)) &&
+      fits_i31(M + 32, 2 * K) && fits_i31(N + 16, K / 2))
     return W4A16Kernel::kGemv16;
   if (K % 64 != 0 || !fits32 || !aligned || M <= 64) return W4A16Kernel::kSplitK;
   auto cost = [&](int bm, int bn, bool quad) {
@@ -981,12 +995,18 @@ hipError_t launch_gemm_w4a16(const W4A16Problem& p, hipStream_t stream, const La
     case W4A16Kernel::kGemv16: {
       const int R = gemv16_rows(p.N, dev.num_cus > 0 ? dev.num_cus : 256);
       const int64_t wgs = (p.N + R - 1) / R;
-      if (wgs > 0x7FFFFFFF || p.M > 16 || p.K % 256 != 0) return hipErrorInvalidValue;
-      // eight waves once K has eight groups (more loads in flight per compute unit)
-      if (p.K / 256 >= 8)
-        hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<8, 4>), dim3((unsigned)wgs), dim3(512), 0, stream, p, R);
-      else
-        hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<4, 4>), dim3((unsigned)wgs), dim3(256), 0, stream, p, R);
+      if (wgs > 0x7FFFFFFF || p.M > 32 || p.K % 256 != 0) return hipErrorInvalidValue;
+      // eight waves once K has eight groups (more loads in flight per compute unit); one or
+      // two 16-row activation blocks
+      const bool wide = p.K / 256 >= 8;
+      const dim3 gd((unsigned)wgs);
+      if (p.M <= 16) {
+        if (wide) hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<8, 4, 1>), gd, dim3(512), 0, stream, p, R);
+        else hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<4, 4, 1>), gd, dim3(256), 0, stream, p, R);
+      } else {
+        if (wide) hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<8, 2, 2>), gd, dim3(512), 0, stream, p, R);
+        else hipLaunchKernelGGL((gemm_w4a16_gemv16_kernel<4, 2, 2>), gd, dim3(256), 0, stream, p, R);
+      }
       return hipGetLastError();
     }
     case W4A16Kernel::kSplitK:

@@ -176,12 +176,12 @@ void gemv16(Stats& st, int64_t rows, int64_t K, int R, bool weights) {
     }
 }
 
-// W4A16 16-row kernel's bf16 activation loads: window [0, M), lanes r < M, 16 bytes k of
-// the lane's 128-byte quarter of group g (K % 256 == 0).
+// W4A16 16-row kernel's bf16 activation loads: window [0, M), rows r and 16 + r below M,
+// 16 bytes k of the lane's 128-byte quarter of group g (K % 256 == 0).
 void w4a16_gemv16_x(Stats& st, int64_t M, int64_t K) {
   const uint32_t xpitch = (uint32_t)(2 * K);
-  for (int lane = 0; lane < 64; ++lane) {
-    const int r = lane & 15, q = lane >> 4;
+  for (int slot = 0; slot < 128; ++slot) {   // lanes of both activation blocks
+    const int r = (slot >> 6) * 16 + (slot & 15), q = (slot & 63) >> 4;
     if (r >= M) continue;
     for (int g = 0; g < (int)(K / 256); ++g)
       for (int k = 0; k < 8; ++k)
@@ -304,7 +304,7 @@ int main(int argc, char** argv) {
   }
   {
     Stats st;
-    for (int64_t M = 1; M <= 16; ++M)
+    for (int64_t M = 1; M <= 32; ++M)
       for (int64_t K : {256, 768, 3072}) w4a16_gemv16_x(st, M, K);
     report("w4a16-gemv16", st, bad);
   }

@@ -169,8 +169,8 @@ def test_gemm_plan_routes_shapes(lib):
 
 
 def test_gemm_w4a16_plan_routes_shapes(lib):
-    """The W4A16 planner (host only): at most 16 rows with K % 256 == 0 go to the 16-row
-    kernel, the rest of at most 64 rows (or K % 64 != 0) to split-K;
+    """The W4A16 planner (host only): at most 16 rows (or 32 in one pass) with K % 256 == 0
+    go to the 16-row kernel, the rest of at most 64 rows (or K % 64 != 0) to split-K;
     longer activations to the tiled kernel with the fewest passes over the compute units
     times its per-stage load cost: the FLUX activations to the 224 x 256 tile with its
     waves along N, medium ones to the smaller tiles along N, and the shapes where 288 x 192
@@ -187,7 +187,10 @@ def test_gemm_w4a16_plan_routes_shapes(lib):
     for M, N, K in [(1, 3072, 3072), (16, 3072, 3072), (1, 12288, 3072), (5, 100, 256)]:
         assert plan(M, N, K) == (L.SUCCESS, GEMV), (M, N, K)   # at most 16 rows, K % 256 == 0
     assert plan(8, 18432, 3072) == (L.SUCCESS, SPLIT)          # beyond three passes
-    for M, K in [(17, 3072), (64, 3072), (1, 3136)]:
+    for M in (17, 32):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, GEMV), M                 # one pass
+    assert plan(17, 4112, 3072) == (L.SUCCESS, SPLIT)
+    for M, K in [(33, 3072), (64, 3072), (1, 3136)]:
         assert plan(M, 3072, K) == (L.SUCCESS, SPLIT), (M, K)
     for M in (65, 128, 256, 512):
         assert plan(M, 3072, 3072) == (L.SUCCESS, W64x128), M

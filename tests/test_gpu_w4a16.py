@@ -42,7 +42,8 @@ def _check(got, x, wp, ws, wgs, label):
     # 48 groups of 256 along K, ragged last workgroups
     (1, 4, 256, "gemv16"), (5, 101, 256, "gemv16"), (16, 1000, 2816, "gemv16"),
     (3, 2050, 12288, "gemv16"), (1, 3072, 3072, "gemv16"), (16, 3072, 3072, "gemv16"),
-    (7, 12285, 512, "gemv16"),
+    (7, 12285, 512, "gemv16"), (17, 3072, 3072, "gemv16"), (32, 700, 768, "gemv16"),
+    (25, 4000, 1280, "gemv16"), (20, 2050, 6144, "gemv16"),
     # the tiles with their waves along N, each ragged in M and N, with one stage (K = 64),
     # a partial last quad of scale stages (K / 64 = 3, 5, 7, 17) and whole quads (10)
     (130, 70, 256, "wide64x128"), (65, 3000, 448, "wide64x128"),
@@ -71,7 +72,7 @@ def test_w4a16_small_shapes_in_full(M, N, K, kernel):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [
-    (17, 256, 1024, "splitk"), (9, 301, 768, "gemv16"), (130, 70, 256, "wide64x128"), (2305, 1537, 128, "wide128x128"),
+    (17, 4200, 1024, "splitk"), (9, 301, 768, "gemv16"), (20, 130, 512, "gemv16"), (130, 70, 256, "wide64x128"), (2305, 1537, 128, "wide128x128"),
     (2049, 2081, 64, "wide96x256"), (2017, 3000, 320, "wide128x256"), (3001, 2999, 192, "wide"),
     (4288, 3088, 64, "fit"), (4096, 4096, 64, "tile256")])
 def test_w4a16_every_scale_code(M, N, K, kernel):
