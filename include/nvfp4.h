@@ -293,10 +293,10 @@ int nvfp4_fp8r_gemm(const void* a_codes, const void* a_scales, const void* w_cod
 /*
  * Whether nvfp4_linear (and nvfp4_linear_devgs) run an M x N x K product as one kernel:
  * the short-activation GEMM that nvfp4_gemm would run (the 16-row kernel, or split-K)
- * first quantizing the bf16 activations into its LDS (for at most 32 rows and 16384
- * elements, where repeating that quantization in every workgroup along N costs less than
- * a second launch), instead of the quantize kernel followed by nvfp4_gemm. num_cus as in
- * nvfp4_gemm_plan. Host only.
+ * first quantizing the bf16 activations into its LDS (for at most 32 rows and 24576
+ * elements on the 16-row kernel, 16384 on split-K, where repeating that quantization in
+ * every workgroup along N costs less than a second launch), instead of the quantize
+ * kernel followed by nvfp4_gemm. num_cus as in nvfp4_gemm_plan. Host only.
  * Writes 1 (one kernel) or 0 (two) to *fused; NVFP4_ERROR_INVALID_VALUE for a null
  * pointer, NVFP4_ERROR_INVALID_SHAPE for shapes the linear rejects.
  */

@@ -1021,35 +1021,49 @@ __global__ void __launch_bounds__(256) gemm_fit_kernel(GemmProblem p) {
 }
 
 // Fused linear for the shortest activations: the workgroup quantizes the M x K bf16
-// activations (M * K <= kFuseElems) into LDS in the NVFP4 layout (codes xq [M][K/2], scales
+// activations (M * K <= kFuseElems, or kFuseElemsGemv in the 16-row kernel) into LDS in the NVFP4 layout (codes xq [M][K/2], scales
 // xqs [M][K/16]) with the quantize kernel's functions, so codes and scales are bit-identical
 // to nvfp4_quantize's, and with `store` also into the caller's workspace. Half block hb
 // (8 elements) per lane, the pair (hb, hb ^ 1) being one block in lanes (2i, 2i + 1) of one
-// wave; the workgroup's `nthreads` threads (a multiple of 64) take half blocks in turn, so
-// both lanes of a pair are always active together.
-constexpr int kFuseElems = 16384;
+// wave; the workgroup's `nthreads` threads (a multiple of 64) take half blocks in turn, U
+// at a time (their loads issued first), so both lanes of a pair are always active
+// together.
+constexpr int kFuseElems = 16384;      // split-K's fused form
+constexpr int kFuseElemsGemv = 24576;  // the 16-row kernel's fused form (12 KiB of codes)
 __device__ __forceinline__ void quantize_to_lds(const FusedQuant& fq, int64_t M, int64_t K,
                                                 uint8_t* xq, uint8_t* xqs, bool store,
                                                 int nthreads) {
+  constexpr int U = 4;  // loads in flight per thread before their half blocks are encoded
   const QuantScale qsc = quant_scale(fq.gs, fq.den, fq.rden, fq.gs_dev);
   const int nhalves = (int)(M * K / 8);
   const u32x4* xv = (const u32x4*)fq.x;
-  for (int hb = threadIdx.x; hb < nhalves; hb += nthreads) {
-    float f[8];
-    unpack_bf16x8(xv[hb], f);
-    float a = 0.0f;
+  for (int base = threadIdx.x; base < nhalves; base += nthreads * U) {
+    u32x4 v[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
-    const float o = __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
-    const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
-    const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
-                                                         : encode_half<false>(f, bs);
-    *(uint32_t*)&xq[4 * hb] = word;
-    if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
-    if (store && fq.ws_packed != nullptr) {
-      *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
-      if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
+    for (int u = 0; u < U; ++u) {
+      const int hb = base + u * nthreads;
+      v[u] = hb < nhalves ? xv[hb] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int hb = base + u * nthreads;
+      if (hb >= nhalves) continue;  // (both lanes of a pair alike: nhalves is even)
+      float f[8];
+      unpack_bf16x8(v[u], f);
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(f[e]));
+      const float o = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+      const BlockScale bs = block_scale(__builtin_fmaxf(a, o), qsc.den, qsc.rden, qsc.gs);
+      const uint32_t word = __any(bs.code == kE4M3MaxCode) ? encode_half<true>(f, bs)
+                                                           : encode_half<false>(f, bs);
+      *(uint32_t*)&xq[4 * hb] = word;
+      if ((hb & 1) == 0) xqs[hb >> 1] = (uint8_t)bs.code;
+      if (store && fq.ws_packed != nullptr) {
+        *(uint32_t*)(fq.ws_packed + 4 * (int64_t)hb) = word;
+        if ((hb & 1) == 0) fq.ws_scales[hb >> 1] = (uint8_t)bs.code;
+      }
     }
   }
 }
@@ -1314,8 +1328,8 @@ template <int NW, int DG, int B, bool kFuse, bool kExp>
 __global__ void __launch_bounds__(64 * NW) gemm_gemv16_kernel(GemmProblem p, int R, FusedQuant fq) {
   typedef float floatx4 __attribute__((ext_vector_type(4)));
   __shared__ floatx4 red[NW][B][64];
-  __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElems / 2 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t xqs[kFuse ? kFuseElems / 16 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xq[kFuse ? kFuseElemsGemv / 2 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xqs[kFuse ? kFuseElemsGemv / 16 : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
@@ -1602,7 +1616,7 @@ hipError_t launch_gemv16(const GemmProblem& p, const FusedQuant& fq, hipStream_t
   const int R = gemv16_rows(p.N, cus > 0 ? cus : 256);
   const int64_t wgs = (p.N + R - 1) / R;
   if (wgs > 0x7FFFFFFF || p.M > 32 || p.K % 256 != 0) return hipErrorInvalidValue;
-  if (kFuse && p.M * p.K > kFuseElems) return hipErrorInvalidValue;
+  if (kFuse && p.M * p.K > kFuseElemsGemv) return hipErrorInvalidValue;
   // eight waves once K has eight groups (more loads in flight per compute unit); one or
   // two 16-row activation blocks
   const bool wide = p.K / 256 >= 8;
@@ -1773,21 +1787,24 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream, const LaunchInf
 
 bool linear_fused(int64_t M, int64_t N, int64_t K, bool aligned, int64_t cus) {
   // activations small enough to quantize in every workgroup (and to sit in its LDS), on
-  // the GEMM the product would run: the 16-row kernel, or split-K with one 32-row
-  // activation group
-  if (M > 32 || M * K > kFuseElems) return false;
+  // the GEMM the product would run: the 16-row kernel (up to 24576 elements: its loads of
+  // the weights are in flight meanwhile; at K = 3072 the fused form took 4.3, 5.6 and
+  // 6.8 us for 1, 6 and 10 rows, the quantize kernel and the GEMM 6.4 us for 11 rows) or
+  // split-K with one 32-row activation group (up to 16384)
+  if (M > 32) return false;
   const GemmPlan g = plan_gemm(M, N, K, aligned, cus);
-  return g.kernel == NVFP4_GEMM_GEMV16 || g.kernel == NVFP4_GEMM_SPLITK;
+  if (g.kernel == NVFP4_GEMM_GEMV16) return M * K <= kFuseElemsGemv;
+  return g.kernel == NVFP4_GEMM_SPLITK && M * K <= kFuseElems;
 }
 
 hipError_t launch_linear_fused(const GemmProblem& p, const FusedQuant& fq, hipStream_t stream,
                                int64_t cus) {
-  if (p.M > 32 || p.M * p.K > kFuseElems) return hipErrorInvalidValue;
+  if (p.M > 32) return hipErrorInvalidValue;
   // (the entry points have checked the operands' alignment, as linear_fused assumes)
   if (plan_gemm(p.M, p.N, p.K, true, cus).kernel == NVFP4_GEMM_GEMV16)
     return launch_gemv16<true>(p, fq, stream, cus);
   const int64_t wgs = (p.N + 31) / 32;
-  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (p.M * p.K > kFuseElems || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (p.K % 64 == 0)
     launch_splitk_kernel<1, 1, 4, 4, true, true>(dim3((unsigned)wgs), dim3(256), stream, p, fq);
   else

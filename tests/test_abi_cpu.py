@@ -224,8 +224,13 @@ def test_linear_plan_fuses_short_activations(lib):
     assert plan(1, 3072, 12288) == (L.SUCCESS, 1)
     assert plan(32, 3072, 512) == (L.SUCCESS, 1)
     assert plan(32, 3072, 544) == (L.SUCCESS, 0)   # 17408 elements
-    assert plan(2, 96, 12288) == (L.SUCCESS, 0)
-    for M in (6, 17, 32, 33, 64, 256, 1000, 4608):
+    # the 16-row kernel's fused form takes up to 24576 elements
+    assert plan(2, 96, 12288) == (L.SUCCESS, 1)
+    for M in (6, 8):
+        assert plan(M, 3072, 3072) == (L.SUCCESS, 1), M
+    assert plan(32, 1024, 768) == (L.SUCCESS, 1)
+    assert plan(32, 1024, 1024) == (L.SUCCESS, 0)
+    for M in (9, 17, 32, 33, 64, 256, 1000, 4608):
         assert plan(M, 3072, 3072) == (L.SUCCESS, 0), M
     assert plan(8, 60, 208) == (L.SUCCESS, 0)     # K % 32 == 16: no split-K
     assert plan(0, 3072, 3072) == (L.SUCCESS, 0)

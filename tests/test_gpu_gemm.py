@@ -207,8 +207,9 @@ def test_linear_matches_quantize_then_gemm(name):
     _assert_close(got[rows], ap[rows], as_[rows], ags, wp, ws, wgs, name)
 
 
-@pytest.mark.parametrize("M,N,K,plan", [(1, 640, 256, "fused"), (17, 3072, 1024, "two_kernels"),
-                                         (16, 3072, 1280, "two_kernels"),
+@pytest.mark.parametrize("M,N,K,plan", [(1, 640, 256, "fused"), (17, 3072, 1024, "fused"),
+                                         (16, 3072, 1280, "fused"), (32, 3072, 2304, "two_kernels"),
+                                         (17, 3072, 1056, "two_kernels"),
                                          (600, 700, 256, "two_kernels")])
 def test_linear_calibrated_scales_with_subnormal_product(M, N, K, plan):
     """nvfp4_linear on tensors of magnitude 2^-70 and 2^-60 (all positive, so the sums do

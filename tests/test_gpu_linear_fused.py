@@ -71,6 +71,8 @@ def _check(x, w, ags, label, scale_dev=False):
     (1, 3072, 3072), (5, 3072, 3072), (32, 200, 160), (5, 33, 96), (31, 1000, 224),
     (1, 64, 32), (3, 5000, 1056), (2, 96, 6144), (1, 3072, 12288), (16, 1024, 1024),
     (32, 12288, 512),
+    # the 16-row kernel's fused form beyond 16384 elements (up to 24576)
+    (6, 3072, 3072), (8, 3072, 3072), (24, 1024, 1024), (2, 96, 12288),
 ])
 def test_fused_linear_matches_two_kernels(M, N, K):
     x, w = _inputs(M, N, K, M * 7 + N + K)
@@ -93,11 +95,14 @@ def test_fused_linear_device_scales():
 
 
 def test_plan_boundary():
-    """At most 32 rows and 16384 elements fuse; just past either bound the linear runs as
-    quantize + GEMM, with the same workspace contents."""
+    """At most 32 rows and 16384 elements fuse (24576 on the 16-row kernel); just past
+    either bound the linear runs as quantize + GEMM, with the same workspace contents."""
     assert nv.linear_plan(32, 3072, 512) == "fused"
     assert nv.linear_plan(32, 3072, 544) == "two_kernels"
     assert nv.linear_plan(33, 3072, 256) == "two_kernels"
+    # the 16-row kernel (K % 256 == 0) fuses up to 24576 elements
+    assert nv.linear_plan(32, 1024, 768) == "fused"
+    assert nv.linear_plan(32, 1024, 1024) == "two_kernels"
     x, w = _inputs(33, 256, 256, 7)
     ags = O.global_scale(x)
     wgs = O.global_scale(w)
