@@ -92,6 +92,9 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
 #ifndef NVFP4_QUANT_WG_PER_CU
 #define NVFP4_QUANT_WG_PER_CU 32
 #endif
+#ifndef NVFP4_QUANT_WG_PER_CU_SMALL
+#define NVFP4_QUANT_WG_PER_CU_SMALL 6
+#endif
   constexpr int kThreads = 256;
   constexpr int kUnroll = NVFP4_QUANT_UNROLL;
   const float den = 6.0f * gs;   // IEEE binary32 on the host
@@ -99,7 +102,11 @@ hipError_t launch_quantize(const void* x, int64_t M, int64_t K, float gs, void* 
   const int64_t want = (nhalves + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   // Enough workgroups to fill every CU several times over; the grid-stride loop covers
   // the rest.
-  const int64_t cap = (int64_t)dev.num_cus * NVFP4_QUANT_WG_PER_CU;
+  // Workgroups per compute unit: up to 2^21 half blocks (a 4608 x 3072 activation) fewer
+  // workgroups that loop 2-3 times start sooner and finish together (8.64 -> 8.03 us there);
+  // larger tensors stream best with many (4608 x 12288: 24.7 us at 32, 25.8-26.6 at 4-12).
+  const int64_t per_cu = nhalves <= ((int64_t)1 << 21) ? NVFP4_QUANT_WG_PER_CU_SMALL : NVFP4_QUANT_WG_PER_CU;
+  const int64_t cap = (int64_t)dev.num_cus * per_cu;
   const int grid = (int)(want < cap ? want : cap);
   hipLaunchKernelGGL((quantize_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
                      (const u32x4*)x, (uint32_t*)packed, (uint8_t*)scales, nhalves, gs, den, rden,
